@@ -1,0 +1,182 @@
+"""CPU oracle for MoE dispatch layout and scatter: TEST INFRASTRUCTURE ONLY.
+
+A ctypes wrapper around ``dispatch_oracle.c``: plain single-threaded C that
+follows the "DeepEP Counting Sort / Bucketization" page step by step (Count,
+Prefix Sum with alignment, rank- and expert-level slot scatter, row copies with
+zero padding). Only ``tests/``, the smoke check and the benchmark's CPU
+baseline may import this package; the product library never does, and the two
+share no code.
+
+Every function here is marshalling: numpy arrays in, the C oracle does the
+arithmetic, numpy arrays out.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dispatch_oracle.c")
+LIB_PATH = os.path.join(_HERE, "libdispatch_oracle.so")
+
+BAD_EXPERT = 1
+RECV_OVERFLOW = 2
+RANK_OVERFLOW = 4
+DUP_EXPERT = 8
+
+_lib = None
+
+
+def build(src: str = _SRC, out: str = LIB_PATH) -> str:
+    """Compile the oracle with gcc (single-threaded, -O2)."""
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
+                    "-I", _HERE, "-o", tmp, src], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def load_library(path: str):
+    """Load a compiled oracle from ``path`` (the default build, or a test's variant)."""
+    lib = ctypes.CDLL(path)
+    i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    lib.oracle_dispatch_layout.argtypes = [i64, i32, i32, i32, i32, p, i64, i64,
+                                           p, p, p, p, p, p, p, p]
+    lib.oracle_dispatch_layout.restype = ctypes.c_int
+    lib.oracle_dispatch_scatter.argtypes = [i64, i32, i32, i64, i32, p, p, p, p, p, p,
+                                            p, p, p, p, ctypes.c_int]
+    lib.oracle_dispatch_scatter.restype = ctypes.c_int
+    return lib
+
+
+def _load(lib=None):
+    global _lib
+    if lib is not None:
+        return lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        _lib = load_library(LIB_PATH)
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+# Value the wrappers put in inverse-map entries beyond the totals, so a test
+# can see that nothing past the totals was written.
+CANARY = -7
+
+
+@dataclasses.dataclass
+class Layout:
+    status: int
+    num_experts: int
+    num_ranks: int
+    alignment: int
+    expert_count: np.ndarray        # int32 [E]
+    rank_count: np.ndarray          # int32 [R]
+    expert_psum: np.ndarray         # int32 [E+1], exclusive, aligned
+    rank_psum: np.ndarray           # int32 [R+1], exclusive
+    expert_slot: np.ndarray         # int32 [T, K]
+    rank_slot: np.ndarray           # int32 [T, K]
+    recv_src_token_idx: np.ndarray  # int32 [recv_capacity]
+    rank_src_token_idx: np.ndarray  # int32 [rank_capacity]
+
+    @property
+    def num_recv_rows(self) -> int:
+        return int(self.expert_psum[-1])
+
+    @property
+    def num_rank_rows(self) -> int:
+        return int(self.rank_psum[-1])
+
+
+def max_rows(num_tokens: int, num_topk: int, num_experts: int, num_ranks: int,
+             alignment: int) -> tuple:
+    """Worst-case row counts: every pair routed, every expert padded by A-1."""
+    return (num_tokens * num_topk + num_experts * (max(alignment, 1) - 1),
+            num_tokens * min(num_topk, num_ranks))
+
+
+def layout(topk_idx: np.ndarray, num_experts: int, num_ranks: int, alignment: int = 1,
+           recv_capacity: Optional[int] = None, rank_capacity: Optional[int] = None,
+           lib=None) -> Layout:
+    """Counts, psums, slot maps and inverse maps of one routing table."""
+    lib = _load(lib)
+    topk = np.ascontiguousarray(topk_idx, dtype=np.int64)
+    if topk.ndim != 2:
+        raise ValueError("topk_idx must be [T, K]")
+    t, k = topk.shape
+    mr, mk = max_rows(t, k, num_experts, num_ranks, alignment)
+    recv_capacity = mr if recv_capacity is None else recv_capacity
+    rank_capacity = mk if rank_capacity is None else rank_capacity
+    out = Layout(
+        status=0, num_experts=num_experts, num_ranks=num_ranks, alignment=alignment,
+        expert_count=np.zeros(num_experts, np.int32), rank_count=np.zeros(num_ranks, np.int32),
+        expert_psum=np.zeros(num_experts + 1, np.int32), rank_psum=np.zeros(num_ranks + 1, np.int32),
+        expert_slot=np.full((t, k), CANARY, np.int32), rank_slot=np.full((t, k), CANARY, np.int32),
+        recv_src_token_idx=np.full(max(recv_capacity, 0), CANARY, np.int32),
+        rank_src_token_idx=np.full(max(rank_capacity, 0), CANARY, np.int32))
+    rc = lib.oracle_dispatch_layout(
+        t, k, num_experts, num_ranks, alignment, _ptr(topk), recv_capacity, rank_capacity,
+        _ptr(out.expert_count), _ptr(out.rank_count), _ptr(out.expert_psum), _ptr(out.rank_psum),
+        _ptr(out.expert_slot), _ptr(out.rank_slot), _ptr(out.recv_src_token_idx),
+        _ptr(out.rank_src_token_idx))
+    if rc < 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    out.status = rc
+    return out
+
+
+@dataclasses.dataclass
+class Rows:
+    rank_x: Optional[np.ndarray]    # uint8 [N_r, row_bytes]
+    rank_sf: Optional[np.ndarray]   # float32 [N_r, S]
+    recv_x: Optional[np.ndarray]    # uint8 [P, row_bytes]
+    recv_sf: Optional[np.ndarray]   # float32 [P, S]
+
+
+def scatter(lay: Layout, x_bytes: np.ndarray, x_sf: Optional[np.ndarray] = None,
+            rank_contig: bool = True, expert_major: bool = True, zero_pad: bool = True,
+            fill: int = 0xA5, lib=None) -> Rows:
+    """Rank-contiguous and expert-major row copies of one layout.
+
+    Output rows are pre-filled with ``fill`` so that unwritten bytes are visible.
+    """
+    if lay.status != 0:
+        raise ValueError("layout carries an error status; rows are unspecified")
+    lib = _load(lib)
+    x_bytes = np.ascontiguousarray(x_bytes, dtype=np.uint8)
+    t, row_bytes = x_bytes.shape
+    k = lay.expert_slot.shape[1]
+    s = 0 if x_sf is None else int(x_sf.shape[1])
+    sf = None if x_sf is None else np.ascontiguousarray(x_sf, dtype=np.float32)
+    n_rank, n_recv = lay.num_rank_rows, lay.num_recv_rows
+
+    def rows(n, width, dtype, on):
+        if not on:
+            return None
+        a = np.empty((n, width), dtype=dtype)
+        a.view(np.uint8)[...] = fill
+        return a
+
+    out = Rows(rank_x=rows(n_rank, row_bytes, np.uint8, rank_contig),
+               rank_sf=rows(n_rank, s, np.float32, rank_contig and s > 0),
+               recv_x=rows(n_recv, row_bytes, np.uint8, expert_major),
+               recv_sf=rows(n_recv, s, np.float32, expert_major and s > 0))
+    rc = lib.oracle_dispatch_scatter(
+        t, k, lay.num_experts, row_bytes, s, _ptr(x_bytes), _ptr(sf),
+        _ptr(lay.expert_count), _ptr(lay.expert_psum), _ptr(lay.expert_slot),
+        _ptr(lay.rank_slot), _ptr(out.rank_x), _ptr(out.rank_sf), _ptr(out.recv_x),
+        _ptr(out.recv_sf), 1 if zero_pad else 0)
+    if rc != 0:
+        raise ValueError(f"oracle scatter failed (code {rc})")
+    return out

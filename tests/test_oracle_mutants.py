@@ -1,0 +1,123 @@
+"""Planted mistakes in a copy of the CPU oracle must fail the pins (CPU only).
+
+Each mutant is the oracle's C source with one plausible mistake written in (a
+dropped alignment, the wrong rounding, the wrong dedup owner, an off-by-one
+cursor, reversed token order, interleaved ranks, unmarked pads, a wrong copy
+source, a skipped zero fill). It is compiled into a temporary library and run
+on a few inputs; the pin checks must reject every mutant. This shows the pins
+are sharp enough to catch such mistakes in the real oracle.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "dispatch_oracle.c")
+
+LAYOUT_MUTANTS = {
+    "no_alignment": ("run += align_up(expert_count[e], A);", "run += expert_count[e];", 1),
+    "floor_alignment": ("return ((c + a - 1) / a) * a;", "return (c / a) * a;", 1),
+    "lowest_k_owns_rank_slot": (
+        "            for (int32_t j = k + 1; j < K; ++j)\n"
+        "                if (is_routed(row[j], E) && row[j] / experts_per_rank == r) owner = 0;\n"
+        "            if (owner) {",
+        "            for (int32_t j = 0; j < k; ++j)\n"
+        "                if (is_routed(row[j], E) && row[j] / experts_per_rank == r) owner = 0;\n"
+        "            if (owner) {", 1),
+    "no_rank_dedup": ("if (owner) rank_count[r] += 1;", "rank_count[r] += 1;", 1),
+    "cursor_off_by_one": ("expert_cursor[e] = expert_psum[e];", "expert_cursor[e] = expert_psum[e] + 1;", 1),
+    "rank_cursor_off_by_one": ("rank_cursor[r] = rank_psum[r];", "rank_cursor[r] = rank_psum[r] + (r > 0);", 1),
+    "reversed_token_order": (
+        "    for (int64_t t = 0; t < T; ++t) {\n        const int64_t* row = topk_idx + t * K;\n"
+        "        for (int32_t k = 0; k < K; ++k) {\n            const int64_t e = row[k];\n"
+        "            if (e < 0) {",
+        "    for (int64_t t = T - 1; t >= 0; --t) {\n        const int64_t* row = topk_idx + t * K;\n"
+        "        for (int32_t k = 0; k < K; ++k) {\n            const int64_t e = row[k];\n"
+        "            if (e < 0) {", 1),
+    "interleaved_ranks": ("const int64_t r = e / experts_per_rank;", "const int64_t r = e % R;", 2),
+    "pads_not_marked": ("recv_src_token_idx[s] = -1;", "recv_src_token_idx[s] = 0;", 1),
+    "psum_lags_one_expert": ("        run += align_up(expert_count[e], A);\n        expert_psum[e + 1] = (int32_t)run;",
+                             "        expert_psum[e + 1] = (int32_t)run;\n        run += align_up(expert_count[e], A);", 1),
+}
+
+SCATTER_MUTANTS = {
+    "wrong_source_row": ("memcpy(recv_x + slot * row_bytes, x + t * row_bytes",
+                         "memcpy(recv_x + slot * row_bytes, x + ((t + 1) % T) * row_bytes", 1),
+    "rank_rows_skip_first_token": ("const int64_t row = rank_slot[t * K + k];",
+                                   "const int64_t row = t == 0 ? -1 : rank_slot[t * K + k];", 1),
+    "no_zero_pad": ("if (recv_x) memset(recv_x + s * row_bytes, 0, (size_t)row_bytes);", "(void)0;", 1),
+    "sf_short_copy": ("memcpy(recv_sf + slot * S, x_sf + t * S, sf_bytes);",
+                      "memcpy(recv_sf + slot * S, x_sf + t * S, sf_bytes - 4);", 1),
+}
+
+
+def _mutant_lib(tmp_path, name, old, new, count):
+    src = open(SRC).read()
+    assert src.count(old) == count, f"{name}: pattern found {src.count(old)} times"
+    path = tmp_path / f"mut_{name}.c"
+    path.write_text(src.replace(old, new))
+    so = str(tmp_path / f"libmut_{name}.so")
+    oracle.build(str(path), so)
+    return oracle.load_library(so)
+
+
+def _cases():
+    rng = np.random.default_rng(5)
+    out = []
+    for t, k, e, r, a in [(37, 4, 16, 4, 4), (64, 6, 12, 3, 3), (20, 3, 8, 2, 1), (50, 8, 32, 8, 8)]:
+        g = rng.gumbel(size=(t, e))
+        topk = np.argsort(-g, axis=1, kind="stable")[:, :k].astype(np.int64)
+        topk[rng.random((t, k)) < 0.15] = -1
+        out.append((topk, e, r, a))
+    w = W.get("tiny")
+    out.append((W.make_topk(w), w.num_experts, w.num_ranks, w.alignment))
+    return out
+
+
+def _layout_rejected(lib):
+    for topk, e, r, a in _cases():
+        # Spare capacity keeps an off-by-one mutant's stray write inside the
+        # arrays, where the canary check sees it.
+        mr, mk = oracle.max_rows(topk.shape[0], topk.shape[1], e, r, a)
+        try:
+            lay = oracle.layout(topk, e, r, a, recv_capacity=mr + 64, rank_capacity=mk + 64, lib=lib)
+            pins.check_layout(topk, e, r, a, lay, canary=oracle.CANARY)
+            pins.check_against_brute_force(topk, e, r, a, lay)
+        except AssertionError:
+            return True
+    return False
+
+
+@pytest.mark.parametrize("name", sorted(LAYOUT_MUTANTS))
+def test_layout_mutant_is_caught(tmp_path, name):
+    lib = _mutant_lib(tmp_path, name, *LAYOUT_MUTANTS[name])
+    assert _layout_rejected(lib), f"pins did not catch mutant {name}"
+
+
+@pytest.mark.parametrize("name", sorted(SCATTER_MUTANTS))
+def test_scatter_mutant_is_caught(tmp_path, name):
+    lib = _mutant_lib(tmp_path, name, *SCATTER_MUTANTS[name])
+    rng = np.random.default_rng(9)
+    caught = False
+    for topk, e, r, a in _cases():
+        t = topk.shape[0]
+        x = rng.integers(0, 256, size=(t, 64), dtype=np.uint8)
+        sf = rng.uniform(0.5, 2.0, size=(t, 3)).astype(np.float32)
+        lay = oracle.layout(topk, e, r, a)
+        rows = oracle.scatter(lay, x, sf, lib=lib)
+        try:
+            pins.check_rows(lay, x, sf, rows)
+        except AssertionError:
+            caught = True
+            break
+    assert caught, f"pins did not catch mutant {name}"
+
+
+def test_unmutated_oracle_passes_same_cases(tmp_path):
+    lib = _mutant_lib(tmp_path, "identity", "int status = 0;", "int status = 0;", 1)
+    assert not _layout_rejected(lib)
