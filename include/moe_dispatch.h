@@ -1,0 +1,149 @@
+/*
+ * moe_dispatch.h: C ABI of the MI355X (gfx950) MoE token dispatch library.
+ *
+ * The library computes the dispatch layout of a token batch as a counting
+ * sort ("DeepEP Counting Sort / Bucketization" page: Count -> Prefix Sum ->
+ * Scatter, sections 2 to 8) and moves the token rows into two layouts:
+ *
+ *   - a rank-contiguous buffer: one row per (token, destination rank), rank r's
+ *     block is rows [rank_psum[r], rank_psum[r+1]) (the page's rank-level
+ *     scatter, section 6.2-6.3);
+ *   - an expert-major buffer recv_x: one row per routed (token, expert) pair,
+ *     expert e's bucket is rows [expert_psum[e], expert_psum[e+1]), padded with
+ *     zero rows up to a multiple of the expert alignment (the page's expand
+ *     mode and copy epilogue, sections 6.4, 7 and 8).
+ *
+ * A "rank" is a logical group of E/R consecutive experts on this one GPU:
+ * expert e belongs to rank e / (E/R). Inside every expert bucket and every
+ * rank block, rows follow ascending token index, so the whole layout is unique
+ * and deterministic. The (token, rank) slot is held by the highest k of that
+ * rank in the token (the page's dedup "master lane", section 4.2).
+ *
+ * Conventions for every entry point:
+ *   - Ownership: all buffer pointers are device pointers allocated and owned by
+ *     the caller. The library allocates, frees and retains no memory.
+ *   - Asynchrony: all work is enqueued on `stream` (a hipStream_t, NULL = the
+ *     null stream); no entry point synchronizes. Buffers must stay alive until
+ *     the stream has passed the work.
+ *   - Host errors: a negative return code is given before anything is
+ *     enqueued (see DISPATCH_ERR_*).
+ *   - Device errors: dispatch_layout writes a status word (DISPATCH_STATUS_*).
+ *     When it is non-zero, slot maps, inverse maps and rows are unspecified and
+ *     dispatch_scatter writes no row.
+ *   - Rows and inverse-map entries beyond the totals (expert_psum[E],
+ *     rank_psum[R]) up to the capacities are never written.
+ *   - Reentrancy: the library is stateless; concurrent calls need their own
+ *     workspaces and outputs.
+ */
+#ifndef MOE_DISPATCH_H
+#define MOE_DISPATCH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DISPATCH_ABI_VERSION 1
+
+/* Limits. K <= 32 follows the page's bound on the top-k width (section 4.2). */
+#define DISPATCH_MAX_TOPK 32
+#define DISPATCH_MAX_EXPERTS 4096
+
+/* Host error codes (returned before any work is enqueued). */
+#define DISPATCH_OK 0
+#define DISPATCH_ERR_NULL (-1)      /* a required pointer is NULL */
+#define DISPATCH_ERR_ARG (-2)       /* a size or flag is out of range */
+#define DISPATCH_ERR_ALIGN (-3)     /* row_bytes % 16 != 0 or a pointer is misaligned */
+#define DISPATCH_ERR_WORKSPACE (-4) /* workspace missing, too small or misaligned */
+#define DISPATCH_ERR_HIP (-5)       /* the HIP runtime refused a launch */
+
+/* Device status bits written by dispatch_layout to *status. */
+#define DISPATCH_STATUS_BAD_EXPERT 1u     /* an entry of topk_idx is >= num_experts */
+#define DISPATCH_STATUS_RECV_OVERFLOW 2u  /* expert_psum[E] > recv_capacity_rows */
+#define DISPATCH_STATUS_RANK_OVERFLOW 4u  /* rank_psum[R] > rank_capacity_rows */
+#define DISPATCH_STATUS_DUP_EXPERT 8u     /* an expert repeated within one token */
+
+/* Output selection for dispatch_scatter. */
+#define DISPATCH_RANK_CONTIG 1u  /* write rank_x (and rank_sf) */
+#define DISPATCH_EXPERT_MAJOR 2u /* write recv_x (and recv_sf) */
+#define DISPATCH_ZERO_PAD 4u     /* zero the alignment pad rows of recv_x / recv_sf */
+#define DISPATCH_ALL_OUTPUTS (DISPATCH_RANK_CONTIG | DISPATCH_EXPERT_MAJOR | DISPATCH_ZERO_PAD)
+
+typedef struct dispatch_problem {
+    int64_t num_tokens;         /* T >= 0 */
+    int32_t num_topk;           /* K, 1..DISPATCH_MAX_TOPK */
+    int32_t num_experts;        /* E, 1..DISPATCH_MAX_EXPERTS */
+    int32_t num_ranks;          /* R >= 1, E % R == 0 */
+    int32_t expert_alignment;   /* A >= 1; 1 = no padding (section 7.2) */
+    int32_t topk_idx_bytes;     /* width of a topk_idx entry: 8 (int64) or 4 (int32) */
+    int32_t sf_per_token;       /* S >= 0 fp32 scale factors per token (H/128 for fp8, else 0) */
+    int64_t row_bytes;          /* bytes per token row (H * element size), > 0, multiple of 16 */
+    int64_t recv_capacity_rows; /* rows of recv_x / recv_sf / recv_src_token_idx */
+    int64_t rank_capacity_rows; /* rows of rank_x / rank_sf / rank_src_token_idx */
+    uint32_t flags;             /* DISPATCH_* output selection, used by dispatch_scatter */
+    uint32_t reserved;          /* must be 0 */
+} dispatch_problem_t;
+
+/* Layout outputs; every pointer is a caller-owned device int32 array. */
+typedef struct dispatch_layout {
+    int32_t* expert_count;       /* [E]   routed pairs per expert, before alignment */
+    int32_t* rank_count;         /* [R]   tokens per rank, deduplicated (section 4.2) */
+    int32_t* expert_psum;        /* [E+1] exclusive psum of align(expert_count, A); [E] = total rows */
+    int32_t* rank_psum;          /* [R+1] exclusive psum of rank_count; [R] = total rank rows */
+    int32_t* expert_slot;        /* [T*K] recv_x row of pair (t, k), -1 if masked */
+    int32_t* rank_slot;          /* [T*K] rank_x row of (t, rank of k) at the owning k, else -1 */
+    int32_t* recv_src_token_idx; /* [recv_capacity_rows] token of each recv_x row, -1 on pads */
+    int32_t* rank_src_token_idx; /* [rank_capacity_rows] token of each rank_x row */
+    int32_t* status;             /* [1]   DISPATCH_STATUS_* bits, 0 = success */
+} dispatch_layout_t;
+
+/* Version of this ABI (DISPATCH_ABI_VERSION). */
+int dispatch_abi_version(void);
+
+/* Static, human-readable text for a host error code. Never NULL. */
+const char* dispatch_strerror(int code);
+
+/* Bytes of device workspace dispatch_layout needs for this problem (T, K, E,
+ * R are read). The workspace must be 256-byte aligned and zero-filled before
+ * its first use; every completed dispatch_layout call leaves its control words
+ * zero again, so it can be reused without clearing (the page's self-cleaning
+ * counters, section 6.2). */
+int dispatch_workspace_size(const dispatch_problem_t* problem, size_t* bytes);
+
+/* Worst-case row counts, for sizing outputs without reading the totals back:
+ * max_recv_rows = T*K + E*(A-1) and max_rank_rows = T*min(K, R). Either
+ * output pointer may be NULL. */
+int dispatch_max_rows(const dispatch_problem_t* problem, int64_t* max_recv_rows,
+                      int64_t* max_rank_rows);
+
+/* Count -> Prefix Sum -> slot assignment (sections 4, 5, 6.2, 6.4 and 7).
+ * topk_idx: device [T, K] row-major of problem->topk_idx_bytes wide signed
+ * integers; a negative entry is masked. Writes every field of `out` (counts
+ * and psums always; slot and inverse maps when *status is 0). Needs
+ * `workspace` of at least dispatch_workspace_size() bytes. */
+int dispatch_layout(const dispatch_problem_t* problem, const void* topk_idx,
+                    const dispatch_layout_t* out, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/* Row scatter of a layout made by dispatch_layout with the same problem
+ * (sections 6.3, 7.3 and 8.2). Reads layout->expert_count, expert_psum,
+ * expert_slot, rank_slot and status. x: device [T, row_bytes] (opaque bytes,
+ * bf16 or fp8 alike), 16-byte aligned. x_sf: device fp32 [T, S] or NULL when
+ * S == 0. Writes, as selected by problem->flags:
+ *   rank_x [rank_psum[R], row_bytes] and rank_sf [rank_psum[R], S];
+ *   recv_x [expert_psum[E], row_bytes] and recv_sf [expert_psum[E], S], with
+ *   pad rows zeroed under DISPATCH_ZERO_PAD.
+ * Copies are bitwise. Writes nothing when the layout's status is non-zero. */
+int dispatch_scatter(const dispatch_problem_t* problem, const dispatch_layout_t* layout,
+                     const void* x, const float* x_sf, void* rank_x, float* rank_sf,
+                     void* recv_x, float* recv_sf, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DISPATCH_H */

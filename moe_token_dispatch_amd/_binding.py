@@ -1,0 +1,266 @@
+"""ctypes binding of the dispatch C ABI (``include/moe_dispatch.h``).
+
+Argument marshalling only: every step of dispatch runs in the HIP kernels of
+``libmoe_dispatch.so``. torch supplies device memory and the current stream.
+The library must have been built (``python -m moe_token_dispatch_amd.build``);
+loading fails loudly otherwise, and there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Tuple
+
+import torch  # load torch's HIP runtime first so the library binds to the same one
+
+from .build import LIB_PATH
+
+ABI_VERSION = 1
+MAX_TOPK = 32
+MAX_EXPERTS = 4096
+
+OK = 0
+ERR_NULL = -1
+ERR_ARG = -2
+ERR_ALIGN = -3
+ERR_WORKSPACE = -4
+ERR_HIP = -5
+
+STATUS_BAD_EXPERT = 1
+STATUS_RECV_OVERFLOW = 2
+STATUS_RANK_OVERFLOW = 4
+STATUS_DUP_EXPERT = 8
+
+RANK_CONTIG = 1
+EXPERT_MAJOR = 2
+ZERO_PAD = 4
+ALL_OUTPUTS = RANK_CONTIG | EXPERT_MAJOR | ZERO_PAD
+
+
+class DispatchError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {dispatch_strerror(code)} (code {code})")
+
+
+class Problem(ctypes.Structure):
+    """dispatch_problem_t."""
+
+    _fields_ = [
+        ("num_tokens", ctypes.c_int64),
+        ("num_topk", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("num_ranks", ctypes.c_int32),
+        ("expert_alignment", ctypes.c_int32),
+        ("topk_idx_bytes", ctypes.c_int32),
+        ("sf_per_token", ctypes.c_int32),
+        ("row_bytes", ctypes.c_int64),
+        ("recv_capacity_rows", ctypes.c_int64),
+        ("rank_capacity_rows", ctypes.c_int64),
+        ("flags", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+    ]
+
+
+class LayoutPtrs(ctypes.Structure):
+    """dispatch_layout_t."""
+
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "expert_count", "rank_count", "expert_psum", "rank_psum", "expert_slot", "rank_slot",
+        "recv_src_token_idx", "rank_src_token_idx", "status")]
+
+
+_LIB = None
+
+# Exported symbols of include/moe_dispatch.h.
+SYMBOLS = ("dispatch_abi_version", "dispatch_strerror", "dispatch_workspace_size",
+           "dispatch_max_rows", "dispatch_layout", "dispatch_scatter")
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmoe_dispatch.so (built in-tree) and declare its signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m moe_token_dispatch_amd.build`")
+    lib = ctypes.CDLL(path)
+    p, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.dispatch_abi_version.argtypes = []
+    lib.dispatch_abi_version.restype = i
+    lib.dispatch_strerror.argtypes = [i]
+    lib.dispatch_strerror.restype = ctypes.c_char_p
+    lib.dispatch_workspace_size.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(sz)]
+    lib.dispatch_workspace_size.restype = i
+    lib.dispatch_max_rows.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_int64),
+                                      ctypes.POINTER(ctypes.c_int64)]
+    lib.dispatch_max_rows.restype = i
+    lib.dispatch_layout.argtypes = [ctypes.POINTER(Problem), p, ctypes.POINTER(LayoutPtrs), p, sz, p]
+    lib.dispatch_layout.restype = i
+    lib.dispatch_scatter.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(LayoutPtrs), p, p, p, p, p, p, p]
+    lib.dispatch_scatter.restype = i
+    if lib.dispatch_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path}: ABI version {lib.dispatch_abi_version()} != {ABI_VERSION}")
+    _LIB = lib
+    return lib
+
+
+# ---------------------------------------------------------------- C ABI calls
+
+
+def dispatch_abi_version() -> int:
+    return load_library().dispatch_abi_version()
+
+
+def dispatch_strerror(code: int) -> str:
+    return load_library().dispatch_strerror(code).decode()
+
+
+def dispatch_workspace_size(problem: Problem) -> int:
+    out = ctypes.c_size_t(0)
+    rc = load_library().dispatch_workspace_size(ctypes.byref(problem), ctypes.byref(out))
+    if rc:
+        raise DispatchError(rc, "dispatch_workspace_size")
+    return int(out.value)
+
+
+def dispatch_max_rows(problem: Problem) -> Tuple[int, int]:
+    recv, rank = ctypes.c_int64(0), ctypes.c_int64(0)
+    rc = load_library().dispatch_max_rows(ctypes.byref(problem), ctypes.byref(recv), ctypes.byref(rank))
+    if rc:
+        raise DispatchError(rc, "dispatch_max_rows")
+    return int(recv.value), int(rank.value)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream: Optional[torch.cuda.Stream], device) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+@dataclasses.dataclass
+class LayoutTensors:
+    """Device int32 outputs of dispatch_layout (see dispatch_layout_t)."""
+
+    expert_count: torch.Tensor
+    rank_count: torch.Tensor
+    expert_psum: torch.Tensor
+    rank_psum: torch.Tensor
+    expert_slot: torch.Tensor
+    rank_slot: torch.Tensor
+    recv_src_token_idx: torch.Tensor
+    rank_src_token_idx: torch.Tensor
+    status: torch.Tensor
+
+    def ptrs(self) -> LayoutPtrs:
+        return LayoutPtrs(*[t.data_ptr() for t in (
+            self.expert_count, self.rank_count, self.expert_psum, self.rank_psum, self.expert_slot,
+            self.rank_slot, self.recv_src_token_idx, self.rank_src_token_idx, self.status)])
+
+
+def _check_device_tensor(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def dispatch_layout(problem: Problem, topk_idx: torch.Tensor, out: LayoutTensors,
+                    workspace: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Enqueue Count -> Prefix Sum -> slot assignment on the stream."""
+    _check_device_tensor(topk_idx, "topk_idx")
+    if topk_idx.element_size() != problem.topk_idx_bytes:
+        raise ValueError("topk_idx element width does not match problem.topk_idx_bytes")
+    _check_device_tensor(workspace, "workspace")
+    for f in dataclasses.fields(out):
+        _check_device_tensor(getattr(out, f.name), f.name, torch.int32)
+    lay = out.ptrs()
+    rc = load_library().dispatch_layout(ctypes.byref(problem), _ptr(topk_idx), ctypes.byref(lay),
+                                        _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                        _stream_handle(stream, topk_idx.device))
+    if rc:
+        raise DispatchError(rc, "dispatch_layout")
+
+
+def dispatch_scatter(problem: Problem, layout: LayoutTensors, x: torch.Tensor,
+                     x_sf: Optional[torch.Tensor], rank_x: Optional[torch.Tensor],
+                     rank_sf: Optional[torch.Tensor], recv_x: Optional[torch.Tensor],
+                     recv_sf: Optional[torch.Tensor], stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Enqueue the row scatter of a layout on the stream."""
+    _check_device_tensor(x, "x")
+    for name, t in (("x_sf", x_sf), ("rank_x", rank_x), ("rank_sf", rank_sf), ("recv_x", recv_x),
+                    ("recv_sf", recv_sf)):
+        if t is not None:
+            _check_device_tensor(t, name)
+    lay = layout.ptrs()
+    rc = load_library().dispatch_scatter(ctypes.byref(problem), ctypes.byref(lay), _ptr(x), _ptr(x_sf),
+                                         _ptr(rank_x), _ptr(rank_sf), _ptr(recv_x), _ptr(recv_sf),
+                                         _stream_handle(stream, x.device))
+    if rc:
+        raise DispatchError(rc, "dispatch_scatter")
+
+
+# ------------------------------------------------- allocation helpers (plumbing)
+
+
+def make_problem(num_tokens: int, num_topk: int, num_experts: int, num_ranks: int,
+                 expert_alignment: int = 1, topk_idx_bytes: int = 8, row_bytes: int = 0,
+                 sf_per_token: int = 0, recv_capacity_rows: Optional[int] = None,
+                 rank_capacity_rows: Optional[int] = None, flags: int = ALL_OUTPUTS) -> Problem:
+    """A problem; capacities default to the library's worst-case row counts."""
+    p = Problem(num_tokens, num_topk, num_experts, num_ranks, expert_alignment, topk_idx_bytes,
+                sf_per_token, row_bytes, 0, 0, flags, 0)
+    max_recv, max_rank = dispatch_max_rows(p)
+    p.recv_capacity_rows = max_recv if recv_capacity_rows is None else recv_capacity_rows
+    p.rank_capacity_rows = max_rank if rank_capacity_rows is None else rank_capacity_rows
+    return p
+
+
+def alloc_layout(problem: Problem, device) -> LayoutTensors:
+    i32 = dict(dtype=torch.int32, device=device)
+    t, k = problem.num_tokens, problem.num_topk
+    return LayoutTensors(
+        expert_count=torch.empty(problem.num_experts, **i32),
+        rank_count=torch.empty(problem.num_ranks, **i32),
+        expert_psum=torch.empty(problem.num_experts + 1, **i32),
+        rank_psum=torch.empty(problem.num_ranks + 1, **i32),
+        expert_slot=torch.empty((t, k), **i32),
+        rank_slot=torch.empty((t, k), **i32),
+        recv_src_token_idx=torch.empty(max(problem.recv_capacity_rows, 1), **i32),
+        rank_src_token_idx=torch.empty(max(problem.rank_capacity_rows, 1), **i32),
+        status=torch.empty(1, **i32))
+
+
+def alloc_workspace(problem: Problem, device) -> torch.Tensor:
+    """A zero-filled workspace (zeroed once; the library keeps its control words zero)."""
+    n = dispatch_workspace_size(problem)
+    return torch.zeros((n + 255) // 256 * 256, dtype=torch.uint8, device=device)
+
+
+@dataclasses.dataclass
+class RowBuffers:
+    rank_x: Optional[torch.Tensor]   # uint8 [rank_capacity_rows, row_bytes]
+    rank_sf: Optional[torch.Tensor]  # float32 [rank_capacity_rows, S]
+    recv_x: Optional[torch.Tensor]   # uint8 [recv_capacity_rows, row_bytes]
+    recv_sf: Optional[torch.Tensor]  # float32 [recv_capacity_rows, S]
+
+
+def alloc_rows(problem: Problem, device) -> RowBuffers:
+    rb, s = problem.row_bytes, problem.sf_per_token
+    want_rank = bool(problem.flags & RANK_CONTIG)
+    want_expert = bool(problem.flags & EXPERT_MAJOR)
+
+    def rows(n, width, dtype, on):
+        return torch.empty((max(n, 1), width), dtype=dtype, device=device) if on and width > 0 else None
+
+    return RowBuffers(rank_x=rows(problem.rank_capacity_rows, rb, torch.uint8, want_rank),
+                      rank_sf=rows(problem.rank_capacity_rows, s, torch.float32, want_rank),
+                      recv_x=rows(problem.recv_capacity_rows, rb, torch.uint8, want_expert),
+                      recv_sf=rows(problem.recv_capacity_rows, s, torch.float32, want_expert))

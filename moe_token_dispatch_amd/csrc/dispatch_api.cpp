@@ -1,0 +1,136 @@
+// C ABI of the dispatch library: argument checks, workspace sizing and the
+// launches. Every check runs on the host before anything is enqueued, so a
+// rejected call leaves the stream and all buffers untouched.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "dispatch_common.hpp"
+#include "moe_dispatch.h"
+
+using moe_dispatch::TileGeometry;
+
+namespace {
+
+bool aligned_to(const void* ptr, uintptr_t bytes) { return (reinterpret_cast<uintptr_t>(ptr) % bytes) == 0; }
+
+// Checks shared by every entry point that takes a problem.
+int check_problem(const dispatch_problem_t* p) {
+    if (p == nullptr) return DISPATCH_ERR_NULL;
+    if (p->num_tokens < 0) return DISPATCH_ERR_ARG;
+    if (p->num_topk < 1 || p->num_topk > DISPATCH_MAX_TOPK) return DISPATCH_ERR_ARG;
+    if (p->num_experts < 1 || p->num_experts > DISPATCH_MAX_EXPERTS) return DISPATCH_ERR_ARG;
+    if (p->num_ranks < 1 || p->num_ranks > p->num_experts || p->num_experts % p->num_ranks != 0)
+        return DISPATCH_ERR_ARG;
+    if (p->expert_alignment < 1) return DISPATCH_ERR_ARG;
+    if (p->topk_idx_bytes != 4 && p->topk_idx_bytes != 8) return DISPATCH_ERR_ARG;
+    if (p->sf_per_token < 0) return DISPATCH_ERR_ARG;
+    if (p->recv_capacity_rows < 0 || p->rank_capacity_rows < 0) return DISPATCH_ERR_ARG;
+    if ((p->flags & ~uint32_t(DISPATCH_ALL_OUTPUTS)) != 0 || p->reserved != 0) return DISPATCH_ERR_ARG;
+    // Slots and row counts are int32: the worst case must fit.
+    const int64_t worst = p->num_tokens * p->num_topk + int64_t(p->num_experts) * (p->expert_alignment - 1);
+    if (p->num_tokens > INT32_MAX || worst > INT32_MAX) return DISPATCH_ERR_ARG;
+    return DISPATCH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dispatch_abi_version(void) { return DISPATCH_ABI_VERSION; }
+
+const char* dispatch_strerror(int code) {
+    switch (code) {
+        case DISPATCH_OK: return "success";
+        case DISPATCH_ERR_NULL: return "a required pointer is NULL";
+        case DISPATCH_ERR_ARG: return "a size, count or flag is out of range";
+        case DISPATCH_ERR_ALIGN: return "row_bytes is not a multiple of 16 or a pointer is misaligned";
+        case DISPATCH_ERR_WORKSPACE: return "workspace is missing, too small or not 256-byte aligned";
+        case DISPATCH_ERR_HIP: return "the HIP runtime refused a kernel launch";
+        default: return "unknown dispatch error code";
+    }
+}
+
+int dispatch_workspace_size(const dispatch_problem_t* problem, size_t* bytes) {
+    int rc = check_problem(problem);
+    if (rc != DISPATCH_OK) return rc;
+    if (bytes == nullptr) return DISPATCH_ERR_NULL;
+    const TileGeometry g = moe_dispatch::make_geometry(problem->num_tokens, problem->num_topk,
+                                                       problem->num_experts, problem->num_ranks);
+    *bytes = moe_dispatch::workspace_bytes(g);
+    return DISPATCH_OK;
+}
+
+int dispatch_max_rows(const dispatch_problem_t* problem, int64_t* max_recv_rows, int64_t* max_rank_rows) {
+    int rc = check_problem(problem);
+    if (rc != DISPATCH_OK) return rc;
+    const int64_t k_or_r = problem->num_topk < problem->num_ranks ? problem->num_topk : problem->num_ranks;
+    if (max_recv_rows)
+        *max_recv_rows = problem->num_tokens * problem->num_topk +
+                         int64_t(problem->num_experts) * (problem->expert_alignment - 1);
+    if (max_rank_rows) *max_rank_rows = problem->num_tokens * k_or_r;
+    return DISPATCH_OK;
+}
+
+int dispatch_layout(const dispatch_problem_t* problem, const void* topk_idx, const dispatch_layout_t* out,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_problem(problem);
+    if (rc != DISPATCH_OK) return rc;
+    const dispatch_problem_t& p = *problem;
+    if (out == nullptr) return DISPATCH_ERR_NULL;
+    if (!out->expert_count || !out->rank_count || !out->expert_psum || !out->rank_psum || !out->status)
+        return DISPATCH_ERR_NULL;
+    if (p.num_tokens > 0 && (!topk_idx || !out->expert_slot || !out->rank_slot)) return DISPATCH_ERR_NULL;
+    if (p.recv_capacity_rows > 0 && !out->recv_src_token_idx) return DISPATCH_ERR_NULL;
+    if (p.rank_capacity_rows > 0 && !out->rank_src_token_idx) return DISPATCH_ERR_NULL;
+    if (workspace == nullptr) return DISPATCH_ERR_WORKSPACE;
+
+    if (topk_idx && !aligned_to(topk_idx, p.topk_idx_bytes)) return DISPATCH_ERR_ALIGN;
+    const void* ints[] = {out->expert_count, out->rank_count, out->expert_psum, out->rank_psum,
+                          out->expert_slot, out->rank_slot, out->recv_src_token_idx,
+                          out->rank_src_token_idx, out->status};
+    for (const void* q : ints)
+        if (q && !aligned_to(q, 4)) return DISPATCH_ERR_ALIGN;
+    if (!aligned_to(workspace, 256)) return DISPATCH_ERR_WORKSPACE;
+
+    const TileGeometry g = moe_dispatch::make_geometry(p.num_tokens, p.num_topk, p.num_experts, p.num_ranks);
+    if (workspace_bytes < moe_dispatch::workspace_bytes(g)) return DISPATCH_ERR_WORKSPACE;
+
+    if (moe_dispatch::launch_layout(p, g, topk_idx, *out, workspace, stream) != hipSuccess)
+        return DISPATCH_ERR_HIP;
+    return DISPATCH_OK;
+}
+
+int dispatch_scatter(const dispatch_problem_t* problem, const dispatch_layout_t* layout, const void* x,
+                     const float* x_sf, void* rank_x, float* rank_sf, void* recv_x, float* recv_sf,
+                     hipStream_t stream) {
+    int rc = check_problem(problem);
+    if (rc != DISPATCH_OK) return rc;
+    const dispatch_problem_t& p = *problem;
+    if (p.row_bytes <= 0) return DISPATCH_ERR_ARG;
+    if (p.row_bytes % 16 != 0) return DISPATCH_ERR_ALIGN;
+    if (layout == nullptr || !layout->status || !layout->expert_count || !layout->expert_psum)
+        return DISPATCH_ERR_NULL;
+    const bool want_rank = (p.flags & DISPATCH_RANK_CONTIG) != 0;
+    const bool want_expert = (p.flags & DISPATCH_EXPERT_MAJOR) != 0;
+    const bool want_sf = p.sf_per_token > 0;
+    if (p.num_tokens > 0) {
+        if (!x || !layout->expert_slot || !layout->rank_slot) return DISPATCH_ERR_NULL;
+        if (want_sf && !x_sf) return DISPATCH_ERR_NULL;
+    }
+    if (want_rank && p.rank_capacity_rows > 0 && (!rank_x || (want_sf && !rank_sf))) return DISPATCH_ERR_NULL;
+    if (want_expert && p.recv_capacity_rows > 0 && (!recv_x || (want_sf && !recv_sf))) return DISPATCH_ERR_NULL;
+    const void* rows[] = {x, rank_x, recv_x};
+    for (const void* q : rows)
+        if (q && !aligned_to(q, 16)) return DISPATCH_ERR_ALIGN;
+    const void* words[] = {x_sf, rank_sf, recv_sf, layout->expert_slot, layout->rank_slot,
+                           layout->expert_count, layout->expert_psum, layout->status};
+    for (const void* q : words)
+        if (q && !aligned_to(q, 4)) return DISPATCH_ERR_ALIGN;
+
+    if (moe_dispatch::launch_scatter(p, *layout, x, x_sf, rank_x, rank_sf, recv_x, recv_sf, stream) != hipSuccess)
+        return DISPATCH_ERR_HIP;
+    return DISPATCH_OK;
+}
+
+}  // extern "C"

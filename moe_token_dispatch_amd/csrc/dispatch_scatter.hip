@@ -1,0 +1,209 @@
+// Row scatter on gfx950: copy each token row into its rank-contiguous rows and
+// its expert-major rows, and zero the alignment pad rows.
+//
+// This is the data move of the method ("DeepEP Counting Sort / Bucketization"
+// page): the rank-level copy of sections 6.2-6.3, the expert-major copy of the
+// expand mode (sections 6.4 and 8.2) and the zero padding of section 7.3. It
+// moves nearly all of the bytes, so it is built for HBM bandwidth: one
+// wavefront per token reads the row once, 16 bytes per lane per instruction,
+// holds it in registers and writes it to every destination row of that token
+// (the read-once / write-to-many-destinations copy of the "Symmetric Memory"
+// page's sender warp, here to local rows). Destination slots come from the
+// layout's expert_slot / rank_slot, which are wavefront-uniform, so the
+// destination loop runs on scalar registers. Pad rows are cleared by extra
+// wavefronts after the token wavefronts, a few rows each.
+#include "dispatch_common.hpp"
+
+namespace moe_dispatch {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kScatterWaves = 4;  // wavefronts per 256-thread workgroup
+constexpr int kPadRowsPerWave = 8;
+
+struct ScatterParams {
+    int64_t num_tokens;
+    int64_t row_vecs;        // row_bytes / 16
+    int64_t token_waves;     // num_tokens rounded up to whole workgroups
+    int64_t recv_capacity;   // rows of recv_x / recv_sf
+    int64_t rank_capacity;   // rows of rank_x / rank_sf
+    int32_t num_topk;
+    int32_t sf_per_token;
+    int32_t num_experts;
+    int32_t pad_waves_per_expert;
+    int32_t write_rank;      // rank_x / rank_sf requested
+    int32_t write_expert;    // recv_x / recv_sf requested
+};
+
+__device__ __forceinline__ void store_row_part(u32x4* __restrict__ dst, const u32x4& v) {
+    __builtin_nontemporal_store(v, dst);
+}
+
+template <int V>
+__device__ __forceinline__ void copy_token(const u32x4* __restrict__ x, const uint32_t* __restrict__ x_sf,
+                                           const ScatterParams& p, int64_t t, int lane,
+                                           const int32_t* __restrict__ expert_slot,
+                                           const int32_t* __restrict__ rank_slot,
+                                           u32x4* __restrict__ rank_x, uint32_t* __restrict__ rank_sf,
+                                           u32x4* __restrict__ recv_x, uint32_t* __restrict__ recv_sf) {
+    const int K = p.num_topk;
+    int es = -1, rs = -1;
+    if (lane < K) {
+        es = expert_slot[t * K + lane];
+        rs = rank_slot[t * K + lane];
+    }
+    // Slots past the capacities never occur for a layout with status 0; they
+    // are dropped here so that no store can leave the output buffers.
+    if (!p.write_expert || es >= p.recv_capacity) es = -1;
+    if (!p.write_rank || rs >= p.rank_capacity) rs = -1;
+    const int64_t nv = p.row_vecs;
+    const u32x4* src = x + t * nv;
+    for (int64_t base = 0; base < nv; base += (int64_t)kWave * V) {
+        u32x4 v[V];
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            const int64_t i = base + j * kWave + lane;
+            if (i < nv) v[j] = __builtin_nontemporal_load(src + i);
+        }
+        for (int k = 0; k < K; ++k) {
+            const int d_expert = __builtin_amdgcn_readlane(es, k);
+            if (d_expert >= 0) {
+                u32x4* dst = recv_x + (int64_t)d_expert * nv;
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    const int64_t i = base + j * kWave + lane;
+                    if (i < nv) store_row_part(dst + i, v[j]);
+                }
+            }
+            const int d_rank = __builtin_amdgcn_readlane(rs, k);
+            if (d_rank >= 0) {
+                u32x4* dst = rank_x + (int64_t)d_rank * nv;
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    const int64_t i = base + j * kWave + lane;
+                    if (i < nv) store_row_part(dst + i, v[j]);
+                }
+            }
+        }
+    }
+    const int S = p.sf_per_token;
+    for (int s0 = 0; s0 < S; s0 += kWave) {
+        const int i = s0 + lane;
+        const uint32_t v = i < S ? x_sf[t * S + i] : 0u;
+        for (int k = 0; k < K; ++k) {
+            const int d_expert = __builtin_amdgcn_readlane(es, k);
+            if (d_expert >= 0 && i < S) recv_sf[(int64_t)d_expert * S + i] = v;
+            const int d_rank = __builtin_amdgcn_readlane(rs, k);
+            if (d_rank >= 0 && i < S) rank_sf[(int64_t)d_rank * S + i] = v;
+        }
+    }
+}
+
+__device__ __forceinline__ void zero_pads(const ScatterParams& p, int64_t pad_wave, int lane,
+                                          const int32_t* __restrict__ expert_count,
+                                          const int32_t* __restrict__ expert_psum,
+                                          u32x4* __restrict__ recv_x, uint32_t* __restrict__ recv_sf) {
+    const int e = (int)(pad_wave / p.pad_waves_per_expert);
+    if (e >= p.num_experts) return;
+    const int sub = (int)(pad_wave - (int64_t)e * p.pad_waves_per_expert);
+    const int64_t first = (int64_t)expert_psum[e] + expert_count[e] + (int64_t)sub * kPadRowsPerWave;
+    const int64_t end = min(min(first + kPadRowsPerWave, (int64_t)expert_psum[e + 1]), p.recv_capacity);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const int S = p.sf_per_token;
+    for (int64_t row = first; row < end; ++row) {
+        u32x4* dst = recv_x + row * p.row_vecs;
+        for (int64_t i = lane; i < p.row_vecs; i += kWave) store_row_part(dst + i, zero);
+        for (int i = lane; i < S; i += kWave) recv_sf[row * S + i] = 0u;
+    }
+}
+
+template <int V>
+__global__ void __launch_bounds__(kScatterWaves * kWave)
+scatter_kernel(const u32x4* __restrict__ x, const uint32_t* __restrict__ x_sf, ScatterParams p,
+               const int32_t* __restrict__ expert_slot, const int32_t* __restrict__ rank_slot,
+               const int32_t* __restrict__ expert_count, const int32_t* __restrict__ expert_psum,
+               const int32_t* __restrict__ status, u32x4* __restrict__ rank_x,
+               uint32_t* __restrict__ rank_sf, u32x4* __restrict__ recv_x, uint32_t* __restrict__ recv_sf) {
+    if (*status != 0) return;  // the layout is unspecified: write nothing
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave_id = (int64_t)blockIdx.x * kScatterWaves +
+                            __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (wave_id < p.token_waves) {
+        if (wave_id < p.num_tokens)
+            copy_token<V>(x, x_sf, p, wave_id, lane, expert_slot, rank_slot, rank_x, rank_sf, recv_x, recv_sf);
+    } else {
+        zero_pads(p, wave_id - p.token_waves, lane, expert_count, expert_psum, recv_x, recv_sf);
+    }
+}
+
+template <int V>
+hipError_t launch_v(dim3 grid, hipStream_t stream, const u32x4* x, const uint32_t* x_sf, ScatterParams p,
+                    const int32_t* expert_slot, const int32_t* rank_slot, const int32_t* expert_count,
+                    const int32_t* expert_psum, const int32_t* status, u32x4* rank_x, uint32_t* rank_sf,
+                    u32x4* recv_x, uint32_t* recv_sf) {
+    void* args[] = {&x, &x_sf, &p, &expert_slot, &rank_slot, &expert_count, &expert_psum,
+                    &status, &rank_x, &rank_sf, &recv_x, &recv_sf};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&scatter_kernel<V>), grid,
+                           dim3(kScatterWaves * kWave), args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_scatter(const dispatch_problem_t& prob, const dispatch_layout_t& lay, const void* x,
+                          const float* x_sf, void* rank_x, float* rank_sf, void* recv_x, float* recv_sf,
+                          hipStream_t stream) {
+    ScatterParams p{};
+    p.num_tokens = prob.num_tokens;
+    p.row_vecs = prob.row_bytes / 16;
+    p.token_waves = (prob.num_tokens + kScatterWaves - 1) / kScatterWaves * kScatterWaves;
+    p.recv_capacity = prob.recv_capacity_rows;
+    p.rank_capacity = prob.rank_capacity_rows;
+    p.num_topk = prob.num_topk;
+    p.sf_per_token = prob.sf_per_token;
+    p.num_experts = prob.num_experts;
+    p.write_rank = (prob.flags & DISPATCH_RANK_CONTIG) != 0;
+    p.write_expert = (prob.flags & DISPATCH_EXPERT_MAJOR) != 0;
+    const bool pads = p.write_expert && (prob.flags & DISPATCH_ZERO_PAD) && prob.expert_alignment > 1;
+    p.pad_waves_per_expert = pads ? (prob.expert_alignment - 1 + kPadRowsPerWave - 1) / kPadRowsPerWave : 1;
+    const int64_t pad_waves = pads ? (int64_t)prob.num_experts * p.pad_waves_per_expert : 0;
+    const int64_t blocks = (p.token_waves + pad_waves + kScatterWaves - 1) / kScatterWaves;
+    if (blocks == 0) return hipSuccess;
+    const dim3 grid((unsigned)blocks);
+    const int64_t per_lane = (p.row_vecs + kWave - 1) / kWave;
+    const int v = per_lane < 1 ? 1 : (per_lane > 16 ? 16 : (int)per_lane);
+
+    auto* xs = static_cast<const u32x4*>(x);
+    auto* sfs = reinterpret_cast<const uint32_t*>(x_sf);
+    auto* rx = static_cast<u32x4*>(rank_x);
+    auto* rsf = reinterpret_cast<uint32_t*>(rank_sf);
+    auto* ex = static_cast<u32x4*>(recv_x);
+    auto* esf = reinterpret_cast<uint32_t*>(recv_sf);
+#define MOE_DISPATCH_SCATTER_CASE(N)                                                                   \
+    case N:                                                                                            \
+        return launch_v<N>(grid, stream, xs, sfs, p, lay.expert_slot, lay.rank_slot, lay.expert_count, \
+                           lay.expert_psum, lay.status, rx, rsf, ex, esf);
+    switch (v) {
+        MOE_DISPATCH_SCATTER_CASE(1)
+        MOE_DISPATCH_SCATTER_CASE(2)
+        MOE_DISPATCH_SCATTER_CASE(3)
+        MOE_DISPATCH_SCATTER_CASE(4)
+        MOE_DISPATCH_SCATTER_CASE(5)
+        MOE_DISPATCH_SCATTER_CASE(6)
+        MOE_DISPATCH_SCATTER_CASE(7)
+        MOE_DISPATCH_SCATTER_CASE(8)
+        MOE_DISPATCH_SCATTER_CASE(9)
+        MOE_DISPATCH_SCATTER_CASE(10)
+        MOE_DISPATCH_SCATTER_CASE(11)
+        MOE_DISPATCH_SCATTER_CASE(12)
+        MOE_DISPATCH_SCATTER_CASE(13)
+        MOE_DISPATCH_SCATTER_CASE(14)
+        MOE_DISPATCH_SCATTER_CASE(15)
+        default:
+            return launch_v<16>(grid, stream, xs, sfs, p, lay.expert_slot, lay.rank_slot, lay.expert_count,
+                                lay.expert_psum, lay.status, rx, rsf, ex, esf);
+    }
+#undef MOE_DISPATCH_SCATTER_CASE
+}
+
+}  // namespace moe_dispatch

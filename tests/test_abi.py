@@ -1,0 +1,141 @@
+"""The C ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments with the documented host error codes before touching the
+GPU (no compute call runs here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_token_dispatch_amd as M
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe_dispatch.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(dispatch_\w+)\s*\(", text, flags=re.M)))
+
+
+def _defines():
+    out = {}
+    for name, val in re.findall(r"#define\s+(DISPATCH_\w+)\s+\(?(-?\d+)u?\)?", open(HEADER).read()):
+        out[name] = int(val)
+    return out
+
+
+def test_library_exports_every_declared_symbol():
+    lib = M.load_library()
+    declared = _declared_functions()
+    assert set(declared) == set(M.SYMBOLS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_binding_constants_match_header():
+    d = _defines()
+    assert d["DISPATCH_ABI_VERSION"] == M.dispatch_abi_version() == 1
+    assert (d["DISPATCH_ERR_NULL"], d["DISPATCH_ERR_ARG"], d["DISPATCH_ERR_ALIGN"],
+            d["DISPATCH_ERR_WORKSPACE"], d["DISPATCH_ERR_HIP"]) == (
+        M.ERR_NULL, M.ERR_ARG, M.ERR_ALIGN, M.ERR_WORKSPACE, M.ERR_HIP)
+    assert (d["DISPATCH_STATUS_BAD_EXPERT"], d["DISPATCH_STATUS_RECV_OVERFLOW"],
+            d["DISPATCH_STATUS_RANK_OVERFLOW"], d["DISPATCH_STATUS_DUP_EXPERT"]) == (
+        M.STATUS_BAD_EXPERT, M.STATUS_RECV_OVERFLOW, M.STATUS_RANK_OVERFLOW, M.STATUS_DUP_EXPERT)
+    assert (d["DISPATCH_RANK_CONTIG"], d["DISPATCH_EXPERT_MAJOR"], d["DISPATCH_ZERO_PAD"]) == (
+        M.RANK_CONTIG, M.EXPERT_MAJOR, M.ZERO_PAD)
+    assert d["DISPATCH_MAX_TOPK"] == M.MAX_TOPK and d["DISPATCH_MAX_EXPERTS"] == M.MAX_EXPERTS
+    assert ctypes.sizeof(M.Problem) == 64 and ctypes.sizeof(M.LayoutPtrs) == 9 * 8
+
+
+def test_strerror_covers_codes():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert M.dispatch_strerror(code) and "unknown" not in M.dispatch_strerror(code)
+    assert "unknown" in M.dispatch_strerror(-99)
+
+
+def test_max_rows_and_workspace():
+    p = M.make_problem(4096, 8, 256, 8, 1, row_bytes=14336)
+    assert M.dispatch_max_rows(p) == (4096 * 8, 4096 * 8)
+    p = M.make_problem(65536, 8, 256, 8, 128, row_bytes=7168, sf_per_token=56)
+    assert M.dispatch_max_rows(p) == (65536 * 8 + 256 * 127, 65536 * 8)
+    p = M.make_problem(100, 8, 64, 4, 4, row_bytes=64)
+    assert M.dispatch_max_rows(p) == (800 + 64 * 3, 400)  # min(K, R) = 4 rank rows per token
+    ws = M.dispatch_workspace_size(p)
+    assert ws >= 256 and ws % 256 == 0
+    # Workspace grows with the number of tiles and keys.
+    assert M.dispatch_workspace_size(M.make_problem(1 << 20, 8, 256, 8)) > ws
+
+
+BAD_PROBLEMS = [
+    dict(num_tokens=-1), dict(num_topk=0), dict(num_topk=33), dict(num_experts=0),
+    dict(num_experts=4097), dict(num_ranks=3), dict(num_ranks=0), dict(num_ranks=512),
+    dict(expert_alignment=0), dict(topk_idx_bytes=2), dict(sf_per_token=-1), dict(flags=8),
+    dict(recv_capacity_rows=-1), dict(reserved=1), dict(num_tokens=1 << 31),
+    dict(num_tokens=1 << 28, expert_alignment=1 << 20),
+]
+
+
+@pytest.mark.parametrize("bad", BAD_PROBLEMS)
+def test_bad_problem_rejected(bad):
+    p = M.Problem(100, 8, 256, 8, 1, 8, 0, 64, 1000, 1000, M.ALL_OUTPUTS, 0)
+    for k, v in bad.items():
+        setattr(p, k, v)
+    lib = M.load_library()
+    size = ctypes.c_size_t(0)
+    assert lib.dispatch_workspace_size(ctypes.byref(p), ctypes.byref(size)) == M.ERR_ARG
+    lay = M.LayoutPtrs(*([16] * 9))
+    assert lib.dispatch_layout(ctypes.byref(p), 16, ctypes.byref(lay), 256, 1 << 20, None) == M.ERR_ARG
+    assert lib.dispatch_scatter(ctypes.byref(p), ctypes.byref(lay), 16, 16, 16, 16, 16, 16, None) == M.ERR_ARG
+
+
+def test_host_errors_before_launch():
+    """Null, alignment and workspace errors come back without any GPU work."""
+    lib = M.load_library()
+    p = M.Problem(100, 8, 256, 8, 1, 8, 4, 64, 1000, 1000, M.ALL_OUTPUTS, 0)
+    good = M.LayoutPtrs(*([4096] * 9))
+    ws_need = M.dispatch_workspace_size(p)
+    call = lambda prob, topk, lay, ws, n: lib.dispatch_layout(  # noqa: E731
+        ctypes.byref(prob) if prob is not None else None, topk,
+        ctypes.byref(lay) if lay is not None else None, ws, n, None)
+    assert call(None, 4096, good, 4096, ws_need) == M.ERR_NULL
+    assert call(p, None, good, 4096, ws_need) == M.ERR_NULL
+    assert call(p, 4096, None, 4096, ws_need) == M.ERR_NULL
+    for i in range(9):
+        lay = M.LayoutPtrs(*([4096] * 9))
+        setattr(lay, M.LayoutPtrs._fields_[i][0], None)
+        assert call(p, 4096, lay, 4096, ws_need) == M.ERR_NULL, i
+    assert call(p, 4100, good, 4096, ws_need) == M.ERR_ALIGN  # int64 table not 8-byte aligned
+    lay = M.LayoutPtrs(*([4096] * 9))
+    lay.expert_slot = 4098
+    assert call(p, 4096, lay, 4096, ws_need) == M.ERR_ALIGN
+    assert call(p, 4096, good, None, ws_need) == M.ERR_WORKSPACE
+    assert call(p, 4096, good, 4096 + 64, ws_need) == M.ERR_WORKSPACE  # not 256-byte aligned
+    assert call(p, 4096, good, 4096, ws_need - 1) == M.ERR_WORKSPACE
+
+    sc = lambda prob, lay, x, sf, rx, rsf, ex, esf: lib.dispatch_scatter(  # noqa: E731
+        ctypes.byref(prob), ctypes.byref(lay) if lay is not None else None, x, sf, rx, rsf, ex, esf, None)
+    assert sc(p, None, 4096, 4096, 4096, 4096, 4096, 4096) == M.ERR_NULL
+    assert sc(p, good, None, 4096, 4096, 4096, 4096, 4096) == M.ERR_NULL
+    assert sc(p, good, 4096, None, 4096, 4096, 4096, 4096) == M.ERR_NULL  # S > 0 needs x_sf
+    assert sc(p, good, 4096, 4096, None, 4096, 4096, 4096) == M.ERR_NULL
+    assert sc(p, good, 4096, 4096, 4096, 4096, None, 4096) == M.ERR_NULL
+    assert sc(p, good, 4104, 4096, 4096, 4096, 4096, 4096) == M.ERR_ALIGN  # x not 16-byte aligned
+    assert sc(p, good, 4096, 4098, 4096, 4096, 4096, 4096) == M.ERR_ALIGN
+    p2 = M.Problem(100, 8, 256, 8, 1, 8, 4, 72, 1000, 1000, M.ALL_OUTPUTS, 0)
+    assert sc(p2, good, 4096, 4096, 4096, 4096, 4096, 4096) == M.ERR_ALIGN  # row_bytes % 16
+    p3 = M.Problem(100, 8, 256, 8, 1, 8, 4, 0, 1000, 1000, M.ALL_OUTPUTS, 0)
+    assert sc(p3, good, 4096, 4096, 4096, 4096, 4096, 4096) == M.ERR_ARG
+    # Only the selected outputs are required: with expert-major rows alone and
+    # no scale factors, NULL rank buffers pass and a misaligned recv_x is caught.
+    p4 = M.Problem(100, 8, 256, 8, 1, 8, 0, 64, 1000, 1000, M.EXPERT_MAJOR, 0)
+    assert sc(p4, good, 4096, None, None, None, 4104, None) == M.ERR_ALIGN
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+
+    p = M.make_problem(4, 2, 8, 2, 1, row_bytes=16)
+    with pytest.raises(ValueError):
+        M.dispatch_layout(p, torch.zeros((4, 2), dtype=torch.int64), None, torch.zeros(256, dtype=torch.uint8))

@@ -1,0 +1,190 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, bit for bit.
+
+Every count, psum, slot, inverse-map entry, status bit and copied byte must
+equal the oracle's. Canary bands check that nothing past the totals is
+written. Runs on an MI355X only (marked ``gpu``).
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _banner(msg):
+    print(f"\n[gpu-parity] {msg}", flush=True)
+
+
+def _reduced(w: W.Workload, t: int) -> W.Workload:
+    return dataclasses.replace(w, name=f"{w.name}_T{t}", num_tokens=t)
+
+
+def _check_full(w: W.Workload, topk_bytes: int = 8):
+    inp = W.make_inputs(w)
+    xb = inp.x_bytes()
+    ref = oracle.layout(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment)
+    run = H.run_gpu(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment, xb, inp.x_sf,
+                    topk_bytes=topk_bytes)
+    H.assert_layout_equal(run, ref)
+    H.assert_rows_full(run, ref, xb, inp.x_sf)
+
+
+# Reduced-size variants of the five workloads: full element-by-element parity
+# on every output, several tiles and a ragged last tile.
+@pytest.mark.parametrize("name,t", [("tiny", 256), ("dsv3_bf16", 2500), ("dsv3_fp8_a128", 2311),
+                                    ("zipf_bf16", 3001), ("ranklocal_fp8_a128", 2777)])
+def test_reduced_workload_full_parity(name, t):
+    w = _reduced(W.get(name), t)
+    _banner(w.describe())
+    _check_full(w)
+
+
+# The five workloads at full size, in the launch configuration the benchmark
+# times: the whole layout bit-exact, rows checked against the oracle on
+# samples (full rows for the smaller ones) and on every row by a device gather.
+@pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
+def test_workload_full_size(name):
+    w = W.get(name)
+    _banner(w.describe())
+    inp = W.make_inputs(w)
+    xb = inp.x_bytes()
+    ref = oracle.layout(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment)
+    run = H.run_gpu(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment, xb, inp.x_sf)
+    H.assert_layout_equal(run, ref)
+    if w.num_tokens * w.row_bytes <= 64 << 20:
+        H.assert_rows_full(run, ref, xb, inp.x_sf)
+    else:
+        H.assert_rows_sampled(run, ref, xb, inp.x_sf)
+    H.assert_rows_gather_property(run, ref)
+
+
+def _edge(topk, e, r, a, row_bytes=64, s=0, seed=0, **kw):
+    t = topk.shape[0]
+    xb = H.random_rows(seed, t, row_bytes)
+    sf = None if s == 0 else np.random.default_rng([seed, 7]).uniform(0.5, 2, (t, s)).astype(np.float32)
+    ref = oracle.layout(topk, e, r, a, recv_capacity=kw.get("recv_capacity"),
+                        rank_capacity=kw.get("rank_capacity"))
+    run = H.run_gpu(topk, e, r, a, xb, sf, **kw)
+    H.assert_layout_equal(run, ref)
+    if ref.status == 0:
+        H.assert_rows_full(run, ref, xb, sf)
+    return run, ref
+
+
+def _uniform(seed, t, k, e, mask=0.0):
+    w = W.Workload("edge", t, 64, "bf16", False, e, 1, k, mask_frac=mask, seed=seed)
+    return W.make_topk(w)
+
+
+@pytest.mark.parametrize("t", [0, 1, 2, 63, 64, 65, 1023, 1024, 1025])
+def test_token_counts_around_tiles(t):
+    _banner(f"T={t}")
+    _edge(_uniform(3, t, 8, 256, 0.05), 256, 8, 4)
+
+
+@pytest.mark.parametrize("k,e,r", [(1, 8, 2), (2, 16, 16), (3, 12, 4), (6, 64, 8), (7, 128, 128),
+                                   (16, 64, 4), (32, 64, 8), (32, 32, 32), (5, 4096, 64), (8, 4096, 4096)])
+def test_topk_and_expert_shapes(k, e, r):
+    _banner(f"K={k} E={e} R={r}")
+    _edge(_uniform(5, 777, k, e, 0.1), e, r, 3, row_bytes=48)
+
+
+@pytest.mark.parametrize("a", [1, 2, 3, 64, 128, 1000])
+def test_alignments(a):
+    _banner(f"A={a}")
+    _edge(_uniform(6, 900, 8, 64, 0.02), 64, 8, a, row_bytes=80, s=5)
+
+
+def test_fully_masked_tokens():
+    topk = _uniform(7, 500, 4, 32)
+    topk[::3] = -1
+    topk[1::7, :2] = -5  # any negative value is masked
+    _edge(topk, 32, 4, 8)
+
+
+def test_all_tokens_on_few_experts():
+    w = W.Workload("single", 3000, 64, "bf16", False, 128, 16, 8, routing=W.ROUTING_SINGLE)
+    _edge(W.make_topk(w), 128, 16, 64)
+
+
+def test_one_expert_per_rank_and_one_rank():
+    _edge(_uniform(8, 1500, 8, 64), 64, 64, 1)
+    _edge(_uniform(9, 1500, 8, 64), 64, 1, 2)
+
+
+def test_int32_routing_table():
+    w = _reduced(W.get("dsv3_bf16"), 1800)
+    _banner("int32 topk")
+    _check_full(w, topk_bytes=4)
+
+
+@pytest.mark.parametrize("row_bytes,s", [(16, 1), (208, 3), (1040, 70), (32768, 0), (40976, 130)])
+def test_row_and_scale_factor_widths(row_bytes, s):
+    _banner(f"row_bytes={row_bytes} S={s}")
+    _edge(_uniform(10, 300, 4, 32, 0.1), 32, 4, 4, row_bytes=row_bytes, s=s)
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3, 6, 7])
+def test_output_selection(flags):
+    _banner(f"flags={flags}")
+    _edge(_uniform(11, 400, 8, 64, 0.05), 64, 8, 16, row_bytes=96, s=2, flags=flags)
+
+
+def test_status_bad_expert_writes_nothing():
+    topk = _uniform(12, 300, 4, 16)
+    topk[123, 2] = 16
+    run, ref = _edge(topk, 16, 4, 1)
+    assert ref.status == oracle.BAD_EXPERT
+    assert np.all(run.layout.expert_slot.cpu().numpy() == H.CANARY)
+    for name in ("rank_x", "recv_x"):
+        assert np.all(getattr(run.rows, name).cpu().numpy() == H.ROW_FILL)
+
+
+def test_status_duplicate_expert():
+    topk = _uniform(13, 300, 4, 16)
+    topk[77, 3] = topk[77, 0]
+    run, ref = _edge(topk, 16, 4, 2)
+    assert ref.status == oracle.DUP_EXPERT
+
+
+def test_status_capacity_overflow_writes_nothing():
+    topk = _uniform(14, 600, 8, 64)
+    mr, mk = oracle.max_rows(600, 8, 64, 8, 4)
+    full = oracle.layout(topk, 64, 8, 4)
+    run, ref = _edge(topk, 64, 8, 4, recv_capacity=full.num_recv_rows - 1, rank_capacity=mk)
+    assert ref.status == oracle.RECV_OVERFLOW
+    assert np.all(run.rows.recv_x.cpu().numpy() == H.ROW_FILL)
+    run, ref = _edge(topk, 64, 8, 4, recv_capacity=mr, rank_capacity=full.num_rank_rows - 1)
+    assert ref.status == oracle.RANK_OVERFLOW
+    assert np.all(run.rows.rank_x.cpu().numpy() == H.ROW_FILL)
+    _edge(topk, 64, 8, 4, recv_capacity=full.num_recv_rows, rank_capacity=full.num_rank_rows)
+
+
+def test_deterministic_repeats_and_workspace_reuse():
+    """Ten runs give identical bits; one workspace serves calls of different sizes."""
+    w = W.get("dsv3_bf16")
+    inp = W.make_inputs(w)
+    xb = inp.x_bytes()
+    ref = oracle.layout(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment)
+    first = H.run_gpu(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment, xb)
+    H.assert_layout_equal(first, ref)
+    ws = first.workspace
+    for i in range(10):
+        run = H.run_gpu(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment, xb, workspace=ws)
+        for f in dataclasses.fields(run.layout):
+            assert torch.equal(getattr(run.layout, f.name), getattr(first.layout, f.name)), (i, f.name)
+        assert torch.equal(run.rows.recv_x, first.rows.recv_x) and torch.equal(run.rows.rank_x, first.rows.rank_x)
+    small = _uniform(15, 333, 8, 256, 0.05)
+    ref_s = oracle.layout(small, 256, 8, 1)
+    run_s = H.run_gpu(small, 256, 8, 1, H.random_rows(1, 333, 64), workspace=ws)
+    H.assert_layout_equal(run_s, ref_s)
+    run = H.run_gpu(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment, xb, workspace=ws)
+    H.assert_layout_equal(run, ref)
+    assert not bool(ws[:8].any()), "workspace control words not left zero"
