@@ -1,0 +1,278 @@
+"""Throughput of MoE dispatch (layout + scatter) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole dispatch hot path over one batch: the layout
+(count, prefix sums, stable slots, inverse maps) and the row scatter into the
+rank-contiguous and expert-major buffers, on inputs already resident in HBM.
+The default workload is 4096 tokens x 7168 bf16, top-8 of 256 experts in 8
+logical ranks with 5% of the routing entries masked.
+
+Prints one JSON line with the throughput in algorithmic GB/s (bytes the method
+must move per step / wall time per step), the scatter kernel's roofline
+(achieved bandwidth against the 8 TB/s HBM peak, timed with HIP events on the
+stream the kernel runs on) and the CPU oracle's throughput on the same input
+as a baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "dispatch GB/s & % HBM peak, 4096 tok×7168 bf16, top-8 of 256 experts"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scatter_traffic.json")
+SCATTER_SOURCES = [os.path.join(ROOT, "moe_token_dispatch_amd", "csrc", f)
+                   for f in ("dispatch_scatter.hip", "dispatch_common.hpp")]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=500)
+    ap.add_argument("--workload", default=None, help="workload name (default: the metric workload)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for counter calibration)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(t, k, e, r, idx_bytes, row_bytes, s, t_live, p_rows, n_rank):
+    """Bytes the method must move per step (workspace traffic excluded).
+
+    Routing read + each live token row read once + every rank row and every
+    expert-major row (pads included) written + counts, psums, slot maps and
+    inverse maps written.
+    """
+    row = row_bytes + 4 * s
+    layout = t * k * idx_bytes + 4 * (2 * e + 2 * r + 2 + 2 * t * k + p_rows + n_rank)
+    scatter_rows = t_live * row + (n_rank + p_rows) * row
+    return layout + scatter_rows, layout, scatter_rows
+
+
+def scatter_launch_bytes(t, k, e, row_bytes, s, t_live, p_rows, n_rank):
+    """Algorithmic bytes of one scatter launch: live rows read once, slot maps
+    read, every destination row written (pads as zeros)."""
+    row = row_bytes + 4 * s
+    return t_live * row + (n_rank + p_rows) * row + 2 * 4 * t * k + 4 * (2 * e + 1)
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(launches_per_step=1):
+    """HBM bytes per scatter launch from committed rocprofv3 counters, or None
+    when they are missing or were taken on another version of the kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_digest(SCATTER_SOURCES):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration():
+    import torch
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    reps = 20
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copy_GBps": 2 * n / dt / 1e9}), flush=True)
+
+
+def measure_device_ceiling(torch):
+    """Practical HBM ceilings on this machine: torch's device copy and fill."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(3)
+    b = torch.empty_like(a)
+    out = {}
+    for name, fn, nbytes in (("copy", lambda: b.copy_(a), 2 * n), ("fill", lambda: b.fill_(7), n)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        out[f"{name}_GBps"] = round(nbytes * 10 / (time.perf_counter() - t0) / 1e9, 1)
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(inp, w, budget_s):
+    """The CPU oracle as it stands (single-threaded C), layout + scatter of the
+    same input, repeated until the time budget is spent."""
+    import oracle
+
+    prep = oracle.Prepared(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment, inp.x_bytes(), inp.x_sf)
+    prep.run_layout()
+    prep.run_scatter()  # warm-up
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while time.perf_counter() < t_end or len(times) < 3:
+        t0 = time.perf_counter()
+        rc = prep.run_layout()
+        rc |= prep.run_scatter()
+        times.append(time.perf_counter() - t0)
+        if rc:
+            raise RuntimeError(f"oracle status {rc}")
+    return statistics.median(times), len(times)
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the dispatch path here has no cross-GPU exchange).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import moe_token_dispatch_amd as M
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda:0"
+    w = W.get(args.workload or W.METRIC_WORKLOAD)
+    inp = W.make_inputs(w)
+    t, k = inp.topk_idx.shape
+    s = w.sf_per_token
+    prob = M.make_problem(t, k, w.num_experts, w.num_ranks, w.alignment, 8, w.row_bytes, s)
+    lay = M.alloc_layout(prob, dev)
+    ws = M.alloc_workspace(prob, dev)
+    rows = M.alloc_rows(prob, dev)
+    topk_d = torch.from_numpy(inp.topk_idx).to(dev)
+    x_d = inp.x.view(torch.uint8).to(dev)
+    sf_d = None if inp.x_sf is None else torch.from_numpy(inp.x_sf).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    plan = M.Plan(prob, topk_d, lay, ws, x_d, sf_d, rows, stream)
+
+    def step(ev=None):
+        plan.layout()
+        if ev is not None:
+            ev[0].record(stream)
+        plan.scatter()
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(lay.status.item()) != 0:
+        raise RuntimeError(f"dispatch status {int(lay.status.item())}")
+
+    # Two events per step bracket the scatter kernel on the stream it runs on;
+    # the span from one step's scatter end to the next one's scatter start is
+    # the layout plus the launch gaps.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    scatter_ms = [e[0].elapsed_time(e[1]) for e in events]
+    layout_ms = [events[i - 1][1].elapsed_time(events[i][0]) for i in range(1, len(events))] or [0.0]
+    p_rows = int(lay.expert_psum[-1].item())
+    n_rank = int(lay.rank_psum[-1].item())
+    t_live = int((inp.topk_idx >= 0).any(axis=1).sum())
+    p_valid = int((inp.topk_idx >= 0).sum())
+    total_b, layout_b, _ = algorithmic_bytes(t, k, w.num_experts, w.num_ranks, 8, w.row_bytes, s,
+                                             t_live, p_rows, n_rank)
+    sc_b = scatter_launch_bytes(t, k, w.num_experts, w.row_bytes, s, t_live, p_rows, n_rank)
+    ms_per_step = wall / args.steps * 1e3
+    value = total_b / (wall / args.steps) / 1e9
+    sc_mean_ms = statistics.mean(scatter_ms)
+    achieved = sc_b / (sc_mean_ms * 1e-3) / 1e9
+    traffic = load_traffic()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        med, reps = cpu_baseline(inp, w, args.cpu_seconds)
+        cpu = {"value": round(total_b / med / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"full {w.name} step (layout + scatter of all {t} tokens), median of {reps} runs, "
+                         "single-threaded C oracle on pre-faulted host buffers",
+               "ms_per_step": round(med * 1e3, 2)}
+
+    ceiling = measure_device_ceiling(torch)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "tokens": t, "hidden": w.hidden, "x_dtype": w.dtype,
+            "sf_per_token": s, "experts": w.num_experts, "ranks": w.num_ranks, "topk": k,
+            "routing": w.routing, "mask_frac": w.mask_frac, "expert_alignment": w.alignment,
+            "outputs": "rank-contiguous + expert-major (zero pads)", "parallelism": "single GPU",
+        },
+        "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": total_b,
+        "tokens_per_s": round(t / (wall / args.steps), 1),
+        "pairs_per_s": round(p_valid / (wall / args.steps), 1),
+        "layout_and_gaps_us_mean": round(statistics.mean(layout_ms) * 1e3, 2),
+        "scatter_us_mean": round(sc_mean_ms * 1e3, 2),
+        "rows": {"expert_major": p_rows, "rank_contig": n_rank, "live_tokens": t_live, "pairs": p_valid},
+        "roofline": {
+            "kernel": "scatter_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": sc_b,
+        },
+        "device_ceiling": ceiling,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -49,9 +49,11 @@ extern "C" {
 
 #define DISPATCH_ABI_VERSION 1
 
-/* Limits. K <= 32 follows the page's bound on the top-k width (section 4.2). */
+/* Limits. K <= 32 follows the page's bound on the top-k width (section 4.2);
+ * R <= 1024 follows its kNumMaxRanks (section 6.2). */
 #define DISPATCH_MAX_TOPK 32
 #define DISPATCH_MAX_EXPERTS 4096
+#define DISPATCH_MAX_RANKS 1024
 
 /* Host error codes (returned before any work is enqueued). */
 #define DISPATCH_OK 0
@@ -77,11 +79,11 @@ typedef struct dispatch_problem {
     int64_t num_tokens;         /* T >= 0 */
     int32_t num_topk;           /* K, 1..DISPATCH_MAX_TOPK */
     int32_t num_experts;        /* E, 1..DISPATCH_MAX_EXPERTS */
-    int32_t num_ranks;          /* R >= 1, E % R == 0 */
+    int32_t num_ranks;          /* R, 1..DISPATCH_MAX_RANKS, E % R == 0 */
     int32_t expert_alignment;   /* A >= 1; 1 = no padding (section 7.2) */
     int32_t topk_idx_bytes;     /* width of a topk_idx entry: 8 (int64) or 4 (int32) */
     int32_t sf_per_token;       /* S >= 0 fp32 scale factors per token (H/128 for fp8, else 0) */
-    int64_t row_bytes;          /* bytes per token row (H * element size), > 0, multiple of 16 */
+    int64_t row_bytes;          /* bytes per token row (H * element size), multiple of 16, 16..2^31-16 */
     int64_t recv_capacity_rows; /* rows of recv_x / recv_sf / recv_src_token_idx */
     int64_t rank_capacity_rows; /* rows of rank_x / rank_sf / rank_src_token_idx */
     uint32_t flags;             /* DISPATCH_* output selection, used by dispatch_scatter */
@@ -108,10 +110,10 @@ int dispatch_abi_version(void);
 const char* dispatch_strerror(int code);
 
 /* Bytes of device workspace dispatch_layout needs for this problem (T, K, E,
- * R are read). The workspace must be 256-byte aligned and zero-filled before
- * its first use; every completed dispatch_layout call leaves its control words
- * zero again, so it can be reused without clearing (the page's self-cleaning
- * counters, section 6.2). */
+ * R are read). The workspace must be 256-byte aligned. It holds per-tile
+ * histograms that each call rewrites before reading, so it needs no clearing,
+ * before the first call or between calls; it carries nothing from one call to
+ * the next. */
 int dispatch_workspace_size(const dispatch_problem_t* problem, size_t* bytes);
 
 /* Worst-case row counts, for sizing outputs without reading the totals back:

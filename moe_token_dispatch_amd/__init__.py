@@ -8,8 +8,8 @@ stream into the C calls.
 """
 
 from ._binding import (  # noqa: F401
-    ALL_OUTPUTS, ERR_ALIGN, ERR_ARG, ERR_HIP, ERR_NULL, ERR_WORKSPACE, EXPERT_MAJOR, MAX_EXPERTS,
-    MAX_TOPK, OK, RANK_CONTIG, STATUS_BAD_EXPERT, STATUS_DUP_EXPERT, STATUS_RANK_OVERFLOW,
+    ALL_OUTPUTS, ERR_ALIGN, ERR_ARG, ERR_HIP, ERR_NULL, ERR_WORKSPACE, EXPERT_MAJOR, MAX_EXPERTS, Plan,
+    MAX_RANKS, MAX_TOPK, OK, RANK_CONTIG, STATUS_BAD_EXPERT, STATUS_DUP_EXPERT, STATUS_RANK_OVERFLOW,
     STATUS_RECV_OVERFLOW, SYMBOLS, ZERO_PAD, DispatchError, LayoutPtrs, LayoutTensors, Problem,
     RowBuffers, alloc_layout, alloc_rows, alloc_workspace, dispatch_abi_version, dispatch_layout,
     dispatch_max_rows, dispatch_scatter, dispatch_strerror, dispatch_workspace_size, load_library,

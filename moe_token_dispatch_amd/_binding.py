@@ -15,11 +15,12 @@ from typing import Optional, Tuple
 
 import torch  # load torch's HIP runtime first so the library binds to the same one
 
-from .build import LIB_PATH
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_dispatch.so")
 
 ABI_VERSION = 1
 MAX_TOPK = 32
 MAX_EXPERTS = 4096
+MAX_RANKS = 1024
 
 OK = 0
 ERR_NULL = -1
@@ -239,9 +240,9 @@ def alloc_layout(problem: Problem, device) -> LayoutTensors:
 
 
 def alloc_workspace(problem: Problem, device) -> torch.Tensor:
-    """A zero-filled workspace (zeroed once; the library keeps its control words zero)."""
+    """Workspace for dispatch_layout (needs no clearing; torch allocations are 256-byte aligned)."""
     n = dispatch_workspace_size(problem)
-    return torch.zeros((n + 255) // 256 * 256, dtype=torch.uint8, device=device)
+    return torch.empty((n + 255) // 256 * 256, dtype=torch.uint8, device=device)
 
 
 @dataclasses.dataclass
@@ -264,3 +265,59 @@ def alloc_rows(problem: Problem, device) -> RowBuffers:
                       rank_sf=rows(problem.rank_capacity_rows, s, torch.float32, want_rank),
                       recv_x=rows(problem.recv_capacity_rows, rb, torch.uint8, want_expert),
                       recv_sf=rows(problem.recv_capacity_rows, s, torch.float32, want_expert))
+
+
+class Plan:
+    """A prepared dispatch: the problem, the tensors and the stream are checked
+    once and the C arguments are built once, so each call is a single C call.
+
+    ``layout()`` enqueues dispatch_layout, ``scatter()`` enqueues
+    dispatch_scatter, ``__call__`` does both. The tensors must stay alive and
+    keep their storage while the plan is used.
+    """
+
+    def __init__(self, problem: Problem, topk_idx: torch.Tensor, layout: LayoutTensors,
+                 workspace: torch.Tensor, x: Optional[torch.Tensor] = None,
+                 x_sf: Optional[torch.Tensor] = None, rows: Optional[RowBuffers] = None,
+                 stream: Optional[torch.cuda.Stream] = None):
+        _check_device_tensor(topk_idx, "topk_idx")
+        if topk_idx.element_size() != problem.topk_idx_bytes:
+            raise ValueError("topk_idx element width does not match problem.topk_idx_bytes")
+        _check_device_tensor(workspace, "workspace")
+        for f in dataclasses.fields(layout):
+            _check_device_tensor(getattr(layout, f.name), f.name, torch.int32)
+        self._lib = load_library()
+        self._keep = (problem, topk_idx, layout, workspace, x, x_sf, rows)
+        self._lay = layout.ptrs()
+        handle = _stream_handle(stream, topk_idx.device)
+        self._layout_args = (ctypes.byref(problem), _ptr(topk_idx), ctypes.byref(self._lay), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), handle)
+        self._scatter_args = None
+        if x is not None:
+            _check_device_tensor(x, "x")
+            rows = rows if rows is not None else RowBuffers(None, None, None, None)
+            for name in ("rank_x", "rank_sf", "recv_x", "recv_sf"):
+                t = getattr(rows, name)
+                if t is not None:
+                    _check_device_tensor(t, name)
+            if x_sf is not None:
+                _check_device_tensor(x_sf, "x_sf")
+            self._scatter_args = (ctypes.byref(problem), ctypes.byref(self._lay), _ptr(x), _ptr(x_sf),
+                                  _ptr(rows.rank_x), _ptr(rows.rank_sf), _ptr(rows.recv_x), _ptr(rows.recv_sf),
+                                  handle)
+
+    def layout(self) -> None:
+        rc = self._lib.dispatch_layout(*self._layout_args)
+        if rc:
+            raise DispatchError(rc, "dispatch_layout")
+
+    def scatter(self) -> None:
+        if self._scatter_args is None:
+            raise ValueError("this plan has no token batch to scatter")
+        rc = self._lib.dispatch_scatter(*self._scatter_args)
+        if rc:
+            raise DispatchError(rc, "dispatch_scatter")
+
+    def __call__(self) -> None:
+        self.layout()
+        self.scatter()

@@ -20,7 +20,8 @@ int check_problem(const dispatch_problem_t* p) {
     if (p->num_tokens < 0) return DISPATCH_ERR_ARG;
     if (p->num_topk < 1 || p->num_topk > DISPATCH_MAX_TOPK) return DISPATCH_ERR_ARG;
     if (p->num_experts < 1 || p->num_experts > DISPATCH_MAX_EXPERTS) return DISPATCH_ERR_ARG;
-    if (p->num_ranks < 1 || p->num_ranks > p->num_experts || p->num_experts % p->num_ranks != 0)
+    if (p->num_ranks < 1 || p->num_ranks > DISPATCH_MAX_RANKS || p->num_ranks > p->num_experts ||
+        p->num_experts % p->num_ranks != 0)
         return DISPATCH_ERR_ARG;
     if (p->expert_alignment < 1) return DISPATCH_ERR_ARG;
     if (p->topk_idx_bytes != 4 && p->topk_idx_bytes != 8) return DISPATCH_ERR_ARG;
@@ -107,7 +108,7 @@ int dispatch_scatter(const dispatch_problem_t* problem, const dispatch_layout_t*
     int rc = check_problem(problem);
     if (rc != DISPATCH_OK) return rc;
     const dispatch_problem_t& p = *problem;
-    if (p.row_bytes <= 0) return DISPATCH_ERR_ARG;
+    if (p.row_bytes <= 0 || p.row_bytes > INT32_MAX) return DISPATCH_ERR_ARG;
     if (p.row_bytes % 16 != 0) return DISPATCH_ERR_ALIGN;
     if (layout == nullptr || !layout->status || !layout->expert_count || !layout->expert_psum)
         return DISPATCH_ERR_NULL;

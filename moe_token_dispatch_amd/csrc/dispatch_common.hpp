@@ -2,12 +2,12 @@
 //
 // Tile geometry of the layout pass. The routing table is cut into tiles of
 // consecutive tokens, one workgroup per tile. A workgroup holds W wavefronts;
-// wavefront w owns a sub-tile of CHUNKS chunks, and a chunk packs
-// floor(64 / K) tokens x K top-k entries into the 64 lanes of a wavefront, one
-// lane per (token, k) pair, in (token, k) order. Processing chunks in order
-// inside a wavefront, sub-tiles in order inside a tile and tiles in order
-// inside the batch walks the pairs in ascending token order, which is what
-// makes the slots stable without any order-dependent atomics.
+// wavefront w owns CH consecutive chunks, and a chunk packs floor(64 / K)
+// tokens x K top-k entries into the 64 lanes of a wavefront, one lane per
+// (token, k) pair, in (token, k) order. Ranking chunks in order inside a
+// wavefront, wavefronts in order inside a tile and tiles in order inside the
+// batch walks the pairs in ascending token order, which is what makes the
+// slots stable without any order-dependent atomics.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,29 +17,27 @@
 
 namespace moe_dispatch {
 
-constexpr int kWave = 64;            // gfx950 wavefront width
-constexpr int kChunksPerWave = 8;    // chunks per wavefront sub-tile
-constexpr int kMaxWavesPerTile = 16; // 1024-thread workgroups
-constexpr int kLdsBudgetInts = 16000; // per-wavefront key counters, under 64 KiB of LDS
-constexpr size_t kWorkspaceHeader = 256;
-
-// Workspace control words (zero between calls; the last workgroup of the
-// count kernel resets them).
-struct WorkspaceHeader {
-    uint32_t ticket;     // workgroups of the count kernel that have finished
-    uint32_t error_bits; // DISPATCH_STATUS_* bits raised by any workgroup
-};
+constexpr int kWave = 64;             // gfx950 wavefront width
+constexpr int kLayoutThreads = 256;   // at most 4 wavefronts per layout workgroup
+constexpr int kScanSegments = 16;     // wavefronts per column-scan workgroup
+constexpr int kMaxTilesTarget = 512;  // more chunks per wavefront beyond this many tiles
+constexpr int kLdsBudgetInts = 16000; // LDS ints per workgroup for key arrays, under 64 KiB
 
 struct TileGeometry {
     int64_t num_tokens;
     int32_t num_topk;
     int32_t tokens_per_chunk;   // floor(64 / K)
-    int32_t tokens_per_wave;    // tokens_per_chunk * kChunksPerWave
+    int32_t chunks_per_wave;    // CH: 1, 2, 4 or 8
+    int32_t tokens_per_wave;    // tokens_per_chunk * CH
     int32_t waves_per_tile;     // W
     int32_t tokens_per_tile;    // W * tokens_per_wave
     int32_t num_tiles;          // >= 1
     int32_t num_keys;           // E + R: expert keys first, then rank keys
-    size_t hist_bytes;          // one [num_tiles][num_keys] int32 table, 256-byte padded
+    size_t ws_tile_hist;        // workspace byte offsets of the arrays below
+    size_t ws_tile_prefix;
+    size_t ws_totals;
+    size_t ws_tile_err;
+    size_t ws_bytes;
 };
 
 inline size_t round_up_256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -50,19 +48,36 @@ inline TileGeometry make_geometry(int64_t num_tokens, int32_t num_topk, int32_t 
     g.num_tokens = num_tokens;
     g.num_topk = num_topk;
     g.tokens_per_chunk = kWave / num_topk;
-    g.tokens_per_wave = g.tokens_per_chunk * kChunksPerWave;
     g.num_keys = num_experts + num_ranks;
-    int w = kLdsBudgetInts / g.num_keys;
-    g.waves_per_tile = w < 1 ? 1 : (w > kMaxWavesPerTile ? kMaxWavesPerTile : w);
+    // The assign kernel holds W wavefront counter rows plus two more rows of
+    // num_keys ints in LDS.
+    int w = kLdsBudgetInts / g.num_keys - 2;
+    const int max_w = kLayoutThreads / kWave;
+    g.waves_per_tile = w < 1 ? 1 : (w > max_w ? max_w : w);
+    // Few chunks per wavefront keep the layout spread over many CUs; more
+    // chunks once the tile count would make the column scan long.
+    g.chunks_per_wave = 1;
+    while (g.chunks_per_wave < 8) {
+        const int64_t per_tile = (int64_t)g.waves_per_tile * g.chunks_per_wave * g.tokens_per_chunk;
+        if ((num_tokens + per_tile - 1) / per_tile <= kMaxTilesTarget) break;
+        g.chunks_per_wave *= 2;
+    }
+    g.tokens_per_wave = g.tokens_per_chunk * g.chunks_per_wave;
     g.tokens_per_tile = g.waves_per_tile * g.tokens_per_wave;
-    int64_t tiles = (num_tokens + g.tokens_per_tile - 1) / g.tokens_per_tile;
+    const int64_t tiles = (num_tokens + g.tokens_per_tile - 1) / g.tokens_per_tile;
     g.num_tiles = tiles < 1 ? 1 : (int32_t)tiles;
-    g.hist_bytes = round_up_256((size_t)g.num_tiles * (size_t)g.num_keys * sizeof(int32_t));
+    const size_t table = round_up_256((size_t)g.num_tiles * (size_t)g.num_keys * sizeof(int32_t));
+    g.ws_tile_hist = 0;
+    g.ws_tile_prefix = g.ws_tile_hist + table;
+    g.ws_totals = g.ws_tile_prefix + table;
+    g.ws_tile_err = g.ws_totals + round_up_256((size_t)g.num_keys * sizeof(int32_t));
+    g.ws_bytes = g.ws_tile_err + round_up_256((size_t)g.num_tiles * sizeof(int32_t));
     return g;
 }
 
-// Workspace: [header | tile_hist[num_tiles][num_keys] | tile_base[num_tiles][num_keys]].
-inline size_t workspace_bytes(const TileGeometry& g) { return kWorkspaceHeader + 2 * g.hist_bytes; }
+// Workspace: tile_hist[num_tiles][num_keys], tile_prefix[num_tiles][num_keys],
+// totals[num_keys] and tile_err[num_tiles], int32, each 256-byte aligned.
+inline size_t workspace_bytes(const TileGeometry& g) { return g.ws_bytes; }
 
 // Launchers (defined in the .hip files). They return the HIP error of the launch.
 hipError_t launch_layout(const dispatch_problem_t& p, const TileGeometry& g, const void* topk_idx,

@@ -9,20 +9,25 @@
 // order inside a bucket; here the order is ascending token index, and no
 // atomic decides a slot.
 //
-// Two kernels, both one workgroup per tile of consecutive tokens:
+// The routing table is cut into small tiles so that the whole GPU takes part
+// (ranking a chunk is VALU work, and one CU would serialize a large tile).
+// Three kernels, none of which waits on another workgroup:
 //
-//   count_kernel   Each wavefront ranks its sub-tile's pairs chunk by chunk
-//                  (see rank_chunk) into wavefront-private LDS counters, the
-//                  workgroup adds them into a tile histogram, and the last
-//                  workgroup to finish (a ticket counter; nobody waits on
-//                  anybody) turns all tile histograms into the counts, the
-//                  aligned exclusive psums and, per tile, the base slot of
-//                  every key. It then clears the ticket so the workspace is
-//                  ready for the next call without a memset.
-//   assign_kernel  Each tile ranks its pairs again the same way, scans the
-//                  wavefront counters into sub-tile bases on top of the tile
-//                  base, and writes expert_slot, rank_slot and the inverse
-//                  maps; pad entries of recv_src_token_idx become -1.
+//   count_kernel    one workgroup per tile: each wavefront ranks its chunks
+//                   (see rank_chunk) into wavefront-private LDS counters; the
+//                   tile's histogram row (one count per key) and its error
+//                   bits go to the workspace.
+//   colscan_kernel  one workgroup per 64 keys: exclusive prefix of every
+//                   histogram column over the tiles, and the column totals.
+//   assign_kernel   one workgroup per tile: scans the totals into the aligned
+//                   exclusive psums and the status (the same in every
+//                   workgroup; workgroup 0 stores them), ranks the tile's
+//                   pairs again exactly as count_kernel did, and writes
+//                   expert_slot, rank_slot and the inverse maps; pad entries of
+//                   recv_src_token_idx become -1.
+//
+// Kernel boundaries order every hand-off; the workspace carries nothing from
+// one call to the next and needs no clearing.
 //
 // Rank dedup: among the lanes of one token, the pair that owns a rank is the
 // highest k in that rank (the page's "master lane"). gfx950 has no match-any
@@ -51,12 +56,12 @@ struct LayoutParams {
     int32_t num_tiles;
 };
 
-// Where one lane's pair lands inside its wavefront's sub-tile.
+// Where one lane's pair lands inside its wavefront's chunks.
 struct PairPos {
     int expert;      // expert id, or -1 when the lane holds no routed pair
-    int expert_pos;  // earlier pairs of that expert in the sub-tile
+    int expert_pos;  // earlier pairs of that expert in the wavefront's chunks
     int rank;        // rank id when the lane owns its (token, rank), else -1
-    int rank_pos;    // earlier owned (token, rank) pairs of that rank in the sub-tile
+    int rank_pos;    // earlier owned (token, rank) pairs of that rank in the wavefront's chunks
 };
 
 __device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane) - 1ull; }
@@ -81,7 +86,7 @@ __device__ __forceinline__ void wave_fence() {
 }
 
 // Rank one chunk of pairs. `entry` is this lane's topk entry (-1 for lanes
-// beyond the chunk or the tile). `counters` holds the wavefront's running
+// beyond the chunk or the table). `counters` holds the wavefront's running
 // count of every key over the chunks already ranked; it is advanced by this
 // chunk. Must be called by all 64 lanes together.
 __device__ __forceinline__ PairPos rank_chunk(int64_t entry, int lane, int token_in_chunk,
@@ -96,7 +101,7 @@ __device__ __forceinline__ PairPos rank_chunk(int64_t entry, int lane, int token
     const uint64_t routed = __ballot(valid);
     const uint64_t same_expert = routed & match_key(e, p.expert_bits);
     const uint64_t same_rank = routed & match_key(r, p.rank_bits);
-    const uint64_t own_token = (((K == 64) ? ~0ull : ((1ull << K) - 1ull))) << (token_in_chunk * K);
+    const uint64_t own_token = ((1ull << K) - 1ull) << (token_in_chunk * K);
     const uint64_t below = lanes_below(lane), above = lanes_above(lane);
 
     if (valid && __popcll(same_expert & own_token) > 1) err |= DISPATCH_STATUS_DUP_EXPERT;
@@ -124,28 +129,28 @@ __device__ __forceinline__ PairPos rank_chunk(int64_t entry, int lane, int token
     return pos;
 }
 
-template <typename IdxT>
-__device__ __forceinline__ void load_entries(const IdxT* __restrict__ topk, int64_t wave_tok0,
-                                             int64_t tile_end, int lane, int token_in_chunk, int k,
-                                             const LayoutParams& p, int64_t (&entry)[kChunksPerWave]) {
+template <int CH, typename IdxT>
+__device__ __forceinline__ void load_entries(const IdxT* __restrict__ topk, int64_t wave_tok0, int token_in_chunk,
+                                             int k, const LayoutParams& p, int64_t (&entry)[CH]) {
 #pragma unroll
-    for (int c = 0; c < kChunksPerWave; ++c) {
+    for (int c = 0; c < CH; ++c) {
         const int64_t tok = wave_tok0 + (int64_t)c * p.tokens_per_chunk + token_in_chunk;
-        const bool live = token_in_chunk < p.tokens_per_chunk && tok < tile_end;
+        const bool live = token_in_chunk < p.tokens_per_chunk && tok < p.num_tokens;
         entry[c] = live ? (int64_t)topk[tok * p.num_topk + k] : -1;
     }
 }
 
-// Exclusive scan, in place, of up to n LDS values (each rounded up to a
-// multiple of `align` first) by the whole workgroup. Returns the total.
-__device__ int block_exclusive_scan(int* __restrict__ v, int n, int align, int* __restrict__ scratch) {
+// Exclusive scan of n LDS values (each rounded up to a multiple of `align`
+// first) from `in` into `out` by the whole workgroup. Returns the total.
+__device__ int block_exclusive_scan(const int* __restrict__ in, int* __restrict__ out, int n, int align,
+                                    int* __restrict__ scratch) {
     const int tid = threadIdx.x, nthreads = blockDim.x;
     const int lane = tid & (kWave - 1), wave = tid / kWave, nwaves = nthreads / kWave;
     const int per = (n + nthreads - 1) / nthreads;
     const int lo = min(n, tid * per), hi = min(n, lo + per);
     int local = 0;
     for (int i = lo; i < hi; ++i) {
-        const int c = v[i];
+        const int c = in[i];
         local += align > 1 ? (c + align - 1) / align * align : c;
     }
     // Kogge-Stone inclusive scan across the 64 lanes (6 steps).
@@ -169,8 +174,8 @@ __device__ int block_exclusive_scan(int* __restrict__ v, int n, int align, int* 
     __syncthreads();
     int run = scratch[wave] + incl - local;
     for (int i = lo; i < hi; ++i) {
-        const int c = v[i];
-        v[i] = run;
+        const int c = in[i];
+        out[i] = run;
         run += align > 1 ? (c + align - 1) / align * align : c;
     }
     const int total = scratch[nwaves];
@@ -178,14 +183,19 @@ __device__ int block_exclusive_scan(int* __restrict__ v, int n, int align, int* 
     return total;
 }
 
-template <typename IdxT>
-__global__ void __launch_bounds__(1024)
-count_kernel(const IdxT* __restrict__ topk, LayoutParams p, WorkspaceHeader* __restrict__ hdr,
-             int32_t* __restrict__ tile_hist, int32_t* __restrict__ tile_base, dispatch_layout_t out) {
+// Workspace views.
+struct Workspace {
+    int32_t* tile_hist;    // [num_tiles][num_keys]
+    int32_t* tile_prefix;  // [num_tiles][num_keys] pairs of the key in earlier tiles
+    int32_t* totals;       // [num_keys]
+    int32_t* tile_err;     // [num_tiles] DISPATCH_STATUS_* bits seen by the tile
+};
+
+template <int CH, typename IdxT>
+__global__ void __launch_bounds__(kLayoutThreads)
+count_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws) {
     extern __shared__ int lds[];  // [W][num_keys] wavefront counters
-    __shared__ int scratch[kMaxWavesPerTile + 1];
     __shared__ uint32_t block_err;
-    __shared__ int is_last;
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int nthreads = blockDim.x, nwaves = nthreads / kWave, nkeys = p.num_keys;
@@ -196,120 +206,118 @@ count_kernel(const IdxT* __restrict__ topk, LayoutParams p, WorkspaceHeader* __r
 
     const int token_in_chunk = lane / p.num_topk;
     const int k = lane - token_in_chunk * p.num_topk;
-    const int64_t tile_tok0 = (int64_t)blockIdx.x * p.tokens_per_tile;
-    const int64_t tile_end = min(p.num_tokens, tile_tok0 + p.tokens_per_tile);
-    const int64_t wave_tok0 = tile_tok0 + (int64_t)wave * p.tokens_per_wave;
-
-    int64_t entry[kChunksPerWave];
-    load_entries(topk, wave_tok0, tile_end, lane, token_in_chunk, k, p, entry);
+    const int64_t wave_tok0 = (int64_t)blockIdx.x * p.tokens_per_tile + (int64_t)wave * p.tokens_per_wave;
+    int64_t entry[CH];
+    load_entries<CH>(topk, wave_tok0, token_in_chunk, k, p, entry);
     uint32_t err = 0;
 #pragma unroll
-    for (int c = 0; c < kChunksPerWave; ++c) (void)rank_chunk(entry[c], lane, token_in_chunk, p, counters, err);
+    for (int c = 0; c < CH; ++c) (void)rank_chunk(entry[c], lane, token_in_chunk, p, counters, err);
     const uint64_t any_bad = __ballot((err & DISPATCH_STATUS_BAD_EXPERT) != 0);
     const uint64_t any_dup = __ballot((err & DISPATCH_STATUS_DUP_EXPERT) != 0);
     if (lane == 0 && (any_bad | any_dup))
         atomicOr(&block_err, (any_bad ? DISPATCH_STATUS_BAD_EXPERT : 0u) | (any_dup ? DISPATCH_STATUS_DUP_EXPERT : 0u));
     __syncthreads();
 
-    // Tile histogram: sum of the wavefront counters.
-    int32_t* my_hist = tile_hist + (int64_t)blockIdx.x * nkeys;
+    int32_t* row = ws.tile_hist + (int64_t)blockIdx.x * nkeys;
     for (int j = tid; j < nkeys; j += nthreads) {
         int s = 0;
         for (int w = 0; w < nwaves; ++w) s += lds[w * nkeys + j];
-        my_hist[j] = s;
+        row[j] = s;
     }
-    if (tid == 0 && block_err)
-        __hip_atomic_fetch_or(&hdr->error_bits, block_err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // Release this tile's histogram device-wide, then take a ticket.
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t ticket =
-            __hip_atomic_fetch_add(&hdr->ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        is_last = ticket == gridDim.x - 1;
-    }
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();  // acquire every other tile's histogram
+    if (tid == 0) ws.tile_err[blockIdx.x] = (int32_t)block_err;
+}
 
-    // ---- Last workgroup: counts, psums and per-tile key bases. ----
-    const int E = p.num_experts, R = p.num_ranks;
-    int* totals = lds;  // the wavefront counters are no longer needed
-    for (int j = tid; j < nkeys; j += nthreads) {
-        int s = 0;
-        for (int i = 0; i < p.num_tiles; ++i) s += tile_hist[(int64_t)i * nkeys + j];
-        totals[j] = s;
-    }
+// Column scan of the tile histograms: 64 keys per workgroup (one per lane),
+// the tiles split into kScanSegments contiguous segments (one per wavefront).
+__global__ void __launch_bounds__(kScanSegments * kWave)
+colscan_kernel(LayoutParams p, Workspace ws) {
+    __shared__ int seg_sum[kScanSegments][kWave];
+    const int lane = threadIdx.x & (kWave - 1), seg = threadIdx.x / kWave;
+    const int j = blockIdx.x * kWave + lane;
+    const int nkeys = p.num_keys, n = p.num_tiles;
+    const int per = (n + kScanSegments - 1) / kScanSegments;
+    const int lo = min(n, seg * per), hi = min(n, lo + per);
+    int s = 0;
+    if (j < nkeys)
+        for (int i = lo; i < hi; ++i) s += ws.tile_hist[(int64_t)i * nkeys + j];
+    seg_sum[seg][lane] = s;
     __syncthreads();
-    for (int j = tid; j < nkeys; j += nthreads) {
-        if (j < E) out.expert_count[j] = totals[j];
-        else out.rank_count[j - E] = totals[j];
-    }
-    __syncthreads();
-    // Exclusive psums (alignment before the sum, section 7.2); totals[] now
-    // holds each key's first slot.
-    const int recv_rows = block_exclusive_scan(totals, E, p.alignment, scratch);
-    const int rank_rows = block_exclusive_scan(totals + E, R, 1, scratch);
-    for (int j = tid; j < nkeys; j += nthreads) {
-        if (j < E) out.expert_psum[j] = totals[j];
-        else out.rank_psum[j - E] = totals[j];
-    }
-    // Per-tile base slot of every key: the key's first slot plus the pairs
-    // of that key in earlier tiles.
-    for (int j = tid; j < nkeys; j += nthreads) {
-        int run = totals[j];
-        for (int i = 0; i < p.num_tiles; ++i) {
-            const int h = tile_hist[(int64_t)i * nkeys + j];
-            tile_base[(int64_t)i * nkeys + j] = run;
+    int run = 0;
+    for (int q = 0; q < seg; ++q) run += seg_sum[q][lane];
+    if (j < nkeys) {
+        for (int i = lo; i < hi; ++i) {
+            const int h = ws.tile_hist[(int64_t)i * nkeys + j];
+            ws.tile_prefix[(int64_t)i * nkeys + j] = run;
             run += h;
         }
-    }
-    if (tid == 0) {
-        out.expert_psum[E] = recv_rows;
-        out.rank_psum[R] = rank_rows;
-        uint32_t status = __hip_atomic_load(&hdr->error_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (recv_rows > p.recv_capacity) status |= DISPATCH_STATUS_RECV_OVERFLOW;
-        if (rank_rows > p.rank_capacity) status |= DISPATCH_STATUS_RANK_OVERFLOW;
-        *out.status = (int32_t)status;
-        // Leave the control words zero for the next call.
-        __hip_atomic_store(&hdr->error_bits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&hdr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (seg == kScanSegments - 1) ws.totals[j] = run;
     }
 }
 
-template <typename IdxT>
-__global__ void __launch_bounds__(1024)
-assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, const int32_t* __restrict__ tile_base,
-              dispatch_layout_t out) {
-    if (*out.status != 0) return;  // the layout is unspecified: write nothing
+template <int CH, typename IdxT>
+__global__ void __launch_bounds__(kLayoutThreads)
+assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispatch_layout_t out) {
+    // LDS: [W][num_keys] wavefront counters, then totals[num_keys] and first[num_keys].
     extern __shared__ int lds[];
+    __shared__ int scratch[kLayoutThreads / kWave + 1];
+    __shared__ uint32_t block_err;
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int nthreads = blockDim.x, nwaves = nthreads / kWave, nkeys = p.num_keys;
-    const int K = p.num_topk, E = p.num_experts;
+    const int K = p.num_topk, E = p.num_experts, R = p.num_ranks;
+    const int tile = blockIdx.x;
     int* counters = lds + wave * nkeys;
+    int* totals = lds + nwaves * nkeys;  // per key, over all tiles
+    int* first = totals + nkeys;         // per key, first slot (exclusive psum)
     for (int i = lane; i < nkeys; i += kWave) counters[i] = 0;
-    wave_fence();
+    for (int j = tid; j < nkeys; j += nthreads) totals[j] = ws.totals[j];
+    if (tid == 0) block_err = 0;
+    __syncthreads();
+    uint32_t tile_errs = 0;
+    for (int i = tid; i < p.num_tiles; i += nthreads) tile_errs |= (uint32_t)ws.tile_err[i];
+    if (tile_errs) atomicOr(&block_err, tile_errs);
 
     const int token_in_chunk = lane / K;
     const int k = lane - token_in_chunk * K;
-    const int64_t tile_tok0 = (int64_t)blockIdx.x * p.tokens_per_tile;
-    const int64_t tile_end = min(p.num_tokens, tile_tok0 + p.tokens_per_tile);
-    const int64_t wave_tok0 = tile_tok0 + (int64_t)wave * p.tokens_per_wave;
-
-    int64_t entry[kChunksPerWave];
-    load_entries(topk, wave_tok0, tile_end, lane, token_in_chunk, k, p, entry);
+    const int64_t wave_tok0 = (int64_t)tile * p.tokens_per_tile + (int64_t)wave * p.tokens_per_wave;
+    int64_t entry[CH];
+    load_entries<CH>(topk, wave_tok0, token_in_chunk, k, p, entry);
     uint32_t err = 0;
-    PairPos pos[kChunksPerWave];
+    PairPos pos[CH];
 #pragma unroll
-    for (int c = 0; c < kChunksPerWave; ++c) pos[c] = rank_chunk(entry[c], lane, token_in_chunk, p, counters, err);
-    __syncthreads();
+    for (int c = 0; c < CH; ++c) pos[c] = rank_chunk(entry[c], lane, token_in_chunk, p, counters, err);
 
-    // Sub-tile bases: scan the wavefront counters of each key in wavefront
-    // order, on top of the tile's base slot for that key.
-    const int32_t* my_base = tile_base + (int64_t)blockIdx.x * nkeys;
+    // Exclusive psums: expert counts aligned up first (section 7.2), rank
+    // counts as they are (section 5.2). The scan's barriers also publish the
+    // wavefront counters and block_err.
+    const int recv_rows = block_exclusive_scan(totals, first, E, p.alignment, scratch);
+    const int rank_rows = block_exclusive_scan(totals + E, first + E, R, 1, scratch);
+    uint32_t status = block_err;
+    if (recv_rows > p.recv_capacity) status |= DISPATCH_STATUS_RECV_OVERFLOW;
+    if (rank_rows > p.rank_capacity) status |= DISPATCH_STATUS_RANK_OVERFLOW;
+    if (tile == 0) {
+        for (int j = tid; j < nkeys; j += nthreads) {
+            if (j < E) {
+                out.expert_count[j] = totals[j];
+                out.expert_psum[j] = first[j];
+            } else {
+                out.rank_count[j - E] = totals[j];
+                out.rank_psum[j - E] = first[j];
+            }
+        }
+        if (tid == 0) {
+            out.expert_psum[E] = recv_rows;
+            out.rank_psum[R] = rank_rows;
+            *out.status = (int32_t)status;
+        }
+    }
+    if (status != 0) return;  // the layout is unspecified: write nothing more
+
+    // Base slot of every wavefront's chunks: the key's first slot, plus its
+    // pairs in earlier tiles, plus its pairs in earlier wavefronts of this tile.
+    const int32_t* prefix = ws.tile_prefix + (int64_t)tile * nkeys;
     for (int j = tid; j < nkeys; j += nthreads) {
-        int run = my_base[j];
+        int run = first[j] + prefix[j];
         for (int w = 0; w < nwaves; ++w) {
             const int c = lds[w * nkeys + j];
             lds[w * nkeys + j] = run;
@@ -319,12 +327,13 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, const int32_t* __re
     __syncthreads();
 
 #pragma unroll
-    for (int c = 0; c < kChunksPerWave; ++c) {
+    for (int c = 0; c < CH; ++c) {
         const int64_t tok = wave_tok0 + (int64_t)c * p.tokens_per_chunk + token_in_chunk;
-        const bool live = token_in_chunk < p.tokens_per_chunk && tok < tile_end;
+        const bool live = token_in_chunk < p.tokens_per_chunk && tok < p.num_tokens;
         if (!live) continue;
-        const int es = pos[c].expert >= 0 ? counters[pos[c].expert] + pos[c].expert_pos : -1;
-        const int rs = pos[c].rank >= 0 ? counters[E + pos[c].rank] + pos[c].rank_pos : -1;
+        const int e = pos[c].expert, r = pos[c].rank;
+        const int es = e >= 0 ? counters[e] + pos[c].expert_pos : -1;
+        const int rs = r >= 0 ? counters[E + r] + pos[c].rank_pos : -1;
         out.expert_slot[tok * K + k] = es;
         out.rank_slot[tok * K + k] = rs;
         // Slots are below the totals, which fit the capacities when the
@@ -336,9 +345,9 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, const int32_t* __re
     // Alignment pads of recv_src_token_idx (section 7.3): the slots after an
     // expert's real rows up to its aligned end map to no token.
     if (p.alignment > 1) {
-        for (int e = blockIdx.x; e < E; e += gridDim.x) {
-            const int lo = out.expert_psum[e] + out.expert_count[e];
-            const int hi = (int)min((int64_t)out.expert_psum[e + 1], p.recv_capacity);
+        for (int e = tile; e < E; e += gridDim.x) {
+            const int lo = first[e] + totals[e];
+            const int hi = (int)min((int64_t)(e + 1 < E ? first[e + 1] : recv_rows), p.recv_capacity);
             for (int s = lo + tid; s < hi; s += nthreads) out.recv_src_token_idx[s] = -1;
         }
     }
@@ -350,25 +359,39 @@ int bits_for(int n) {  // bits needed to tell apart n distinct ids
     return b;
 }
 
-template <typename IdxT>
+template <int CH, typename IdxT>
 hipError_t launch_typed(const LayoutParams& p, const TileGeometry& g, const void* topk,
-                        const dispatch_layout_t& out, void* workspace, hipStream_t stream) {
-    auto* hdr = reinterpret_cast<WorkspaceHeader*>(workspace);
-    auto* tile_hist = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kWorkspaceHeader);
-    auto* tile_base = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kWorkspaceHeader + g.hist_bytes);
+                        const dispatch_layout_t& out, const Workspace& ws, hipStream_t stream) {
     const auto* idx = static_cast<const IdxT*>(topk);
     const dim3 grid(g.num_tiles), block(g.waves_per_tile * kWave);
-    const size_t lds = (size_t)g.waves_per_tile * g.num_keys * sizeof(int);
     LayoutParams pc = p;
+    Workspace wc = ws;
     dispatch_layout_t oc = out;
-    void* count_args[] = {&idx, &pc, &hdr, &tile_hist, &tile_base, &oc};
-    hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&count_kernel<IdxT>), grid, block,
-                                     count_args, lds, stream);
+    const size_t count_lds = (size_t)g.waves_per_tile * g.num_keys * sizeof(int);
+    void* count_args[] = {&idx, &pc, &wc};
+    hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&count_kernel<CH, IdxT>), grid, block,
+                                     count_args, count_lds, stream);
     if (err != hipSuccess) return err;
-    const int32_t* base_c = tile_base;
-    void* assign_args[] = {&idx, &pc, &base_c, &oc};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<IdxT>), grid, block,
-                           assign_args, lds, stream);
+    void* scan_args[] = {&pc, &wc};
+    err = hipLaunchKernel(reinterpret_cast<const void*>(&colscan_kernel),
+                          dim3((g.num_keys + kWave - 1) / kWave), dim3(kScanSegments * kWave), scan_args, 0,
+                          stream);
+    if (err != hipSuccess) return err;
+    const size_t assign_lds = (size_t)(g.waves_per_tile + 2) * g.num_keys * sizeof(int);
+    void* assign_args[] = {&idx, &pc, &wc, &oc};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, IdxT>), grid, block,
+                           assign_args, assign_lds, stream);
+}
+
+template <typename IdxT>
+hipError_t launch_chunks(const LayoutParams& p, const TileGeometry& g, const void* topk,
+                         const dispatch_layout_t& out, const Workspace& ws, hipStream_t stream) {
+    switch (g.chunks_per_wave) {
+        case 1: return launch_typed<1, IdxT>(p, g, topk, out, ws, stream);
+        case 2: return launch_typed<2, IdxT>(p, g, topk, out, ws, stream);
+        case 4: return launch_typed<4, IdxT>(p, g, topk, out, ws, stream);
+        default: return launch_typed<8, IdxT>(p, g, topk, out, ws, stream);
+    }
 }
 
 }  // namespace
@@ -391,8 +414,14 @@ hipError_t launch_layout(const dispatch_problem_t& prob, const TileGeometry& g, 
     p.tokens_per_tile = g.tokens_per_tile;
     p.num_keys = g.num_keys;
     p.num_tiles = g.num_tiles;
-    if (prob.topk_idx_bytes == 8) return launch_typed<int64_t>(p, g, topk_idx, out, workspace, stream);
-    return launch_typed<int32_t>(p, g, topk_idx, out, workspace, stream);
+    char* base = static_cast<char*>(workspace);
+    Workspace ws;
+    ws.tile_hist = reinterpret_cast<int32_t*>(base + g.ws_tile_hist);
+    ws.tile_prefix = reinterpret_cast<int32_t*>(base + g.ws_tile_prefix);
+    ws.totals = reinterpret_cast<int32_t*>(base + g.ws_totals);
+    ws.tile_err = reinterpret_cast<int32_t*>(base + g.ws_tile_err);
+    if (prob.topk_idx_bytes == 8) return launch_chunks<int64_t>(p, g, topk_idx, out, ws, stream);
+    return launch_chunks<int32_t>(p, g, topk_idx, out, ws, stream);
 }
 
 }  // namespace moe_dispatch

@@ -180,3 +180,41 @@ def scatter(lay: Layout, x_bytes: np.ndarray, x_sf: Optional[np.ndarray] = None,
     if rc != 0:
         raise ValueError(f"oracle scatter failed (code {rc})")
     return out
+
+
+class Prepared:
+    """The oracle's layout + scatter of one input, on pre-allocated, pre-faulted
+    host buffers, for timing the oracle as it stands (the CPU baseline)."""
+
+    def __init__(self, topk_idx: np.ndarray, num_experts: int, num_ranks: int, alignment: int,
+                 x_bytes: np.ndarray, x_sf: Optional[np.ndarray] = None):
+        self.lib = _load()
+        self.topk = np.ascontiguousarray(topk_idx, dtype=np.int64)
+        self.t, self.k = self.topk.shape
+        self.e, self.r, self.a = num_experts, num_ranks, alignment
+        self.x = np.ascontiguousarray(x_bytes, dtype=np.uint8)
+        self.row_bytes = self.x.shape[1]
+        self.sf = None if x_sf is None else np.ascontiguousarray(x_sf, dtype=np.float32)
+        self.s = 0 if x_sf is None else self.sf.shape[1]
+        self.recv_cap, self.rank_cap = max_rows(self.t, self.k, num_experts, num_ranks, alignment)
+        z = lambda *shape, dt=np.int32: np.ones(shape, dtype=dt)  # noqa: E731  (ones: pre-faulted)
+        self.expert_count, self.rank_count = z(num_experts), z(num_ranks)
+        self.expert_psum, self.rank_psum = z(num_experts + 1), z(num_ranks + 1)
+        self.expert_slot, self.rank_slot = z(self.t, self.k), z(self.t, self.k)
+        self.recv_src, self.rank_src = z(self.recv_cap), z(self.rank_cap)
+        self.rank_x = z(self.rank_cap, self.row_bytes, dt=np.uint8)
+        self.recv_x = z(self.recv_cap, self.row_bytes, dt=np.uint8)
+        self.rank_sf = z(self.rank_cap, self.s, dt=np.float32) if self.s else None
+        self.recv_sf = z(self.recv_cap, self.s, dt=np.float32) if self.s else None
+
+    def run_layout(self) -> int:
+        return self.lib.oracle_dispatch_layout(
+            self.t, self.k, self.e, self.r, self.a, _ptr(self.topk), self.recv_cap, self.rank_cap,
+            _ptr(self.expert_count), _ptr(self.rank_count), _ptr(self.expert_psum), _ptr(self.rank_psum),
+            _ptr(self.expert_slot), _ptr(self.rank_slot), _ptr(self.recv_src), _ptr(self.rank_src))
+
+    def run_scatter(self) -> int:
+        return self.lib.oracle_dispatch_scatter(
+            self.t, self.k, self.e, self.row_bytes, self.s, _ptr(self.x), _ptr(self.sf),
+            _ptr(self.expert_count), _ptr(self.expert_psum), _ptr(self.expert_slot), _ptr(self.rank_slot),
+            _ptr(self.rank_x), _ptr(self.rank_sf), _ptr(self.recv_x), _ptr(self.recv_sf), 1)

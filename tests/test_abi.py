@@ -46,6 +46,7 @@ def test_binding_constants_match_header():
     assert (d["DISPATCH_RANK_CONTIG"], d["DISPATCH_EXPERT_MAJOR"], d["DISPATCH_ZERO_PAD"]) == (
         M.RANK_CONTIG, M.EXPERT_MAJOR, M.ZERO_PAD)
     assert d["DISPATCH_MAX_TOPK"] == M.MAX_TOPK and d["DISPATCH_MAX_EXPERTS"] == M.MAX_EXPERTS
+    assert d["DISPATCH_MAX_RANKS"] == M.MAX_RANKS
     assert ctypes.sizeof(M.Problem) == 64 and ctypes.sizeof(M.LayoutPtrs) == 9 * 8
 
 
@@ -71,6 +72,7 @@ def test_max_rows_and_workspace():
 BAD_PROBLEMS = [
     dict(num_tokens=-1), dict(num_topk=0), dict(num_topk=33), dict(num_experts=0),
     dict(num_experts=4097), dict(num_ranks=3), dict(num_ranks=0), dict(num_ranks=512),
+    dict(num_experts=4096, num_ranks=2048),
     dict(expert_alignment=0), dict(topk_idx_bytes=2), dict(sf_per_token=-1), dict(flags=8),
     dict(recv_capacity_rows=-1), dict(reserved=1), dict(num_tokens=1 << 31),
     dict(num_tokens=1 << 28, expert_alignment=1 << 20),
@@ -126,6 +128,8 @@ def test_host_errors_before_launch():
     p2 = M.Problem(100, 8, 256, 8, 1, 8, 4, 72, 1000, 1000, M.ALL_OUTPUTS, 0)
     assert sc(p2, good, 4096, 4096, 4096, 4096, 4096, 4096) == M.ERR_ALIGN  # row_bytes % 16
     p3 = M.Problem(100, 8, 256, 8, 1, 8, 4, 0, 1000, 1000, M.ALL_OUTPUTS, 0)
+    assert sc(p3, good, 4096, 4096, 4096, 4096, 4096, 4096) == M.ERR_ARG
+    p3.row_bytes = 1 << 31  # one row must stay below 2 GiB
     assert sc(p3, good, 4096, 4096, 4096, 4096, 4096, 4096) == M.ERR_ARG
     # Only the selected outputs are required: with expert-major rows alone and
     # no scale factors, NULL rank buffers pass and a misaligned recv_x is caught.
