@@ -32,8 +32,7 @@ if ROOT not in sys.path:
 METRIC = "dispatch GB/s & % HBM peak, 4096 tok×7168 bf16, top-8 of 256 experts"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scatter_traffic.json")
-SCATTER_SOURCES = [os.path.join(ROOT, "moe_token_dispatch_amd", "csrc", f)
-                   for f in ("dispatch_scatter.hip", "dispatch_common.hpp")]
+SCATTER_SOURCES = [os.path.join(ROOT, "moe_token_dispatch_amd", "csrc", "dispatch_scatter.hip")]
 
 
 def parse_args():
