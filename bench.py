@@ -41,6 +41,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default=None, help="workload name (default: the metric workload)")
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="bracket the scatter with HIP events on every n-th timed step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -196,19 +198,25 @@ def main():
     if int(lay.status.item()) != 0:
         raise RuntimeError(f"dispatch status {int(lay.status.item())}")
 
-    # Two events per step bracket the scatter kernel on the stream it runs on;
-    # the span from one step's scatter end to the next one's scatter start is
-    # the layout plus the launch gaps.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    # On every n-th timed step two events bracket the scatter kernel on the
+    # stream it runs on (sampling keeps the event records' own cost out of most
+    # steps); on the step before a sampled one, an event after its scatter
+    # gives the layout-plus-launch-gap span up to the sampled scatter's start.
+    every = max(1, args.event_every)
+    sampled = [i for i in range(args.steps) if i % every == every - 1]
+    events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for i in sampled}
+    before = {i - 1: torch.cuda.Event(enable_timing=True) for i in sampled if i > 0}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step(events.get(i))
+        if i in before:
+            before[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    scatter_ms = [e[0].elapsed_time(e[1]) for e in events]
-    layout_ms = [events[i - 1][1].elapsed_time(events[i][0]) for i in range(1, len(events))] or [0.0]
+    scatter_ms = [events[i][0].elapsed_time(events[i][1]) for i in sampled]
+    layout_ms = [before[i - 1].elapsed_time(events[i][0]) for i in sampled if i - 1 in before] or [0.0]
     p_rows = int(lay.expert_psum[-1].item())
     n_rank = int(lay.rank_psum[-1].item())
     t_live = int((inp.topk_idx >= 0).any(axis=1).sum())
@@ -256,6 +264,7 @@ def main():
         "pairs_per_s": round(p_valid / (wall / args.steps), 1),
         "layout_and_gaps_us_mean": round(statistics.mean(layout_ms) * 1e3, 2),
         "scatter_us_mean": round(sc_mean_ms * 1e3, 2),
+        "scatter_event_samples": len(scatter_ms),
         "rows": {"expert_major": p_rows, "rank_contig": n_rank, "live_tokens": t_live, "pairs": p_valid},
         "roofline": {
             "kernel": "scatter_kernel",

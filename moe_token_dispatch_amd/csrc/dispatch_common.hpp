@@ -18,9 +18,12 @@
 namespace moe_dispatch {
 
 constexpr int kWave = 64;             // gfx950 wavefront width
-constexpr int kLayoutThreads = 256;   // at most 4 wavefronts per layout workgroup
+constexpr int kLayoutThreads = 1024;  // at most 16 wavefronts per layout workgroup
 constexpr int kScanSegments = 16;     // wavefronts per column-scan workgroup
 constexpr int kMaxTilesTarget = 512;  // more chunks per wavefront beyond this many tiles
+constexpr int kFewTiles = 8;          // up to this many tiles, assign reduces the histograms itself
+constexpr int kFewTileWaves = 16;     // wavefronts per tile on the few-tiles path
+constexpr int kManyTileWaves = 4;     // wavefronts per tile on the column-scan path
 constexpr int kLdsBudgetInts = 16000; // LDS ints per workgroup for key arrays, under 64 KiB
 
 struct TileGeometry {
@@ -33,6 +36,7 @@ struct TileGeometry {
     int32_t tokens_per_tile;    // W * tokens_per_wave
     int32_t num_tiles;          // >= 1
     int32_t num_keys;           // E + R: expert keys first, then rank keys
+    bool column_scan;           // false: two kernels (count, assign); true: count, colscan, assign
     size_t ws_tile_hist;        // workspace byte offsets of the arrays below
     size_t ws_tile_prefix;
     size_t ws_totals;
@@ -51,16 +55,25 @@ inline TileGeometry make_geometry(int64_t num_tokens, int32_t num_topk, int32_t 
     g.num_keys = num_experts + num_ranks;
     // The assign kernel holds W wavefront counter rows plus two more rows of
     // num_keys ints in LDS.
-    int w = kLdsBudgetInts / g.num_keys - 2;
-    const int max_w = kLayoutThreads / kWave;
-    g.waves_per_tile = w < 1 ? 1 : (w > max_w ? max_w : w);
-    // Few chunks per wavefront keep the layout spread over many CUs; more
-    // chunks once the tile count would make the column scan long.
+    const int w_lds = kLdsBudgetInts / g.num_keys - 2;
+    auto clamp_w = [&](int cap) { return w_lds < 1 ? 1 : (w_lds > cap ? cap : w_lds); };
+    // One chunk per wavefront keeps the ranking spread over many CUs. With
+    // few tiles of 16 wavefronts, each assign workgroup reduces the tile
+    // histograms itself (two kernels); otherwise tiles of 4 wavefronts and a
+    // column-scan kernel, with more chunks per wavefront once the tile count
+    // would make the column scan long.
     g.chunks_per_wave = 1;
-    while (g.chunks_per_wave < 8) {
-        const int64_t per_tile = (int64_t)g.waves_per_tile * g.chunks_per_wave * g.tokens_per_chunk;
-        if ((num_tokens + per_tile - 1) / per_tile <= kMaxTilesTarget) break;
-        g.chunks_per_wave *= 2;
+    g.waves_per_tile = clamp_w(kFewTileWaves);
+    const int64_t few_tiles = (num_tokens + (int64_t)g.waves_per_tile * g.tokens_per_chunk - 1) /
+                              ((int64_t)g.waves_per_tile * g.tokens_per_chunk);
+    g.column_scan = few_tiles > kFewTiles;
+    if (g.column_scan) {
+        g.waves_per_tile = clamp_w(kManyTileWaves);
+        while (g.chunks_per_wave < 8) {
+            const int64_t per_tile = (int64_t)g.waves_per_tile * g.chunks_per_wave * g.tokens_per_chunk;
+            if ((num_tokens + per_tile - 1) / per_tile <= kMaxTilesTarget) break;
+            g.chunks_per_wave *= 2;
+        }
     }
     g.tokens_per_wave = g.tokens_per_chunk * g.chunks_per_wave;
     g.tokens_per_tile = g.waves_per_tile * g.tokens_per_wave;

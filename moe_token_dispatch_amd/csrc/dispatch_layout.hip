@@ -11,20 +11,22 @@
 //
 // The routing table is cut into small tiles so that the whole GPU takes part
 // (ranking a chunk is VALU work, and one CU would serialize a large tile).
-// Three kernels, none of which waits on another workgroup:
+// Up to three kernels, none of which waits on another workgroup:
 //
 //   count_kernel    one workgroup per tile: each wavefront ranks its chunks
 //                   (see rank_chunk) into wavefront-private LDS counters; the
 //                   tile's histogram row (one count per key) and its error
 //                   bits go to the workspace.
-//   colscan_kernel  one workgroup per 64 keys: exclusive prefix of every
-//                   histogram column over the tiles, and the column totals.
-//   assign_kernel   one workgroup per tile: scans the totals into the aligned
-//                   exclusive psums and the status (the same in every
-//                   workgroup; workgroup 0 stores them), ranks the tile's
-//                   pairs again exactly as count_kernel did, and writes
-//                   expert_slot, rank_slot and the inverse maps; pad entries of
-//                   recv_src_token_idx become -1.
+//   colscan_kernel  (many tiles only) one workgroup per 64 keys: exclusive
+//                   prefix of every histogram column over the tiles, and the
+//                   column totals.
+//   assign_kernel   one workgroup per tile: takes the column prefixes and
+//                   totals (or, with few tiles, reduces the tile histograms
+//                   itself), scans the totals into the aligned exclusive psums
+//                   and the status (the same in every workgroup; workgroup 0
+//                   stores them), ranks the tile's pairs again exactly as
+//                   count_kernel did, and writes expert_slot, rank_slot and the
+//                   inverse maps; pad entries of recv_src_token_idx become -1.
 //
 // Kernel boundaries order every hand-off; the workspace carries nothing from
 // one call to the next and needs no clearing.
@@ -254,7 +256,7 @@ colscan_kernel(LayoutParams p, Workspace ws) {
     }
 }
 
-template <int CH, typename IdxT>
+template <int CH, bool FROM_HIST, typename IdxT>
 __global__ void __launch_bounds__(kLayoutThreads)
 assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispatch_layout_t out) {
     // LDS: [W][num_keys] wavefront counters, then totals[num_keys] and first[num_keys].
@@ -270,7 +272,23 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
     int* totals = lds + nwaves * nkeys;  // per key, over all tiles
     int* first = totals + nkeys;         // per key, first slot (exclusive psum)
     for (int i = lane; i < nkeys; i += kWave) counters[i] = 0;
-    for (int j = tid; j < nkeys; j += nthreads) totals[j] = ws.totals[j];
+    // totals[] holds each key's pair count over all tiles; first[] holds, for
+    // now, its pairs in tiles before this one.
+    for (int j = tid; j < nkeys; j += nthreads) {
+        if (FROM_HIST) {
+            int before = 0, total = 0;
+            for (int i = 0; i < p.num_tiles; ++i) {
+                const int h = ws.tile_hist[(int64_t)i * nkeys + j];
+                before += i < tile ? h : 0;
+                total += h;
+            }
+            totals[j] = total;
+            first[j] = before;
+        } else {
+            totals[j] = ws.totals[j];
+            first[j] = ws.tile_prefix[(int64_t)tile * nkeys + j];
+        }
+    }
     if (tid == 0) block_err = 0;
     __syncthreads();
     uint32_t tile_errs = 0;
@@ -287,9 +305,19 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
 #pragma unroll
     for (int c = 0; c < CH; ++c) pos[c] = rank_chunk(entry[c], lane, token_in_chunk, p, counters, err);
 
-    // Exclusive psums: expert counts aligned up first (section 7.2), rank
-    // counts as they are (section 5.2). The scan's barriers also publish the
-    // wavefront counters and block_err.
+    // Fold the earlier-tile pairs into the wavefront counters, then scan the
+    // totals into the exclusive psums: expert counts aligned up first
+    // (section 7.2), rank counts as they are (section 5.2). The scan's
+    // barriers also publish the wavefront counters and block_err.
+    __syncthreads();
+    for (int j = tid; j < nkeys; j += nthreads) {
+        int run = first[j];
+        for (int w = 0; w < nwaves; ++w) {
+            const int c = lds[w * nkeys + j];
+            lds[w * nkeys + j] = run;
+            run += c;
+        }
+    }
     const int recv_rows = block_exclusive_scan(totals, first, E, p.alignment, scratch);
     const int rank_rows = block_exclusive_scan(totals + E, first + E, R, 1, scratch);
     uint32_t status = block_err;
@@ -313,27 +341,17 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
     }
     if (status != 0) return;  // the layout is unspecified: write nothing more
 
-    // Base slot of every wavefront's chunks: the key's first slot, plus its
-    // pairs in earlier tiles, plus its pairs in earlier wavefronts of this tile.
-    const int32_t* prefix = ws.tile_prefix + (int64_t)tile * nkeys;
-    for (int j = tid; j < nkeys; j += nthreads) {
-        int run = first[j] + prefix[j];
-        for (int w = 0; w < nwaves; ++w) {
-            const int c = lds[w * nkeys + j];
-            lds[w * nkeys + j] = run;
-            run += c;
-        }
-    }
-    __syncthreads();
-
+    // A pair's slot: its key's first slot, plus the key's pairs in earlier
+    // tiles and earlier wavefronts of this tile (the counters), plus its rank
+    // inside the wavefront's chunks.
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int64_t tok = wave_tok0 + (int64_t)c * p.tokens_per_chunk + token_in_chunk;
         const bool live = token_in_chunk < p.tokens_per_chunk && tok < p.num_tokens;
         if (!live) continue;
         const int e = pos[c].expert, r = pos[c].rank;
-        const int es = e >= 0 ? counters[e] + pos[c].expert_pos : -1;
-        const int rs = r >= 0 ? counters[E + r] + pos[c].rank_pos : -1;
+        const int es = e >= 0 ? first[e] + counters[e] + pos[c].expert_pos : -1;
+        const int rs = r >= 0 ? first[E + r] + counters[E + r] + pos[c].rank_pos : -1;
         out.expert_slot[tok * K + k] = es;
         out.rank_slot[tok * K + k] = rs;
         // Slots are below the totals, which fit the capacities when the
@@ -372,14 +390,17 @@ hipError_t launch_typed(const LayoutParams& p, const TileGeometry& g, const void
     hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&count_kernel<CH, IdxT>), grid, block,
                                      count_args, count_lds, stream);
     if (err != hipSuccess) return err;
+    const size_t assign_lds = (size_t)(g.waves_per_tile + 2) * g.num_keys * sizeof(int);
+    void* assign_args[] = {&idx, &pc, &wc, &oc};
+    if (!g.column_scan)
+        return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, true, IdxT>), grid, block,
+                               assign_args, assign_lds, stream);
     void* scan_args[] = {&pc, &wc};
     err = hipLaunchKernel(reinterpret_cast<const void*>(&colscan_kernel),
                           dim3((g.num_keys + kWave - 1) / kWave), dim3(kScanSegments * kWave), scan_args, 0,
                           stream);
     if (err != hipSuccess) return err;
-    const size_t assign_lds = (size_t)(g.waves_per_tile + 2) * g.num_keys * sizeof(int);
-    void* assign_args[] = {&idx, &pc, &wc, &oc};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, IdxT>), grid, block,
+    return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, false, IdxT>), grid, block,
                            assign_args, assign_lds, stream);
 }
 
