@@ -187,3 +187,35 @@ def test_deterministic_repeats_and_workspace_reuse():
     H.assert_layout_equal(run_s, ref_s)
     run = H.run_gpu(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment, xb, workspace=ws)
     H.assert_layout_equal(run, ref)
+
+
+def test_replay_scatter_with_saved_layout():
+    """Cached dispatch: the layout is computed once and reused to scatter new
+    token batches with the same routing (the page's cached mode, sections 6.2
+    and 8.3); every replay matches the oracle and leaves the layout untouched."""
+    w = _reduced(W.get("dsv3_fp8_a128"), 1500)
+    _banner("replay " + w.describe())
+    inp = W.make_inputs(w)
+    ref = oracle.layout(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment)
+    run = H.run_gpu(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment, inp.x_bytes(), inp.x_sf)
+    H.assert_layout_equal(run, ref)
+    saved = {f.name: getattr(run.layout, f.name).clone() for f in dataclasses.fields(run.layout)}
+    import moe_token_dispatch_amd as M
+
+    for seed in (101, 102):
+        xb = H.random_rows(seed, w.num_tokens, w.row_bytes)
+        sf = np.random.default_rng([seed, 5]).uniform(0.5, 2, (w.num_tokens, w.sf_per_token)).astype(np.float32)
+        x_d = torch.from_numpy(xb).to(H.DEVICE)
+        sf_d = torch.from_numpy(sf).to(H.DEVICE)
+        M.dispatch_scatter(run.problem, run.layout, x_d, sf_d, run.rows.rank_x, run.rows.rank_sf,
+                           run.rows.recv_x, run.rows.recv_sf)
+        torch.cuda.synchronize()
+        run.x, run.x_sf = x_d, sf_d
+        want = oracle.scatter(ref, xb, sf)
+        p_total, n_rank = ref.num_recv_rows, ref.num_rank_rows
+        assert np.array_equal(run.rows.recv_x[:p_total].cpu().numpy(), want.recv_x), seed
+        assert np.array_equal(run.rows.rank_x[:n_rank].cpu().numpy(), want.rank_x), seed
+        assert np.array_equal(run.rows.recv_sf[:p_total].cpu().numpy().view(np.int32), want.recv_sf.view(np.int32))
+        assert np.array_equal(run.rows.rank_sf[:n_rank].cpu().numpy().view(np.int32), want.rank_sf.view(np.int32))
+        for name, t in saved.items():
+            assert torch.equal(getattr(run.layout, name), t), f"scatter changed layout field {name}"
