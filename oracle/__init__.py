@@ -29,6 +29,7 @@ BAD_EXPERT = 1
 RECV_OVERFLOW = 2
 RANK_OVERFLOW = 4
 DUP_EXPERT = 8
+BAD_COUNT = 16
 
 _lib = None
 
@@ -52,6 +53,8 @@ def load_library(path: str):
     lib.oracle_dispatch_scatter.argtypes = [i64, i32, i32, i64, i32, p, p, p, p, p, p,
                                             p, p, p, p, ctypes.c_int]
     lib.oracle_dispatch_scatter.restype = ctypes.c_int
+    lib.oracle_expand_layout.argtypes = [i32, i32, i32, i32, i32, i32, i32, p, p, i64, p, p, p, p]
+    lib.oracle_expand_layout.restype = ctypes.c_int
     return lib
 
 
@@ -130,6 +133,54 @@ def layout(topk_idx: np.ndarray, num_experts: int, num_ranks: int, alignment: in
         _ptr(out.expert_count), _ptr(out.rank_count), _ptr(out.expert_psum), _ptr(out.rank_psum),
         _ptr(out.expert_slot), _ptr(out.rank_slot), _ptr(out.recv_src_token_idx),
         _ptr(out.rank_src_token_idx))
+    if rc < 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    out.status = rc
+    return out
+
+
+@dataclasses.dataclass
+class ExpandLayout:
+    status: int
+    local_experts: int
+    alignment: int
+    expert_count: np.ndarray      # int32 [E/R]
+    expert_psum: np.ndarray       # int32 [E/R + 1]
+    expert_slot: np.ndarray       # int32 [S*M, K]
+    recv_src_row_idx: np.ndarray  # int32 [recv_capacity]
+
+    @property
+    def num_recv_rows(self) -> int:
+        return int(self.expert_psum[-1])
+
+
+def expand_max_rows(num_sources: int, rows_per_source: int, num_topk: int, num_experts: int,
+                    num_ranks: int, alignment: int) -> int:
+    local = num_experts // num_ranks
+    return num_sources * rows_per_source * min(num_topk, local) + local * (max(alignment, 1) - 1)
+
+
+def expand_layout(recv_topk: np.ndarray, recv_count: np.ndarray, num_sources: int, rows_per_source: int,
+                  num_experts: int, num_ranks: int, local_rank: int, alignment: int = 1,
+                  recv_capacity: Optional[int] = None, lib=None) -> ExpandLayout:
+    """Receiver-side expand layout over the local experts of `local_rank`."""
+    lib = _load(lib)
+    topk = np.ascontiguousarray(recv_topk, dtype=np.int64)
+    counts = np.ascontiguousarray(recv_count, dtype=np.int32)
+    rows, k = topk.shape
+    if rows != num_sources * rows_per_source or counts.shape != (num_sources,):
+        raise ValueError("recv_topk must be [S*M, K] and recv_count [S]")
+    local = num_experts // num_ranks
+    cap = expand_max_rows(num_sources, rows_per_source, k, num_experts, num_ranks, alignment) \
+        if recv_capacity is None else recv_capacity
+    out = ExpandLayout(
+        status=0, local_experts=local, alignment=alignment,
+        expert_count=np.zeros(local, np.int32), expert_psum=np.zeros(local + 1, np.int32),
+        expert_slot=np.full((rows, k), CANARY, np.int32),
+        recv_src_row_idx=np.full(max(cap, 0), CANARY, np.int32))
+    rc = lib.oracle_expand_layout(num_sources, rows_per_source, k, num_experts, num_ranks, local_rank,
+                                  alignment, _ptr(topk), _ptr(counts), cap, _ptr(out.expert_count),
+                                  _ptr(out.expert_psum), _ptr(out.expert_slot), _ptr(out.recv_src_row_idx))
     if rc < 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     out.status = rc

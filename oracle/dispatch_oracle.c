@@ -178,3 +178,78 @@ int oracle_dispatch_scatter(int64_t num_tokens, int32_t num_topk, int32_t num_ex
     }
     return 0;
 }
+
+int oracle_expand_layout(int32_t num_sources, int32_t rows_per_source, int32_t num_topk,
+                         int32_t num_experts, int32_t num_ranks, int32_t local_rank,
+                         int32_t expert_alignment, const int64_t* recv_topk,
+                         const int32_t* recv_count, int64_t recv_capacity,
+                         int32_t* expert_count, int32_t* expert_psum, int32_t* expert_slot,
+                         int32_t* recv_src_row_idx) {
+    const int32_t S = num_sources, M = rows_per_source, K = num_topk, E = num_experts, R = num_ranks;
+    const int32_t A = expert_alignment;
+    if (S < 1 || M < 0 || K < 1 || K > 32 || E < 1 || R < 1 || E % R != 0 || local_rank < 0 ||
+        local_rank >= R || A < 1)
+        return ORACLE_BAD_ARGS;
+    const int32_t L = E / R;                  /* local experts */
+    const int64_t first_expert = (int64_t)local_rank * L;
+    const int64_t rows = (int64_t)S * M;
+    if (rows * K + (int64_t)L * (A - 1) > INT32_MAX) return ORACLE_BAD_ARGS;
+    int status = 0;
+
+    /* Received rows: the first recv_count[s] rows of source s's region; the
+     * rest of the region was never written by that source. */
+    for (int32_t s = 0; s < S; ++s)
+        if (recv_count[s] < 0 || recv_count[s] > M) status |= ORACLE_BAD_COUNT;
+
+    /* Count the pairs of every local expert over the received rows. */
+    for (int32_t e = 0; e < L; ++e) expert_count[e] = 0;
+    for (int32_t s = 0; s < S; ++s) {
+        const int32_t n = recv_count[s] < 0 ? 0 : (recv_count[s] > M ? M : recv_count[s]);
+        for (int32_t i = 0; i < n; ++i) {
+            const int64_t* row = recv_topk + ((int64_t)s * M + i) * K;
+            for (int32_t k = 0; k < K; ++k) {
+                const int64_t e = row[k];
+                if (e < 0) continue;
+                if (e >= E) {
+                    status |= ORACLE_BAD_EXPERT;
+                    continue;
+                }
+                if (e < first_expert || e >= first_expert + L) continue;  /* another rank's expert */
+                for (int32_t j = 0; j < k; ++j)
+                    if (row[j] == e) status |= ORACLE_DUP_EXPERT;
+                expert_count[e - first_expert] += 1;
+            }
+        }
+    }
+
+    /* Aligned exclusive prefix sum over the local experts. */
+    int64_t run = 0;
+    expert_psum[0] = 0;
+    for (int32_t e = 0; e < L; ++e) {
+        run += align_up(expert_count[e], A);
+        expert_psum[e + 1] = (int32_t)run;
+    }
+    if (expert_psum[L] > recv_capacity) status |= ORACLE_RECV_OVERFLOW;
+    if (status) return status;
+
+    /* Slots: a cursor per local expert, walking sources, then rows, then k. */
+    int64_t* cursor = (int64_t*)malloc(sizeof(int64_t) * (size_t)L);
+    if (!cursor) return ORACLE_BAD_ARGS;
+    for (int32_t e = 0; e < L; ++e) cursor[e] = expert_psum[e];
+    for (int64_t q = 0; q < expert_psum[L]; ++q) recv_src_row_idx[q] = -1;
+    for (int64_t q = 0; q < rows * K; ++q) expert_slot[q] = -1;
+    for (int32_t s = 0; s < S; ++s) {
+        for (int32_t i = 0; i < recv_count[s]; ++i) {
+            const int64_t r = (int64_t)s * M + i;
+            for (int32_t k = 0; k < K; ++k) {
+                const int64_t e = recv_topk[r * K + k];
+                if (e < first_expert || e >= first_expert + L) continue;
+                const int64_t slot = cursor[e - first_expert]++;
+                expert_slot[r * K + k] = (int32_t)slot;
+                recv_src_row_idx[slot] = (int32_t)r;
+            }
+        }
+    }
+    free(cursor);
+    return 0;
+}

@@ -61,6 +61,25 @@ int oracle_dispatch_scatter(int64_t num_tokens, int32_t num_topk, int32_t num_ex
                             const int32_t* rank_slot, uint8_t* rank_x, uint32_t* rank_sf,
                             uint8_t* recv_x, uint32_t* recv_sf, int zero_pad);
 
+/* Receiver side of the expand (the page's copy epilogue: sections 3, 6.4
+ * and 8.2-8.3): rows received from S source ranks sit in a receive buffer
+ * with M rows per source; source s sent recv_count[s] rows, each carrying its
+ * token's top-k global expert ids recv_topk[S*M, K]. This receiver owns the
+ * experts [local_rank*E/R, (local_rank+1)*E/R). Outputs, over those local
+ * experts: expert_count[E/R], expert_psum[E/R+1] (aligned, exclusive),
+ * expert_slot[S*M*K] (-1 for non-local or unused entries) and
+ * recv_src_row_idx[recv_capacity] (received row index of each slot, -1 on
+ * pads). Rows inside a local expert's bucket follow (source, row) order.
+ * Status: 1 = expert id >= E, 2 = rows exceed capacity, 8 = a local expert
+ * repeated within a row, 16 = a recv_count outside [0, M]. */
+#define ORACLE_BAD_COUNT 16
+int oracle_expand_layout(int32_t num_sources, int32_t rows_per_source, int32_t num_topk,
+                         int32_t num_experts, int32_t num_ranks, int32_t local_rank,
+                         int32_t expert_alignment, const int64_t* recv_topk,
+                         const int32_t* recv_count, int64_t recv_capacity,
+                         int32_t* expert_count, int32_t* expert_psum, int32_t* expert_slot,
+                         int32_t* recv_src_row_idx);
+
 #ifdef __cplusplus
 }
 #endif

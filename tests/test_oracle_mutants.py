@@ -20,7 +20,7 @@ from tests import pins
 SRC = os.path.join(os.path.dirname(oracle.__file__), "dispatch_oracle.c")
 
 LAYOUT_MUTANTS = {
-    "no_alignment": ("run += align_up(expert_count[e], A);", "run += expert_count[e];", 1),
+    "no_alignment": ("run += align_up(expert_count[e], A);", "run += expert_count[e];", 2),
     "floor_alignment": ("return ((c + a - 1) / a) * a;", "return (c / a) * a;", 1),
     "lowest_k_owns_rank_slot": (
         "            for (int32_t j = k + 1; j < K; ++j)\n"
@@ -42,7 +42,7 @@ LAYOUT_MUTANTS = {
     "interleaved_ranks": ("const int64_t r = e / experts_per_rank;", "const int64_t r = e % R;", 2),
     "pads_not_marked": ("recv_src_token_idx[s] = -1;", "recv_src_token_idx[s] = 0;", 1),
     "psum_lags_one_expert": ("        run += align_up(expert_count[e], A);\n        expert_psum[e + 1] = (int32_t)run;",
-                             "        expert_psum[e + 1] = (int32_t)run;\n        run += align_up(expert_count[e], A);", 1),
+                             "        expert_psum[e + 1] = (int32_t)run;\n        run += align_up(expert_count[e], A);", 2),
 }
 
 SCATTER_MUTANTS = {
@@ -119,5 +119,36 @@ def test_scatter_mutant_is_caught(tmp_path, name):
 
 
 def test_unmutated_oracle_passes_same_cases(tmp_path):
-    lib = _mutant_lib(tmp_path, "identity", "int status = 0;", "int status = 0;", 1)
+    lib = _mutant_lib(tmp_path, "identity", "int status = 0;", "int status = 0;", 2)
     assert not _layout_rejected(lib)
+
+
+EXPAND_MUTANTS = {
+    "expand_reads_past_count": ("        for (int32_t i = 0; i < recv_count[s]; ++i) {\n            const int64_t r = (int64_t)s * M + i;",
+                                "        for (int32_t i = 0; i < M; ++i) {\n            const int64_t r = (int64_t)s * M + i;", 1),
+    "expand_sources_reversed": ("    for (int32_t s = 0; s < S; ++s) {\n        for (int32_t i = 0; i < recv_count[s]; ++i) {",
+                                "    for (int32_t s = S - 1; s >= 0; --s) {\n        for (int32_t i = 0; i < recv_count[s]; ++i) {", 1),
+    "expand_wrong_local_base": ("const int64_t first_expert = (int64_t)local_rank * L;",
+                                "const int64_t first_expert = (int64_t)local_rank * L + (local_rank > 0);", 1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EXPAND_MUTANTS))
+def test_expand_mutant_is_caught(tmp_path, name):
+    from tests.test_oracle_pins import _expand_brute_force, _random_topk as rt
+
+    lib = _mutant_lib(tmp_path, name, *EXPAND_MUTANTS[name])
+    rng = np.random.default_rng(17)
+    caught = False
+    for trial in range(6):
+        s_count, m, k, e, r = 3, 20, 4, 32, 4
+        rank, a = trial % r, 1 + trial % 3
+        recv_topk = np.concatenate([rt(rng, m, k, e, mask=0.1) for _ in range(s_count)])
+        counts = rng.integers(5, m, size=s_count).astype(np.int32)
+        got = oracle.expand_layout(recv_topk, counts, s_count, m, e, r, rank, a, lib=lib)
+        cnt, start, slot, src = _expand_brute_force(recv_topk, counts, s_count, m, e, r, rank, a)
+        if (got.status != 0 or not np.array_equal(got.expert_count, cnt) or not np.array_equal(got.expert_psum, start)
+                or not np.array_equal(got.expert_slot.astype(np.int64), slot)):
+            caught = True
+            break
+    assert caught, f"pins did not catch mutant {name}"

@@ -198,3 +198,119 @@ def test_rows_fp8_nan_payload_survives():
     lay = oracle.layout(topk, 8, 4, 4)
     rows = oracle.scatter(lay, x)
     pins.check_rows(lay, x, None, rows)
+
+
+# ---------------------------------------------------------------- receiver-side expand
+
+
+def _receive_from_one_source(topk, num_experts, num_ranks, rank, spare=7):
+    """The rows rank `rank` receives from a single source, laid out like a
+    fixed-stride receive buffer with `spare` unused rows after them."""
+    lay = oracle.layout(topk, num_experts, num_ranks, 1)
+    lo, hi = int(lay.rank_psum[rank]), int(lay.rank_psum[rank + 1])
+    tokens = lay.rank_src_token_idx[lo:hi].astype(np.int64)
+    m = (hi - lo) + spare
+    recv_topk = np.full((m, topk.shape[1]), 12345, dtype=np.int64)  # junk in unused rows
+    recv_topk[: hi - lo] = topk[tokens]
+    return lay, tokens, recv_topk, np.array([hi - lo], dtype=np.int32), m
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_expand_single_source_equals_sender_expert_major_slice(seed):
+    """With one source, the receiver's expert-major layout over its local
+    experts equals the sender's expert-major layout restricted to that rank's
+    experts (the page's expand builds the same buckets, sections 6.4 and 8.2)."""
+    rng = np.random.default_rng([91, seed])
+    e, r, k, t = 64, 8, 6, 300
+    topk = _random_topk(rng, t, k, e, mask=0.1)
+    a = int(rng.choice([1, 4, 16]))
+    for rank in range(r):
+        send, tokens, recv_topk, counts, m = _receive_from_one_source(topk, e, r, rank)
+        sender = oracle.layout(topk, e, r, a)
+        got = oracle.expand_layout(recv_topk, counts, 1, m, e, r, rank, a)
+        assert got.status == 0
+        L = e // r
+        assert np.array_equal(got.expert_count, sender.expert_count[rank * L:(rank + 1) * L])
+        base = int(sender.expert_psum[rank * L])
+        assert np.array_equal(got.expert_psum, sender.expert_psum[rank * L:(rank + 1) * L + 1] - base)
+        p = got.num_recv_rows
+        src = got.recv_src_row_idx[:p]
+        mapped = np.where(src >= 0, tokens[np.maximum(src, 0)], -1)
+        assert np.array_equal(mapped, sender.recv_src_token_idx[base:base + p])
+        # the pair slots agree too, through the received-row -> token map
+        for i, tok in enumerate(tokens):
+            for kk in range(k):
+                ge = topk[tok, kk]
+                if rank * L <= ge < (rank + 1) * L:
+                    assert got.expert_slot[i, kk] == sender.expert_slot[tok, kk] - base
+                else:
+                    assert got.expert_slot[i, kk] == -1
+
+
+def _expand_brute_force(recv_topk, counts, s_count, m, e, r, rank, a):
+    L = e // r
+    lo = rank * L
+    pairs = [(s * m + i, kk, int(recv_topk[s * m + i, kk]) - lo)
+             for s in range(s_count) for i in range(int(counts[s])) for kk in range(recv_topk.shape[1])
+             if lo <= recv_topk[s * m + i, kk] < lo + L]
+    cnt = [sum(1 for p in pairs if p[2] == x) for x in range(L)]
+    span = []
+    for c in cnt:
+        q = 0
+        while q < c:
+            q += a
+        span.append(q)
+    start = [sum(span[:x]) for x in range(L + 1)]
+    slot = np.full(recv_topk.shape, -1, dtype=np.int64)
+    src = [-1] * start[-1]
+    for x in range(L):
+        q = start[x]
+        for row, kk, ex in pairs:  # already in (source, row, k) order
+            if ex == x:
+                slot[row, kk] = q
+                src[q] = row
+                q += 1
+    return np.array(cnt), np.array(start), slot, np.array(src, dtype=np.int64)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_expand_multi_source_brute_force(seed):
+    rng = np.random.default_rng([92, seed])
+    s_count, m, k, e, r = int(rng.integers(1, 5)), int(rng.integers(0, 40)), 4, 32, 4
+    rank, a = int(rng.integers(0, r)), int(rng.choice([1, 3, 8]))
+    recv_topk = np.full((s_count * m, k), -1, dtype=np.int64)
+    counts = rng.integers(0, m + 1, size=s_count).astype(np.int32)
+    for s in range(s_count):
+        blk = _random_topk(rng, m, k, e, mask=0.15)
+        recv_topk[s * m:(s + 1) * m] = blk
+    got = oracle.expand_layout(recv_topk, counts, s_count, m, e, r, rank, a)
+    assert got.status == 0
+    cnt, start, slot, src = _expand_brute_force(recv_topk, counts, s_count, m, e, r, rank, a)
+    assert np.array_equal(got.expert_count, cnt)
+    assert np.array_equal(got.expert_psum, start)
+    assert np.array_equal(got.expert_slot.astype(np.int64), slot)
+    assert np.array_equal(got.recv_src_row_idx[:start[-1]].astype(np.int64), src)
+    assert np.all(got.recv_src_row_idx[start[-1]:] == oracle.CANARY)
+
+
+def test_expand_status_bits():
+    recv_topk = np.array([[0, 1], [2, 3], [0, 2], [1, 3]], dtype=np.int64)
+    counts = np.array([2, 2], dtype=np.int32)
+    assert oracle.expand_layout(recv_topk, counts, 2, 2, 4, 2, 0, 1).status == 0
+    assert oracle.expand_layout(recv_topk, np.array([3, 2], np.int32), 2, 2, 4, 2, 0, 1).status == oracle.BAD_COUNT
+    assert oracle.expand_layout(recv_topk, np.array([-1, 2], np.int32), 2, 2, 4, 2, 0, 1).status == oracle.BAD_COUNT
+    bad = recv_topk.copy()
+    bad[1, 0] = 4
+    assert oracle.expand_layout(bad, counts, 2, 2, 4, 2, 0, 1).status == oracle.BAD_EXPERT
+    dup = recv_topk.copy()
+    dup[0, 1] = 0  # local expert 0 twice in one row
+    assert oracle.expand_layout(dup, counts, 2, 2, 4, 2, 0, 1).status == oracle.DUP_EXPERT
+    dup_remote = recv_topk.copy()
+    dup_remote[1] = [3, 3]  # another rank's expert twice: not this receiver's concern
+    assert oracle.expand_layout(dup_remote, counts, 2, 2, 4, 2, 0, 1).status == 0
+    # rank 0 owns experts 0, 1: rows 0 (0, 1), 2 (0), 3 (1) -> 4 pairs
+    assert oracle.expand_layout(recv_topk, counts, 2, 2, 4, 2, 0, 1, recv_capacity=3).status == oracle.RECV_OVERFLOW
+    # rows past a source's count are never read, whatever they hold
+    junk = recv_topk.copy()
+    junk[1] = [99, 99]
+    assert oracle.expand_layout(junk, np.array([1, 2], np.int32), 2, 2, 4, 2, 0, 1).status == 0
