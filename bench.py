@@ -47,6 +47,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for counter calibration)")
+    ap.add_argument("--expand", action="store_true",
+                    help="measure the receiver-side expand instead: S sources of the workload send to rank 0")
+    ap.add_argument("--sources", type=int, default=8, help="sources for --expand")
     return ap.parse_args()
 
 
@@ -150,6 +153,89 @@ def cpu_baseline(inp, w, budget_s):
     return statistics.median(times), len(times)
 
 
+def expand_bench(args):
+    """Receiver-side expand: S sources, each the chosen workload with its own
+    seed, run the sender path on the GPU; receiver rank 0 gets every source's
+    rank-0 block in a fixed-stride receive buffer (T rows per source, the
+    most a source can send) and expands it into its expert-major buffer."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import moe_token_dispatch_amd as M
+    import workloads as W
+
+    dev = "cuda:0"
+    base = W.get(args.workload or W.METRIC_WORKLOAD)
+    s_count, rank = args.sources, 0
+    t, k, e, r = base.num_tokens, base.num_topk, base.num_experts, base.num_ranks
+    s_f, rb = base.sf_per_token, base.row_bytes
+    m = t
+    recv_buf = torch.zeros((s_count * m, rb), dtype=torch.uint8, device=dev)
+    recv_sf = torch.zeros((s_count * m, s_f), dtype=torch.float32, device=dev) if s_f else None
+    recv_topk = torch.full((s_count * m, k), -1, dtype=torch.int64, device=dev)
+    counts = torch.zeros(s_count, dtype=torch.int32, device=dev)
+    for s in range(s_count):
+        w = dataclasses.replace(base, seed=base.seed * 1000 + s)
+        inp = W.make_inputs(w)
+        prob = M.make_problem(t, k, e, r, w.alignment, 8, rb, s_f)
+        lay, ws, rows = M.alloc_layout(prob, dev), M.alloc_workspace(prob, dev), M.alloc_rows(prob, dev)
+        topk_d = torch.from_numpy(inp.topk_idx).to(dev)
+        x_d = inp.x.view(torch.uint8).to(dev)
+        sf_d = None if inp.x_sf is None else torch.from_numpy(inp.x_sf).to(dev)
+        M.dispatch_layout(prob, topk_d, lay, ws)
+        M.dispatch_scatter(prob, lay, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x, rows.recv_sf)
+        lo, hi = int(lay.rank_psum[rank].item()), int(lay.rank_psum[rank + 1].item())
+        n = hi - lo
+        # Stand-in for the transport: the block lands at the source's region.
+        recv_buf[s * m:s * m + n] = rows.rank_x[lo:hi]
+        if s_f:
+            recv_sf[s * m:s * m + n] = rows.rank_sf[lo:hi]
+        recv_topk[s * m:s * m + n] = topk_d.index_select(0, lay.rank_src_token_idx[lo:hi].long())
+        counts[s] = n
+        del lay, ws, rows, topk_d, x_d, sf_d
+    q = M.make_expand_problem(s_count, m, k, e, r, rank, base.alignment, 8, rb, s_f)
+    elay = M.alloc_expand_layout(q, dev)
+    ews = M.alloc_expand_workspace(q, dev)
+    recv_x = torch.empty((max(q.recv_capacity_rows, 1), rb), dtype=torch.uint8, device=dev)
+    out_sf = torch.empty((max(q.recv_capacity_rows, 1), s_f), dtype=torch.float32, device=dev) if s_f else None
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        M.dispatch_expand_layout(q, recv_topk, counts, elay, ews, stream)
+        M.dispatch_expand_scatter(q, elay, recv_buf, recv_sf, recv_x, out_sf, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(elay.status.item()) != 0:
+        raise RuntimeError(f"expand status {int(elay.status.item())}")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    received = int(counts.sum().item())
+    p_rows = int(elay.expert_psum[-1].item())
+    local = e // r
+    row = rb + 4 * s_f
+    total_b = received * k * 8 + 4 * s_count + received * row + p_rows * row + \
+        4 * (2 * local + 2 + s_count * m * k + p_rows)
+    out = {
+        "metric": "receiver-side expand GB/s & % HBM peak",
+        "value": round(total_b / dt / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": f"expand of {s_count} x {base.name} into rank {rank}", "sources": s_count,
+                   "rows_per_source": m, "received_rows": received, "expert_major_rows": p_rows,
+                   "local_experts": local, "expert_alignment": base.alignment},
+        "hbm_frac": round(total_b / dt / 1e9 / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": total_b,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -158,6 +244,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.expand:
+        expand_bench(args)
         return
 
     import numpy as np

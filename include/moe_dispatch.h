@@ -68,6 +68,7 @@ extern "C" {
 #define DISPATCH_STATUS_RECV_OVERFLOW 2u  /* expert_psum[E] > recv_capacity_rows */
 #define DISPATCH_STATUS_RANK_OVERFLOW 4u  /* rank_psum[R] > rank_capacity_rows */
 #define DISPATCH_STATUS_DUP_EXPERT 8u     /* an expert repeated within one token */
+#define DISPATCH_STATUS_BAD_COUNT 16u     /* expand: a recv_count outside [0, rows_per_source] */
 
 /* Output selection for dispatch_scatter. */
 #define DISPATCH_RANK_CONTIG 1u  /* write rank_x (and rank_sf) */
@@ -143,6 +144,57 @@ int dispatch_layout(const dispatch_problem_t* problem, const void* topk_idx,
 int dispatch_scatter(const dispatch_problem_t* problem, const dispatch_layout_t* layout,
                      const void* x, const float* x_sf, void* rank_x, float* rank_sf,
                      void* recv_x, float* recv_sf, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Receiver-side expand (the page's copy epilogue: sections 3, 6.4, 8.2, 8.3
+ * and 12). A receiver rank holds the rows S source ranks sent it in a receive
+ * buffer with a fixed stride of rows_per_source rows per source (the page's
+ * kNumMaxTokensPerRank); source s sent recv_count[s] rows, the first ones of
+ * its region, and every row comes with its token's K global expert ids. The
+ * receiver owns the experts [local_rank*E/R, (local_rank+1)*E/R) and builds
+ * the expert-major layout over them: rows of a local expert follow (source,
+ * row) order, buckets are padded to the expert alignment.
+ * ------------------------------------------------------------------------- */
+typedef struct dispatch_expand_problem {
+    int32_t num_sources;        /* S >= 1 */
+    int32_t rows_per_source;    /* M >= 0 rows of the receive buffer per source */
+    int32_t num_topk;           /* K, 1..DISPATCH_MAX_TOPK */
+    int32_t num_experts;        /* E of the sending side (global ids), 1..DISPATCH_MAX_EXPERTS */
+    int32_t num_ranks;          /* R, 1..DISPATCH_MAX_RANKS, E % R == 0 */
+    int32_t local_rank;         /* this receiver, 0..R-1 */
+    int32_t expert_alignment;   /* A >= 1 */
+    int32_t topk_idx_bytes;     /* 8 (int64) or 4 (int32) */
+    int32_t sf_per_token;       /* fp32 scale factors per row, >= 0 */
+    uint32_t reserved;          /* must be 0 */
+    int64_t row_bytes;          /* bytes per row, multiple of 16, 16..2^31-16 (expand_scatter only) */
+    int64_t recv_capacity_rows; /* rows of the expert-major output */
+} dispatch_expand_problem_t;
+
+/* Workspace bytes for dispatch_expand_layout (same rules as dispatch_layout). */
+int dispatch_expand_workspace_size(const dispatch_expand_problem_t* problem, size_t* bytes);
+
+/* Worst-case expert-major rows: S*M*min(K, E/R) + (E/R)*(A-1). */
+int dispatch_expand_max_rows(const dispatch_expand_problem_t* problem, int64_t* max_recv_rows);
+
+/* Expert-major layout of a receive buffer. recv_topk_idx: device [S*M, K]
+ * global expert ids (rows past a source's count are never read). recv_count:
+ * device int32 [S]. `out` uses dispatch_layout_t with its rank fields NULL:
+ * expert_count[E/R], expert_psum[E/R+1], expert_slot[S*M*K] (-1 for another
+ * rank's expert, a masked entry or an unused row), recv_src_token_idx
+ * [recv_capacity_rows] holding the receive-buffer row of each slot (-1 on
+ * pads), status (DISPATCH_STATUS_*; BAD_EXPERT for an id >= E, DUP_EXPERT for
+ * a local expert twice in a row, BAD_COUNT for a count outside [0, M]). */
+int dispatch_expand_layout(const dispatch_expand_problem_t* problem, const void* recv_topk_idx,
+                           const int32_t* recv_count, const dispatch_layout_t* out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* Copies the received rows (recv_buf [S*M, row_bytes], recv_sf_buf [S*M, sf])
+ * into the expert-major recv_x / recv_sf of a layout made by
+ * dispatch_expand_layout, zeroing pad rows. Writes nothing when the layout's
+ * status is non-zero. */
+int dispatch_expand_scatter(const dispatch_expand_problem_t* problem, const dispatch_layout_t* layout,
+                            const void* recv_buf, const float* recv_sf_buf, void* recv_x, float* recv_sf,
+                            hipStream_t stream);
 
 #ifdef __cplusplus
 }

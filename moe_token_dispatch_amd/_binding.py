@@ -33,6 +33,7 @@ STATUS_BAD_EXPERT = 1
 STATUS_RECV_OVERFLOW = 2
 STATUS_RANK_OVERFLOW = 4
 STATUS_DUP_EXPERT = 8
+STATUS_BAD_COUNT = 16
 
 RANK_CONTIG = 1
 EXPERT_MAJOR = 2
@@ -73,11 +74,32 @@ class LayoutPtrs(ctypes.Structure):
         "recv_src_token_idx", "rank_src_token_idx", "status")]
 
 
+class ExpandProblem(ctypes.Structure):
+    """dispatch_expand_problem_t."""
+
+    _fields_ = [
+        ("num_sources", ctypes.c_int32),
+        ("rows_per_source", ctypes.c_int32),
+        ("num_topk", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("num_ranks", ctypes.c_int32),
+        ("local_rank", ctypes.c_int32),
+        ("expert_alignment", ctypes.c_int32),
+        ("topk_idx_bytes", ctypes.c_int32),
+        ("sf_per_token", ctypes.c_int32),
+        ("reserved", ctypes.c_uint32),
+        ("row_bytes", ctypes.c_int64),
+        ("recv_capacity_rows", ctypes.c_int64),
+    ]
+
+
 _LIB = None
 
 # Exported symbols of include/moe_dispatch.h.
 SYMBOLS = ("dispatch_abi_version", "dispatch_strerror", "dispatch_workspace_size",
-           "dispatch_max_rows", "dispatch_layout", "dispatch_scatter")
+           "dispatch_max_rows", "dispatch_layout", "dispatch_scatter",
+           "dispatch_expand_workspace_size", "dispatch_expand_max_rows", "dispatch_expand_layout",
+           "dispatch_expand_scatter")
 
 
 def load_library(path: str = LIB_PATH):
@@ -102,6 +124,15 @@ def load_library(path: str = LIB_PATH):
     lib.dispatch_layout.restype = i
     lib.dispatch_scatter.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(LayoutPtrs), p, p, p, p, p, p, p]
     lib.dispatch_scatter.restype = i
+    ep = ctypes.POINTER(ExpandProblem)
+    lib.dispatch_expand_workspace_size.argtypes = [ep, ctypes.POINTER(sz)]
+    lib.dispatch_expand_workspace_size.restype = i
+    lib.dispatch_expand_max_rows.argtypes = [ep, ctypes.POINTER(ctypes.c_int64)]
+    lib.dispatch_expand_max_rows.restype = i
+    lib.dispatch_expand_layout.argtypes = [ep, p, p, ctypes.POINTER(LayoutPtrs), p, sz, p]
+    lib.dispatch_expand_layout.restype = i
+    lib.dispatch_expand_scatter.argtypes = [ep, ctypes.POINTER(LayoutPtrs), p, p, p, p, p]
+    lib.dispatch_expand_scatter.restype = i
     if lib.dispatch_abi_version() != ABI_VERSION:
         raise ImportError(f"{path}: ABI version {lib.dispatch_abi_version()} != {ABI_VERSION}")
     _LIB = lib
@@ -321,3 +352,96 @@ class Plan:
     def __call__(self) -> None:
         self.layout()
         self.scatter()
+
+
+# ------------------------------------------------------------ receiver-side expand
+
+
+def make_expand_problem(num_sources: int, rows_per_source: int, num_topk: int, num_experts: int,
+                        num_ranks: int, local_rank: int, expert_alignment: int = 1, topk_idx_bytes: int = 8,
+                        row_bytes: int = 16, sf_per_token: int = 0,
+                        recv_capacity_rows: Optional[int] = None) -> ExpandProblem:
+    """An expand problem; the capacity defaults to the library's worst case."""
+    q = ExpandProblem(num_sources, rows_per_source, num_topk, num_experts, num_ranks, local_rank,
+                      expert_alignment, topk_idx_bytes, sf_per_token, 0, row_bytes, 0)
+    cap = ctypes.c_int64(0)
+    rc = load_library().dispatch_expand_max_rows(ctypes.byref(q), ctypes.byref(cap))
+    if rc:
+        raise DispatchError(rc, "dispatch_expand_max_rows")
+    q.recv_capacity_rows = int(cap.value) if recv_capacity_rows is None else recv_capacity_rows
+    return q
+
+
+def dispatch_expand_workspace_size(problem: ExpandProblem) -> int:
+    out = ctypes.c_size_t(0)
+    rc = load_library().dispatch_expand_workspace_size(ctypes.byref(problem), ctypes.byref(out))
+    if rc:
+        raise DispatchError(rc, "dispatch_expand_workspace_size")
+    return int(out.value)
+
+
+@dataclasses.dataclass
+class ExpandLayoutTensors:
+    """Device int32 outputs of dispatch_expand_layout."""
+
+    expert_count: torch.Tensor        # [E/R]
+    expert_psum: torch.Tensor         # [E/R + 1]
+    expert_slot: torch.Tensor         # [S*M, K]
+    recv_src_row_idx: torch.Tensor    # [recv_capacity_rows]
+    status: torch.Tensor              # [1]
+
+    def ptrs(self) -> LayoutPtrs:
+        return LayoutPtrs(self.expert_count.data_ptr(), None, self.expert_psum.data_ptr(), None,
+                          self.expert_slot.data_ptr(), None, self.recv_src_row_idx.data_ptr(), None,
+                          self.status.data_ptr())
+
+
+def alloc_expand_layout(problem: ExpandProblem, device) -> ExpandLayoutTensors:
+    i32 = dict(dtype=torch.int32, device=device)
+    local = problem.num_experts // problem.num_ranks
+    rows = problem.num_sources * problem.rows_per_source
+    return ExpandLayoutTensors(
+        expert_count=torch.empty(local, **i32), expert_psum=torch.empty(local + 1, **i32),
+        expert_slot=torch.empty((rows, problem.num_topk), **i32),
+        recv_src_row_idx=torch.empty(max(problem.recv_capacity_rows, 1), **i32),
+        status=torch.empty(1, **i32))
+
+
+def alloc_expand_workspace(problem: ExpandProblem, device) -> torch.Tensor:
+    n = dispatch_expand_workspace_size(problem)
+    return torch.empty((n + 255) // 256 * 256, dtype=torch.uint8, device=device)
+
+
+def dispatch_expand_layout(problem: ExpandProblem, recv_topk_idx: torch.Tensor, recv_count: torch.Tensor,
+                           out: ExpandLayoutTensors, workspace: torch.Tensor,
+                           stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Enqueue the receiver's expert-major layout of a receive buffer."""
+    _check_device_tensor(recv_topk_idx, "recv_topk_idx")
+    if recv_topk_idx.element_size() != problem.topk_idx_bytes:
+        raise ValueError("recv_topk_idx element width does not match problem.topk_idx_bytes")
+    _check_device_tensor(recv_count, "recv_count", torch.int32)
+    _check_device_tensor(workspace, "workspace")
+    for f in dataclasses.fields(out):
+        _check_device_tensor(getattr(out, f.name), f.name, torch.int32)
+    lay = out.ptrs()
+    rc = load_library().dispatch_expand_layout(
+        ctypes.byref(problem), _ptr(recv_topk_idx), _ptr(recv_count), ctypes.byref(lay), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream_handle(stream, recv_topk_idx.device))
+    if rc:
+        raise DispatchError(rc, "dispatch_expand_layout")
+
+
+def dispatch_expand_scatter(problem: ExpandProblem, layout: ExpandLayoutTensors, recv_buf: torch.Tensor,
+                            recv_sf_buf: Optional[torch.Tensor], recv_x: torch.Tensor,
+                            recv_sf: Optional[torch.Tensor], stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Enqueue the copy of received rows into the expert-major buffer."""
+    _check_device_tensor(recv_buf, "recv_buf")
+    for name, t in (("recv_sf_buf", recv_sf_buf), ("recv_x", recv_x), ("recv_sf", recv_sf)):
+        if t is not None:
+            _check_device_tensor(t, name)
+    lay = layout.ptrs()
+    rc = load_library().dispatch_expand_scatter(ctypes.byref(problem), ctypes.byref(lay), _ptr(recv_buf),
+                                                _ptr(recv_sf_buf), _ptr(recv_x), _ptr(recv_sf),
+                                                _stream_handle(stream, recv_buf.device))
+    if rc:
+        raise DispatchError(rc, "dispatch_expand_scatter")

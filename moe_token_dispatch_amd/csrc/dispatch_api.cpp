@@ -34,6 +34,31 @@ int check_problem(const dispatch_problem_t* p) {
     return DISPATCH_OK;
 }
 
+// The receiver-side expand runs the dispatch kernels on the receive buffer
+// seen as a batch of S*M rows over the E/R local experts and a single rank.
+int check_expand(const dispatch_expand_problem_t* q, dispatch_problem_t* p) {
+    if (q == nullptr) return DISPATCH_ERR_NULL;
+    if (q->num_sources < 1 || q->rows_per_source < 0 || q->reserved != 0) return DISPATCH_ERR_ARG;
+    if (q->num_ranks < 1 || q->num_ranks > DISPATCH_MAX_RANKS || q->num_experts < 1 ||
+        q->num_experts > DISPATCH_MAX_EXPERTS || q->num_experts % q->num_ranks != 0)
+        return DISPATCH_ERR_ARG;
+    if (q->local_rank < 0 || q->local_rank >= q->num_ranks) return DISPATCH_ERR_ARG;
+    *p = dispatch_problem_t{};
+    p->num_tokens = int64_t(q->num_sources) * q->rows_per_source;
+    p->num_topk = q->num_topk;
+    p->num_experts = q->num_experts / q->num_ranks;
+    p->num_ranks = 1;
+    p->expert_alignment = q->expert_alignment;
+    p->topk_idx_bytes = q->topk_idx_bytes;
+    p->sf_per_token = q->sf_per_token;
+    p->row_bytes = q->row_bytes;
+    p->recv_capacity_rows = q->recv_capacity_rows;
+    p->rank_capacity_rows = INT64_MAX;  // no rank outputs; never an overflow
+    p->flags = DISPATCH_EXPERT_MAJOR | DISPATCH_ZERO_PAD;
+    p->reserved = 0;
+    return check_problem(p);
+}
+
 }  // namespace
 
 extern "C" {
@@ -116,7 +141,7 @@ int dispatch_scatter(const dispatch_problem_t* problem, const dispatch_layout_t*
     const bool want_expert = (p.flags & DISPATCH_EXPERT_MAJOR) != 0;
     const bool want_sf = p.sf_per_token > 0;
     if (p.num_tokens > 0) {
-        if (!x || !layout->expert_slot || !layout->rank_slot) return DISPATCH_ERR_NULL;
+        if (!x || !layout->expert_slot || (want_rank && !layout->rank_slot)) return DISPATCH_ERR_NULL;
         if (want_sf && !x_sf) return DISPATCH_ERR_NULL;
     }
     if (want_rank && p.rank_capacity_rows > 0 && (!rank_x || (want_sf && !rank_sf))) return DISPATCH_ERR_NULL;
@@ -132,6 +157,65 @@ int dispatch_scatter(const dispatch_problem_t* problem, const dispatch_layout_t*
     if (moe_dispatch::launch_scatter(p, *layout, x, x_sf, rank_x, rank_sf, recv_x, recv_sf, stream) != hipSuccess)
         return DISPATCH_ERR_HIP;
     return DISPATCH_OK;
+}
+
+int dispatch_expand_workspace_size(const dispatch_expand_problem_t* problem, size_t* bytes) {
+    dispatch_problem_t p;
+    int rc = check_expand(problem, &p);
+    if (rc != DISPATCH_OK) return rc;
+    return dispatch_workspace_size(&p, bytes);
+}
+
+int dispatch_expand_max_rows(const dispatch_expand_problem_t* problem, int64_t* max_recv_rows) {
+    dispatch_problem_t p;
+    int rc = check_expand(problem, &p);
+    if (rc != DISPATCH_OK) return rc;
+    if (max_recv_rows) {
+        const int64_t k = p.num_topk < p.num_experts ? p.num_topk : p.num_experts;
+        *max_recv_rows = p.num_tokens * k + int64_t(p.num_experts) * (p.expert_alignment - 1);
+    }
+    return DISPATCH_OK;
+}
+
+int dispatch_expand_layout(const dispatch_expand_problem_t* problem, const void* recv_topk_idx,
+                           const int32_t* recv_count, const dispatch_layout_t* out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+    dispatch_problem_t p;
+    int rc = check_expand(problem, &p);
+    if (rc != DISPATCH_OK) return rc;
+    if (out == nullptr || !out->expert_count || !out->expert_psum || !out->status) return DISPATCH_ERR_NULL;
+    if (out->rank_count || out->rank_psum || out->rank_slot || out->rank_src_token_idx) return DISPATCH_ERR_ARG;
+    if (p.num_tokens > 0 && (!recv_topk_idx || !out->expert_slot)) return DISPATCH_ERR_NULL;
+    if (!recv_count) return DISPATCH_ERR_NULL;
+    if (p.recv_capacity_rows > 0 && !out->recv_src_token_idx) return DISPATCH_ERR_NULL;
+    if (workspace == nullptr) return DISPATCH_ERR_WORKSPACE;
+    if (recv_topk_idx && !aligned_to(recv_topk_idx, p.topk_idx_bytes)) return DISPATCH_ERR_ALIGN;
+    const void* ints[] = {recv_count, out->expert_count, out->expert_psum, out->expert_slot,
+                          out->recv_src_token_idx, out->status};
+    for (const void* q : ints)
+        if (q && !aligned_to(q, 4)) return DISPATCH_ERR_ALIGN;
+    if (!aligned_to(workspace, 256)) return DISPATCH_ERR_WORKSPACE;
+    const TileGeometry g = moe_dispatch::make_geometry(p.num_tokens, p.num_topk, p.num_experts, p.num_ranks);
+    if (workspace_bytes < moe_dispatch::workspace_bytes(g)) return DISPATCH_ERR_WORKSPACE;
+    moe_dispatch::ExpandView view;
+    view.recv_count = recv_count;
+    view.rows_per_source = problem->rows_per_source;
+    view.first_expert = problem->local_rank * (problem->num_experts / problem->num_ranks);
+    view.global_experts = problem->num_experts;
+    if (moe_dispatch::launch_layout(p, g, recv_topk_idx, *out, workspace, stream, &view) != hipSuccess)
+        return DISPATCH_ERR_HIP;
+    return DISPATCH_OK;
+}
+
+int dispatch_expand_scatter(const dispatch_expand_problem_t* problem, const dispatch_layout_t* layout,
+                            const void* recv_buf, const float* recv_sf_buf, void* recv_x, float* recv_sf,
+                            hipStream_t stream) {
+    dispatch_problem_t p;
+    int rc = check_expand(problem, &p);
+    if (rc != DISPATCH_OK) return rc;
+    if (layout != nullptr && (layout->rank_slot || layout->rank_count)) return DISPATCH_ERR_ARG;
+    p.rank_capacity_rows = 0;
+    return dispatch_scatter(&p, layout, recv_buf, recv_sf_buf, nullptr, nullptr, recv_x, recv_sf, stream);
 }
 
 }  // extern "C"

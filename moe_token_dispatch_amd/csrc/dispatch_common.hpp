@@ -19,7 +19,7 @@ namespace moe_dispatch {
 
 constexpr int kWave = 64;             // gfx950 wavefront width
 constexpr int kLayoutThreads = 1024;  // at most 16 wavefronts per layout workgroup
-constexpr int kScanSegments = 16;     // wavefronts per column-scan workgroup
+constexpr int kScanThreads = 1024;    // threads per column-scan workgroup
 constexpr int kMaxTilesTarget = 512;  // more chunks per wavefront beyond this many tiles
 constexpr int kFewTiles = 8;          // up to this many tiles, assign reduces the histograms itself
 constexpr int kFewTileWaves = 16;     // wavefronts per tile on the few-tiles path
@@ -92,9 +92,19 @@ inline TileGeometry make_geometry(int64_t num_tokens, int32_t num_topk, int32_t 
 // totals[num_keys] and tile_err[num_tiles], int32, each 256-byte aligned.
 inline size_t workspace_bytes(const TileGeometry& g) { return g.ws_bytes; }
 
+// How the receiver-side expand sees its receive buffer through the layout
+// kernels (see dispatch_expand_layout).
+struct ExpandView {
+    const int32_t* recv_count;  // [num_sources] rows each source sent
+    int32_t rows_per_source;    // receive-buffer rows per source
+    int32_t first_expert;       // first global expert id owned by this receiver
+    int32_t global_experts;     // E of the sending side
+};
+
 // Launchers (defined in the .hip files). They return the HIP error of the launch.
 hipError_t launch_layout(const dispatch_problem_t& p, const TileGeometry& g, const void* topk_idx,
-                         const dispatch_layout_t& out, void* workspace, hipStream_t stream);
+                         const dispatch_layout_t& out, void* workspace, hipStream_t stream,
+                         const ExpandView* expand = nullptr);
 hipError_t launch_scatter(const dispatch_problem_t& p, const dispatch_layout_t& lay, const void* x,
                           const float* x_sf, void* rank_x, float* rank_sf, void* recv_x,
                           float* recv_sf, hipStream_t stream);

@@ -56,6 +56,14 @@ struct LayoutParams {
     int32_t tokens_per_tile;
     int32_t num_keys;
     int32_t num_tiles;
+    // Receiver-side expand only: the table is a fixed-stride receive buffer
+    // of rows_per_source rows per source, source s holding recv_count[s]
+    // rows; its expert ids are global, this receiver owns
+    // [first_expert, first_expert + num_experts).
+    const int32_t* recv_count;
+    int32_t rows_per_source;
+    int32_t first_expert;
+    int32_t global_experts;
 };
 
 // Where one lane's pair lands inside its wavefront's chunks.
@@ -131,14 +139,29 @@ __device__ __forceinline__ PairPos rank_chunk(int64_t entry, int lane, int token
     return pos;
 }
 
-template <int CH, typename IdxT>
+// Loads this lane's entry of each of the wavefront's chunks. With EXPAND,
+// the entry is seen from the receiver: rows past their source's count are
+// masked, another rank's experts are masked, local experts are renumbered
+// from 0 and an id >= the global expert count becomes num_experts, which
+// rank_chunk reports as a bad expert.
+template <int CH, bool EXPAND, typename IdxT>
 __device__ __forceinline__ void load_entries(const IdxT* __restrict__ topk, int64_t wave_tok0, int token_in_chunk,
-                                             int k, const LayoutParams& p, int64_t (&entry)[CH]) {
+                                             int k, const LayoutParams& p, int64_t (&entry)[CH], uint32_t& err) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int64_t tok = wave_tok0 + (int64_t)c * p.tokens_per_chunk + token_in_chunk;
         const bool live = token_in_chunk < p.tokens_per_chunk && tok < p.num_tokens;
-        entry[c] = live ? (int64_t)topk[tok * p.num_topk + k] : -1;
+        int64_t v = live ? (int64_t)topk[tok * p.num_topk + k] : -1;
+        if (EXPAND && live) {
+            const int64_t src = tok / p.rows_per_source;
+            const int64_t row = tok - src * p.rows_per_source;
+            const int count = p.recv_count[src];
+            if (count < 0 || count > p.rows_per_source) err |= DISPATCH_STATUS_BAD_COUNT;
+            if (row >= count) v = -1;
+            else if (v >= p.global_experts) v = p.num_experts;
+            else if (v >= 0) v = (v >= p.first_expert && v < p.first_expert + p.num_experts) ? v - p.first_expert : -1;
+        }
+        entry[c] = v;
     }
 }
 
@@ -193,7 +216,7 @@ struct Workspace {
     int32_t* tile_err;     // [num_tiles] DISPATCH_STATUS_* bits seen by the tile
 };
 
-template <int CH, typename IdxT>
+template <int CH, bool EXPAND, typename IdxT>
 __global__ void __launch_bounds__(kLayoutThreads)
 count_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws) {
     extern __shared__ int lds[];  // [W][num_keys] wavefront counters
@@ -210,14 +233,14 @@ count_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws) {
     const int k = lane - token_in_chunk * p.num_topk;
     const int64_t wave_tok0 = (int64_t)blockIdx.x * p.tokens_per_tile + (int64_t)wave * p.tokens_per_wave;
     int64_t entry[CH];
-    load_entries<CH>(topk, wave_tok0, token_in_chunk, k, p, entry);
     uint32_t err = 0;
+    load_entries<CH, EXPAND>(topk, wave_tok0, token_in_chunk, k, p, entry, err);
 #pragma unroll
     for (int c = 0; c < CH; ++c) (void)rank_chunk(entry[c], lane, token_in_chunk, p, counters, err);
-    const uint64_t any_bad = __ballot((err & DISPATCH_STATUS_BAD_EXPERT) != 0);
-    const uint64_t any_dup = __ballot((err & DISPATCH_STATUS_DUP_EXPERT) != 0);
-    if (lane == 0 && (any_bad | any_dup))
-        atomicOr(&block_err, (any_bad ? DISPATCH_STATUS_BAD_EXPERT : 0u) | (any_dup ? DISPATCH_STATUS_DUP_EXPERT : 0u));
+    uint32_t wave_err = 0;
+    for (uint32_t bit = 1; bit <= DISPATCH_STATUS_BAD_COUNT; bit <<= 1)
+        if (__ballot((err & bit) != 0)) wave_err |= bit;
+    if (lane == 0 && wave_err) atomicOr(&block_err, wave_err);
     __syncthreads();
 
     int32_t* row = ws.tile_hist + (int64_t)blockIdx.x * nkeys;
@@ -229,34 +252,42 @@ count_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws) {
     if (tid == 0) ws.tile_err[blockIdx.x] = (int32_t)block_err;
 }
 
-// Column scan of the tile histograms: 64 keys per workgroup (one per lane),
-// the tiles split into kScanSegments contiguous segments (one per wavefront).
-__global__ void __launch_bounds__(kScanSegments * kWave)
-colscan_kernel(LayoutParams p, Workspace ws) {
-    __shared__ int seg_sum[kScanSegments][kWave];
-    const int lane = threadIdx.x & (kWave - 1), seg = threadIdx.x / kWave;
-    const int j = blockIdx.x * kWave + lane;
+// Column scan of the tile histograms. A workgroup takes kpb = min(64, keys)
+// consecutive keys; its kScanThreads threads are (segment, key) pairs, the
+// tiles split into kScanThreads / kpb contiguous segments.
+__global__ void __launch_bounds__(kScanThreads)
+colscan_kernel(LayoutParams p, Workspace ws, int kpb) {
+    __shared__ int seg_sum[kScanThreads];
+    const int nseg = kScanThreads / kpb;
+    const int kk = threadIdx.x % kpb, seg = threadIdx.x / kpb;
+    const bool active = seg < nseg;
+    const int j = blockIdx.x * kpb + kk;
     const int nkeys = p.num_keys, n = p.num_tiles;
-    const int per = (n + kScanSegments - 1) / kScanSegments;
-    const int lo = min(n, seg * per), hi = min(n, lo + per);
+    const int per = (n + nseg - 1) / nseg;
+    const int lo = active ? min(n, seg * per) : n, hi = active ? min(n, lo + per) : n;
+    // Unrolled so that several independent loads are in flight per thread.
     int s = 0;
-    if (j < nkeys)
-        for (int i = lo; i < hi; ++i) s += ws.tile_hist[(int64_t)i * nkeys + j];
-    seg_sum[seg][lane] = s;
-    __syncthreads();
-    int run = 0;
-    for (int q = 0; q < seg; ++q) run += seg_sum[q][lane];
     if (j < nkeys) {
+#pragma unroll 8
+        for (int i = lo; i < hi; ++i) s += ws.tile_hist[(int64_t)i * nkeys + j];
+    }
+    if (active) seg_sum[seg * kpb + kk] = s;
+    __syncthreads();
+    if (!active) return;
+    int run = 0;
+    for (int q = 0; q < seg; ++q) run += seg_sum[q * kpb + kk];
+    if (j < nkeys) {
+#pragma unroll 8
         for (int i = lo; i < hi; ++i) {
             const int h = ws.tile_hist[(int64_t)i * nkeys + j];
             ws.tile_prefix[(int64_t)i * nkeys + j] = run;
             run += h;
         }
-        if (seg == kScanSegments - 1) ws.totals[j] = run;
+        if (seg == nseg - 1) ws.totals[j] = run;
     }
 }
 
-template <int CH, bool FROM_HIST, typename IdxT>
+template <int CH, bool FROM_HIST, bool EXPAND, typename IdxT>
 __global__ void __launch_bounds__(kLayoutThreads)
 assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispatch_layout_t out) {
     // LDS: [W][num_keys] wavefront counters, then totals[num_keys] and first[num_keys].
@@ -277,6 +308,7 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
     for (int j = tid; j < nkeys; j += nthreads) {
         if (FROM_HIST) {
             int before = 0, total = 0;
+#pragma unroll 8
             for (int i = 0; i < p.num_tiles; ++i) {
                 const int h = ws.tile_hist[(int64_t)i * nkeys + j];
                 before += i < tile ? h : 0;
@@ -299,8 +331,8 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
     const int k = lane - token_in_chunk * K;
     const int64_t wave_tok0 = (int64_t)tile * p.tokens_per_tile + (int64_t)wave * p.tokens_per_wave;
     int64_t entry[CH];
-    load_entries<CH>(topk, wave_tok0, token_in_chunk, k, p, entry);
     uint32_t err = 0;
+    load_entries<CH, EXPAND>(topk, wave_tok0, token_in_chunk, k, p, entry, err);
     PairPos pos[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) pos[c] = rank_chunk(entry[c], lane, token_in_chunk, p, counters, err);
@@ -323,19 +355,20 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
     uint32_t status = block_err;
     if (recv_rows > p.recv_capacity) status |= DISPATCH_STATUS_RECV_OVERFLOW;
     if (rank_rows > p.rank_capacity) status |= DISPATCH_STATUS_RANK_OVERFLOW;
+    // The receiver-side expand has no rank outputs (their pointers are NULL).
     if (tile == 0) {
         for (int j = tid; j < nkeys; j += nthreads) {
             if (j < E) {
                 out.expert_count[j] = totals[j];
                 out.expert_psum[j] = first[j];
-            } else {
+            } else if (out.rank_count) {
                 out.rank_count[j - E] = totals[j];
                 out.rank_psum[j - E] = first[j];
             }
         }
         if (tid == 0) {
             out.expert_psum[E] = recv_rows;
-            out.rank_psum[R] = rank_rows;
+            if (out.rank_psum) out.rank_psum[R] = rank_rows;
             *out.status = (int32_t)status;
         }
     }
@@ -353,11 +386,13 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
         const int es = e >= 0 ? first[e] + counters[e] + pos[c].expert_pos : -1;
         const int rs = r >= 0 ? first[E + r] + counters[E + r] + pos[c].rank_pos : -1;
         out.expert_slot[tok * K + k] = es;
-        out.rank_slot[tok * K + k] = rs;
         // Slots are below the totals, which fit the capacities when the
         // status is 0; the bounds are checked anyway before every store.
         if (es >= 0 && es < p.recv_capacity) out.recv_src_token_idx[es] = (int32_t)tok;
-        if (rs >= 0 && rs < p.rank_capacity) out.rank_src_token_idx[rs] = (int32_t)tok;
+        if (out.rank_slot) {
+            out.rank_slot[tok * K + k] = rs;
+            if (rs >= 0 && rs < p.rank_capacity) out.rank_src_token_idx[rs] = (int32_t)tok;
+        }
     }
 
     // Alignment pads of recv_src_token_idx (section 7.3): the slots after an
@@ -377,7 +412,7 @@ int bits_for(int n) {  // bits needed to tell apart n distinct ids
     return b;
 }
 
-template <int CH, typename IdxT>
+template <int CH, bool EXPAND, typename IdxT>
 hipError_t launch_typed(const LayoutParams& p, const TileGeometry& g, const void* topk,
                         const dispatch_layout_t& out, const Workspace& ws, hipStream_t stream) {
     const auto* idx = static_cast<const IdxT*>(topk);
@@ -387,38 +422,39 @@ hipError_t launch_typed(const LayoutParams& p, const TileGeometry& g, const void
     dispatch_layout_t oc = out;
     const size_t count_lds = (size_t)g.waves_per_tile * g.num_keys * sizeof(int);
     void* count_args[] = {&idx, &pc, &wc};
-    hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&count_kernel<CH, IdxT>), grid, block,
+    hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&count_kernel<CH, EXPAND, IdxT>), grid, block,
                                      count_args, count_lds, stream);
     if (err != hipSuccess) return err;
     const size_t assign_lds = (size_t)(g.waves_per_tile + 2) * g.num_keys * sizeof(int);
     void* assign_args[] = {&idx, &pc, &wc, &oc};
     if (!g.column_scan)
-        return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, true, IdxT>), grid, block,
+        return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, true, EXPAND, IdxT>), grid, block,
                                assign_args, assign_lds, stream);
-    void* scan_args[] = {&pc, &wc};
+    int kpb = g.num_keys < kWave ? g.num_keys : kWave;
+    void* scan_args[] = {&pc, &wc, &kpb};
     err = hipLaunchKernel(reinterpret_cast<const void*>(&colscan_kernel),
-                          dim3((g.num_keys + kWave - 1) / kWave), dim3(kScanSegments * kWave), scan_args, 0,
-                          stream);
+                          dim3((g.num_keys + kpb - 1) / kpb), dim3(kScanThreads), scan_args, 0, stream);
     if (err != hipSuccess) return err;
-    return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, false, IdxT>), grid, block,
+    return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, false, EXPAND, IdxT>), grid, block,
                            assign_args, assign_lds, stream);
 }
 
-template <typename IdxT>
+template <bool EXPAND, typename IdxT>
 hipError_t launch_chunks(const LayoutParams& p, const TileGeometry& g, const void* topk,
                          const dispatch_layout_t& out, const Workspace& ws, hipStream_t stream) {
     switch (g.chunks_per_wave) {
-        case 1: return launch_typed<1, IdxT>(p, g, topk, out, ws, stream);
-        case 2: return launch_typed<2, IdxT>(p, g, topk, out, ws, stream);
-        case 4: return launch_typed<4, IdxT>(p, g, topk, out, ws, stream);
-        default: return launch_typed<8, IdxT>(p, g, topk, out, ws, stream);
+        case 1: return launch_typed<1, EXPAND, IdxT>(p, g, topk, out, ws, stream);
+        case 2: return launch_typed<2, EXPAND, IdxT>(p, g, topk, out, ws, stream);
+        case 4: return launch_typed<4, EXPAND, IdxT>(p, g, topk, out, ws, stream);
+        default: return launch_typed<8, EXPAND, IdxT>(p, g, topk, out, ws, stream);
     }
 }
 
 }  // namespace
 
 hipError_t launch_layout(const dispatch_problem_t& prob, const TileGeometry& g, const void* topk_idx,
-                         const dispatch_layout_t& out, void* workspace, hipStream_t stream) {
+                         const dispatch_layout_t& out, void* workspace, hipStream_t stream,
+                         const ExpandView* expand) {
     LayoutParams p{};
     p.num_tokens = prob.num_tokens;
     p.recv_capacity = prob.recv_capacity_rows;
@@ -441,8 +477,16 @@ hipError_t launch_layout(const dispatch_problem_t& prob, const TileGeometry& g, 
     ws.tile_prefix = reinterpret_cast<int32_t*>(base + g.ws_tile_prefix);
     ws.totals = reinterpret_cast<int32_t*>(base + g.ws_totals);
     ws.tile_err = reinterpret_cast<int32_t*>(base + g.ws_tile_err);
-    if (prob.topk_idx_bytes == 8) return launch_chunks<int64_t>(p, g, topk_idx, out, ws, stream);
-    return launch_chunks<int32_t>(p, g, topk_idx, out, ws, stream);
+    if (expand != nullptr) {
+        p.recv_count = expand->recv_count;
+        p.rows_per_source = expand->rows_per_source;
+        p.first_expert = expand->first_expert;
+        p.global_experts = expand->global_experts;
+        if (prob.topk_idx_bytes == 8) return launch_chunks<true, int64_t>(p, g, topk_idx, out, ws, stream);
+        return launch_chunks<true, int32_t>(p, g, topk_idx, out, ws, stream);
+    }
+    if (prob.topk_idx_bytes == 8) return launch_chunks<false, int64_t>(p, g, topk_idx, out, ws, stream);
+    return launch_chunks<false, int32_t>(p, g, topk_idx, out, ws, stream);
 }
 
 }  // namespace moe_dispatch

@@ -71,12 +71,15 @@ __device__ __forceinline__ void copy_token(const u32x4* __restrict__ x, const ui
     int es = -1, rs = -1;
     if (lane < K) {
         es = expert_slot[t * K + lane];
-        rs = rank_slot[t * K + lane];
+        rs = rank_slot != nullptr ? rank_slot[t * K + lane] : -1;
     }
     // Slots past the capacities never occur for a layout with status 0; they
     // are dropped here so that no store can leave the output buffers.
     if (!p.write_expert || es >= p.recv_capacity) es = -1;
     if (!p.write_rank || rs >= p.rank_capacity) rs = -1;
+    // A row with no destination (fully masked token, unused receive-buffer
+    // row) is not read at all.
+    if (__ballot(es >= 0 || rs >= 0) == 0ull) return;
     const int64_t nv = p.row_vecs;
     const u32x4* src = x + t * nv;
     {

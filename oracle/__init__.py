@@ -269,3 +269,32 @@ class Prepared:
             self.t, self.k, self.e, self.row_bytes, self.s, _ptr(self.x), _ptr(self.sf),
             _ptr(self.expert_count), _ptr(self.expert_psum), _ptr(self.expert_slot), _ptr(self.rank_slot),
             _ptr(self.rank_x), _ptr(self.rank_sf), _ptr(self.recv_x), _ptr(self.recv_sf), 1)
+
+
+def expand_scatter(lay: ExpandLayout, recv_buf: np.ndarray, recv_sf: Optional[np.ndarray] = None,
+                   zero_pad: bool = True, fill: int = 0xA5, lib=None) -> Rows:
+    """Expert-major rows of a receiver-side expand: the oracle's row copy over
+    the receive buffer seen as S*M rows (no rank-contiguous output)."""
+    if lay.status != 0:
+        raise ValueError("layout carries an error status; rows are unspecified")
+    lib = _load(lib)
+    buf = np.ascontiguousarray(recv_buf, dtype=np.uint8)
+    rows, row_bytes = buf.shape
+    k = lay.expert_slot.shape[1]
+    s = 0 if recv_sf is None else int(recv_sf.shape[1])
+    sf = None if recv_sf is None else np.ascontiguousarray(recv_sf, dtype=np.float32)
+    n = lay.num_recv_rows
+    recv_x = np.empty((n, row_bytes), dtype=np.uint8)
+    recv_x[...] = fill
+    out_sf = None
+    if s:
+        out_sf = np.empty((n, s), dtype=np.float32)
+        out_sf.view(np.uint8)[...] = fill
+    no_rank = np.full(lay.expert_slot.shape, -1, dtype=np.int32)
+    rc = lib.oracle_dispatch_scatter(
+        rows, k, lay.local_experts, row_bytes, s, _ptr(buf), _ptr(sf), _ptr(lay.expert_count),
+        _ptr(lay.expert_psum), _ptr(lay.expert_slot), _ptr(no_rank), None, None, _ptr(recv_x), _ptr(out_sf),
+        1 if zero_pad else 0)
+    if rc != 0:
+        raise ValueError(f"oracle scatter failed (code {rc})")
+    return Rows(rank_x=None, rank_sf=None, recv_x=recv_x, recv_sf=out_sf)

@@ -143,3 +143,29 @@ def test_binding_refuses_host_tensors():
     p = M.make_problem(4, 2, 8, 2, 1, row_bytes=16)
     with pytest.raises(ValueError):
         M.dispatch_layout(p, torch.zeros((4, 2), dtype=torch.int64), None, torch.zeros(256, dtype=torch.uint8))
+
+
+def test_expand_host_errors():
+    lib = M.load_library()
+    assert ctypes.sizeof(M.ExpandProblem) == 56
+    q = M.ExpandProblem(4, 100, 8, 256, 8, 3, 1, 8, 0, 0, 64, 1000)
+    size = ctypes.c_size_t(0)
+    assert lib.dispatch_expand_workspace_size(ctypes.byref(q), ctypes.byref(size)) == M.OK and size.value > 0
+    cap = ctypes.c_int64(0)
+    assert lib.dispatch_expand_max_rows(ctypes.byref(q), ctypes.byref(cap)) == M.OK
+    assert cap.value == 4 * 100 * 8 + 32 * 0
+    for field, bad in (("num_sources", 0), ("rows_per_source", -1), ("local_rank", 8), ("local_rank", -1),
+                       ("num_ranks", 3), ("num_topk", 33), ("expert_alignment", 0), ("reserved", 1)):
+        b = M.ExpandProblem(4, 100, 8, 256, 8, 3, 1, 8, 0, 0, 64, 1000)
+        setattr(b, field, bad)
+        assert lib.dispatch_expand_workspace_size(ctypes.byref(b), ctypes.byref(size)) == M.ERR_ARG, field
+    expand_only = M.LayoutPtrs(4096, None, 4096, None, 4096, None, 4096, None, 4096)
+    call = lambda lay, topk, counts, ws: lib.dispatch_expand_layout(  # noqa: E731
+        ctypes.byref(q), topk, counts, ctypes.byref(lay), ws, 1 << 20, None)
+    assert call(expand_only, 4096, None, 4096) == M.ERR_NULL            # recv_count required
+    assert call(expand_only, None, 4096, 4096) == M.ERR_NULL            # table required when S*M > 0
+    assert call(M.LayoutPtrs(*([4096] * 9)), 4096, 4096, 4096) == M.ERR_ARG  # rank outputs must be NULL
+    assert call(expand_only, 4100, 4096, 4096) == M.ERR_ALIGN
+    assert call(expand_only, 4096, 4096, None) == M.ERR_WORKSPACE
+    assert lib.dispatch_expand_scatter(ctypes.byref(q), ctypes.byref(M.LayoutPtrs(*([4096] * 9))),
+                                       4096, None, 4096, None, None) == M.ERR_ARG

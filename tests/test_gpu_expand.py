@@ -1,0 +1,204 @@
+"""GPU parity of the receiver-side expand (the page's copy epilogue) against the
+CPU oracle, bit for bit, through the C ABI.
+
+Receive buffers are assembled on the host from seeded source batches: source
+s's rows for receiver r are its tokens routed to at least one of r's experts,
+in token order, placed at rows [s*M, s*M + count) of a fixed-stride buffer;
+the rest of every region holds junk that must never be read.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import moe_token_dispatch_amd as M
+import oracle
+import workloads as W
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _banner(msg):
+    print(f"\n[gpu-expand] {msg}", flush=True)
+
+
+def _source(seed, t, hidden, dtype, with_sf, e, r, k, mask):
+    w = W.Workload(f"src{seed}", t, hidden, dtype, with_sf, e, r, k, mask_frac=mask, seed=seed)
+    inp = W.make_inputs(w)
+    return w, inp
+
+
+def _receive_buffer(sources, e, r, rank, slack, seed):
+    """Host-side plumbing: gather each source's rows for `rank` into a fixed-stride buffer."""
+    epr = e // r
+    picks = []
+    for w, inp in sources:
+        topk = inp.topk_idx
+        mine = ((topk >= rank * epr) & (topk < (rank + 1) * epr)).any(axis=1)
+        picks.append(np.nonzero(mine)[0])
+    m = max(len(p) for p in picks) + slack
+    s_count = len(sources)
+    k = sources[0][1].topk_idx.shape[1]
+    row_bytes = sources[0][0].row_bytes
+    sfw = sources[0][0].sf_per_token
+    rng = np.random.default_rng([seed, 31])
+    recv_topk = rng.integers(-3, e + 5, size=(s_count * m, k)).astype(np.int64)  # junk
+    recv_buf = rng.integers(0, 256, size=(s_count * m, row_bytes), dtype=np.uint8)
+    recv_sf = rng.uniform(-9, 9, size=(s_count * m, sfw)).astype(np.float32) if sfw else None
+    counts = np.zeros(s_count, dtype=np.int32)
+    for s, ((w, inp), pick) in enumerate(zip(sources, picks)):
+        n = len(pick)
+        counts[s] = n
+        recv_topk[s * m:s * m + n] = inp.topk_idx[pick]
+        recv_buf[s * m:s * m + n] = inp.x_bytes()[pick]
+        if sfw:
+            recv_sf[s * m:s * m + n] = inp.x_sf[pick]
+    return recv_topk, recv_buf, recv_sf, counts, m
+
+
+def _run_expand(recv_topk, recv_buf, recv_sf, counts, m, e, r, rank, a, topk_bytes=8, capacity=None):
+    s_count, k = len(counts), recv_topk.shape[1]
+    q = M.make_expand_problem(s_count, m, k, e, r, rank, a, topk_bytes, recv_buf.shape[1],
+                              0 if recv_sf is None else recv_sf.shape[1], capacity)
+    lay = M.alloc_expand_layout(q, H.DEVICE)
+    for f in dataclasses.fields(lay):
+        getattr(lay, f.name).fill_(H.CANARY)
+    ws = M.alloc_expand_workspace(q, H.DEVICE)
+    cap = max(q.recv_capacity_rows, 1)
+    recv_x = torch.full((cap, recv_buf.shape[1]), H.ROW_FILL, dtype=torch.uint8, device=H.DEVICE)
+    sfw = 0 if recv_sf is None else recv_sf.shape[1]
+    recv_sf_out = None
+    if sfw:
+        recv_sf_out = torch.empty((cap, sfw), dtype=torch.float32, device=H.DEVICE)
+        recv_sf_out.view(torch.uint8).fill_(H.ROW_FILL)
+    dt = np.int64 if topk_bytes == 8 else np.int32
+    topk_d = torch.from_numpy(recv_topk.astype(dt)).to(H.DEVICE)
+    counts_d = torch.from_numpy(counts.astype(np.int32)).to(H.DEVICE)
+    buf_d = torch.from_numpy(recv_buf).to(H.DEVICE)
+    sf_d = None if recv_sf is None else torch.from_numpy(recv_sf).to(H.DEVICE)
+    M.dispatch_expand_layout(q, topk_d, counts_d, lay, ws)
+    M.dispatch_expand_scatter(q, lay, buf_d, sf_d, recv_x, recv_sf_out)
+    torch.cuda.synchronize()
+    return q, lay, recv_x, recv_sf_out
+
+
+def _compare(lay, recv_x, recv_sf_out, ref, recv_buf, recv_sf):
+    assert int(lay.status.item()) == ref.status, (int(lay.status.item()), ref.status)
+    assert np.array_equal(lay.expert_count.cpu().numpy(), ref.expert_count)
+    assert np.array_equal(lay.expert_psum.cpu().numpy(), ref.expert_psum)
+    if ref.status != 0:
+        return
+    p = ref.num_recv_rows
+    assert np.array_equal(lay.expert_slot.cpu().numpy(), ref.expert_slot)
+    src = lay.recv_src_row_idx.cpu().numpy()
+    assert np.array_equal(src[:p], ref.recv_src_row_idx[:p])
+    assert np.all(src[p:] == H.CANARY), "recv_src_row_idx written past the total"
+    want = oracle.expand_scatter(ref, recv_buf, recv_sf, fill=H.ROW_FILL)
+    got = recv_x.cpu().numpy()
+    assert np.array_equal(got[:p], want.recv_x), "expert-major rows differ from the oracle"
+    assert np.all(got[p:] == H.ROW_FILL), "rows written past the total"
+    if recv_sf is not None:
+        gs = recv_sf_out.view(torch.uint8).cpu().numpy()
+        assert np.array_equal(gs[:p], want.recv_sf.view(np.uint8))
+        assert np.all(gs[p:] == H.ROW_FILL)
+
+
+@pytest.mark.parametrize("s_count,a,dtype,with_sf,rank", [
+    (1, 1, "bf16", False, 0), (3, 1, "bf16", False, 5), (4, 128, "fp8", True, 2), (8, 16, "fp8", True, 7)])
+def test_expand_multi_source(s_count, a, dtype, with_sf, rank):
+    _banner(f"S={s_count} A={a} {dtype}{'+sf' if with_sf else ''} rank={rank}")
+    e, r, k = 256, 8, 8
+    sources = [_source(100 + s, 700 + 37 * s, 1024, dtype, with_sf, e, r, k, 0.05) for s in range(s_count)]
+    recv_topk, recv_buf, recv_sf, counts, m = _receive_buffer(sources, e, r, rank, slack=13, seed=s_count)
+    ref = oracle.expand_layout(recv_topk, counts, s_count, m, e, r, rank, a)
+    _, lay, recv_x, recv_sf_out = _run_expand(recv_topk, recv_buf, recv_sf, counts, m, e, r, rank, a)
+    _compare(lay, recv_x, recv_sf_out, ref, recv_buf, recv_sf)
+
+
+def test_expand_int32_table_and_skewed_routing():
+    e, r, k = 128, 16, 8
+    sources = []
+    for s in range(3):
+        w = W.Workload(f"z{s}", 900, 512, "bf16", False, e, r, k, routing=W.ROUTING_ZIPF, mask_frac=0.02, seed=40 + s)
+        sources.append((w, W.make_inputs(w)))
+    recv_topk, recv_buf, recv_sf, counts, m = _receive_buffer(sources, e, r, 3, slack=0, seed=9)
+    ref = oracle.expand_layout(recv_topk, counts, 3, m, e, r, 3, 4)
+    _, lay, recv_x, recv_sf_out = _run_expand(recv_topk, recv_buf, recv_sf, counts, m, e, r, 3, 4, topk_bytes=4)
+    _compare(lay, recv_x, recv_sf_out, ref, recv_buf, recv_sf)
+
+
+def test_expand_end_to_end_single_source_matches_sender():
+    """Device-only pipeline: the sender's rank-contiguous rows feed each
+    receiver's expand; the receivers' expert-major buffers, side by side, are
+    the sender's own expert-major buffer (one source), and every receiver
+    matches the oracle."""
+    w = dataclasses.replace(W.get("dsv3_fp8_a128"), num_tokens=1800)
+    _banner("end-to-end " + w.describe())
+    inp = W.make_inputs(w)
+    xb = inp.x_bytes()
+    e, r, a = w.num_experts, w.num_ranks, w.alignment
+    send = H.run_gpu(inp.topk_idx, e, r, a, xb, inp.x_sf)
+    ref_send = oracle.layout(inp.topk_idx, e, r, a)
+    H.assert_layout_equal(send, ref_send)
+    rank_psum = send.layout.rank_psum.cpu().numpy()
+    rank_src = send.layout.rank_src_token_idx
+    topk_d = torch.from_numpy(inp.topk_idx).to(H.DEVICE)
+    epr = e // r
+    for rank in range(r):
+        lo, hi = int(rank_psum[rank]), int(rank_psum[rank + 1])
+        m = hi - lo
+        q = M.make_expand_problem(1, m, w.num_topk, e, r, rank, a, 8, w.row_bytes, w.sf_per_token)
+        lay = M.alloc_expand_layout(q, H.DEVICE)
+        ws = M.alloc_expand_workspace(q, H.DEVICE)
+        cap = max(q.recv_capacity_rows, 1)
+        recv_x = torch.empty((cap, w.row_bytes), dtype=torch.uint8, device=H.DEVICE)
+        recv_sf = torch.empty((cap, w.sf_per_token), dtype=torch.float32, device=H.DEVICE)
+        counts = torch.tensor([m], dtype=torch.int32, device=H.DEVICE)
+        recv_topk = topk_d.index_select(0, rank_src[lo:hi].long()).contiguous()
+        M.dispatch_expand_layout(q, recv_topk, counts, lay, ws)
+        M.dispatch_expand_scatter(q, lay, send.rows.rank_x[lo:hi].contiguous(), send.rows.rank_sf[lo:hi].contiguous(),
+                                  recv_x, recv_sf)
+        torch.cuda.synchronize()
+        assert int(lay.status.item()) == 0
+        base = int(ref_send.expert_psum[rank * epr])
+        p = int(lay.expert_psum[-1].item())
+        assert p == int(ref_send.expert_psum[(rank + 1) * epr]) - base
+        assert torch.equal(recv_x[:p], send.rows.recv_x[base:base + p]), rank
+        assert torch.equal(recv_sf[:p].view(torch.int32), send.rows.recv_sf[base:base + p].view(torch.int32)), rank
+
+
+def test_expand_status_bad_count_and_bad_expert():
+    e, r, k = 32, 4, 4
+    sources = [_source(60 + s, 200, 256, "bf16", False, e, r, k, 0.0) for s in range(2)]
+    recv_topk, recv_buf, recv_sf, counts, m = _receive_buffer(sources, e, r, 1, slack=3, seed=60)
+    bad_counts = counts.copy()
+    bad_counts[1] = m + 1
+    ref = oracle.expand_layout(recv_topk, bad_counts, 2, m, e, r, 1, 1)
+    # the overlong count also makes the region's unused junk rows live, whose
+    # ids past E add the bad-expert bit; the GPU must report the same bits
+    assert ref.status & oracle.BAD_COUNT
+    _, lay, recv_x, _ = _run_expand(recv_topk, recv_buf, recv_sf, bad_counts, m, e, r, 1, 1)
+    _compare(lay, recv_x, None, ref, recv_buf, recv_sf)
+    assert np.all(recv_x.cpu().numpy() == H.ROW_FILL)
+    bad = recv_topk.copy()
+    bad[2, 1] = e
+    ref = oracle.expand_layout(bad, counts, 2, m, e, r, 1, 1)
+    assert ref.status == oracle.BAD_EXPERT
+    _, lay, recv_x, _ = _run_expand(bad, recv_buf, recv_sf, counts, m, e, r, 1, 1)
+    _compare(lay, recv_x, None, ref, recv_buf, recv_sf)
+
+
+@pytest.mark.parametrize("m,counts", [(0, [0, 0]), (5, [0, 0]), (5, [5, 0])])
+def test_expand_empty_and_partial(m, counts):
+    e, r, k = 16, 2, 2
+    rng = np.random.default_rng(5)
+    recv_topk = rng.integers(0, e, size=(2 * m, k)).astype(np.int64)
+    recv_topk[:, 1] = (recv_topk[:, 0] + 1) % e
+    recv_buf = rng.integers(0, 256, size=(2 * m, 32), dtype=np.uint8)
+    c = np.array(counts, dtype=np.int32)
+    ref = oracle.expand_layout(recv_topk, c, 2, m, e, r, 0, 4)
+    _, lay, recv_x, _ = _run_expand(recv_topk, recv_buf, None, c, m, e, r, 0, 4)
+    _compare(lay, recv_x, None, ref, recv_buf, None)
