@@ -55,6 +55,8 @@ def load_library(path: str):
     lib.oracle_dispatch_scatter.restype = ctypes.c_int
     lib.oracle_expand_layout.argtypes = [i32, i32, i32, i32, i32, i32, i32, p, p, i64, p, p, p, p]
     lib.oracle_expand_layout.restype = ctypes.c_int
+    lib.oracle_combine.argtypes = [i64, i32, i64, i64, p, p, p, p]
+    lib.oracle_combine.restype = ctypes.c_int
     return lib
 
 
@@ -298,3 +300,22 @@ def expand_scatter(lay: ExpandLayout, recv_buf: np.ndarray, recv_sf: Optional[np
     if rc != 0:
         raise ValueError(f"oracle scatter failed (code {rc})")
     return Rows(rank_x=None, rank_sf=None, recv_x=recv_x, recv_sf=out_sf)
+
+
+def combine(y_bits: np.ndarray, weights: np.ndarray, expert_slot: np.ndarray, lib=None) -> np.ndarray:
+    """out[t] = sum_k weights[t, k] * y[expert_slot[t, k]] in double precision.
+
+    y_bits: uint16 [rows, H] bf16 bit patterns; weights: float32 [T, K];
+    expert_slot: int32 [T, K] (-1 = no contribution). Returns float64 [T, H].
+    """
+    lib = _load(lib)
+    y = np.ascontiguousarray(y_bits, dtype=np.uint16)
+    w = np.ascontiguousarray(weights, dtype=np.float32)
+    slots = np.ascontiguousarray(expert_slot, dtype=np.int32)
+    t, k = slots.shape
+    rows, hidden = y.shape
+    out = np.empty((t, hidden), dtype=np.float64)
+    rc = lib.oracle_combine(t, k, hidden, rows, _ptr(y), _ptr(w), _ptr(slots), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle combine rejected the arguments (code {rc})")
+    return out

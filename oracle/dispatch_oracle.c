@@ -16,6 +16,14 @@
 #include <stdlib.h>
 #include <string.h>
 
+/* The value of a bfloat16 bit pattern: the upper half of an IEEE binary32. */
+static double bf16_value(uint16_t bits) {
+    const uint32_t word = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &word, sizeof f);
+    return (double)f;
+}
+
 /* ceil(c / a) * a, the page's math::align (section 7.2); align(0, a) = 0 and
  * an alignment of 1 leaves the count unchanged. */
 static int64_t align_up(int64_t c, int64_t a) {
@@ -251,5 +259,23 @@ int oracle_expand_layout(int32_t num_sources, int32_t rows_per_source, int32_t n
         }
     }
     free(cursor);
+    return 0;
+}
+
+int oracle_combine(int64_t num_tokens, int32_t num_topk, int64_t hidden, int64_t rows,
+                   const uint16_t* y, const float* weights, const int32_t* expert_slot, double* out) {
+    if (num_tokens < 0 || num_topk < 1 || hidden < 0 || rows < 0) return ORACLE_BAD_ARGS;
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        double* o = out + t * hidden;
+        for (int64_t h = 0; h < hidden; ++h) o[h] = 0.0;
+        for (int32_t k = 0; k < num_topk; ++k) {
+            const int64_t slot = expert_slot[t * num_topk + k];
+            if (slot < 0) continue;
+            if (slot >= rows) return ORACLE_BAD_ARGS;
+            const double w = (double)weights[t * num_topk + k];
+            const uint16_t* row = y + slot * hidden;
+            for (int64_t h = 0; h < hidden; ++h) o[h] += w * bf16_value(row[h]);
+        }
+    }
     return 0;
 }

@@ -80,6 +80,15 @@ int oracle_expand_layout(int32_t num_sources, int32_t rows_per_source, int32_t n
                          int32_t* expert_count, int32_t* expert_psum, int32_t* expert_slot,
                          int32_t* recv_src_row_idx);
 
+/* Combine, the reverse of the expert-major scatter: out[t, h] = sum over the
+ * token's routed k of weight[t, k] * y[expert_slot[t, k], h]. y is bf16
+ * [rows, H] (raw 16-bit patterns), weights fp32 [T, K]; the sum is taken in
+ * double precision (exact up to double rounding) and written as double
+ * [T, H]. Entries with expert_slot < 0 contribute nothing. Returns -1 for a
+ * slot >= rows. */
+int oracle_combine(int64_t num_tokens, int32_t num_topk, int64_t hidden, int64_t rows,
+                   const uint16_t* y, const float* weights, const int32_t* expert_slot, double* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -152,3 +152,32 @@ def test_expand_mutant_is_caught(tmp_path, name):
             caught = True
             break
     assert caught, f"pins did not catch mutant {name}"
+
+
+COMBINE_MUTANTS = {
+    "combine_ignores_weight": ("const double w = (double)weights[t * num_topk + k];", "const double w = 1.0;", 1),
+    "combine_skips_first_k": ("        for (int32_t k = 0; k < num_topk; ++k) {\n            const int64_t slot = expert_slot[t * num_topk + k];",
+                              "        for (int32_t k = 1; k < num_topk; ++k) {\n            const int64_t slot = expert_slot[t * num_topk + k];", 1),
+    "combine_float_accumulate": ("o[h] += w * bf16_value(row[h]);", "o[h] = (float)(o[h] + (float)w * (float)bf16_value(row[h]));", 1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(COMBINE_MUTANTS))
+def test_combine_mutant_is_caught(tmp_path, name):
+    from tests import test_oracle_pins as P
+
+    lib = _mutant_lib(tmp_path, name, *COMBINE_MUTANTS[name])
+    caught = False
+    for seed in range(3):
+        topk, lay, y, wts = P._combine_case(seed)
+        got = oracle.combine(y, wts, lay.expert_slot, lib=lib)
+        yv = P._bf16_bits_to_f64(y)
+        slots = lay.expert_slot
+        want = np.zeros((slots.shape[0], y.shape[1]))
+        for kk in range(slots.shape[1]):
+            valid = slots[:, kk] >= 0
+            want[valid] += wts[valid, kk].astype(np.float64)[:, None] * yv[slots[valid, kk]]
+        if not np.allclose(got, want, rtol=1e-13, atol=1e-300):
+            caught = True
+            break
+    assert caught, f"pins did not catch mutant {name}"

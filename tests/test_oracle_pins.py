@@ -314,3 +314,75 @@ def test_expand_status_bits():
     junk = recv_topk.copy()
     junk[1] = [99, 99]
     assert oracle.expand_layout(junk, np.array([1, 2], np.int32), 2, 2, 4, 2, 0, 1).status == 0
+
+
+# ---------------------------------------------------------------- combine
+
+
+def _bf16_bits_to_f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _combine_case(seed, t=64, k=6, e=32, h=40, mask=0.2):
+    rng = np.random.default_rng([93, seed])
+    topk = _random_topk(rng, t, k, e, mask=mask)
+    lay = oracle.layout(topk, e, 4, 3)
+    rows = lay.num_recv_rows
+    y = rng.integers(0, 1 << 16, size=(rows, h), dtype=np.uint16)
+    y[(y & 0x7F80) == 0x7F80] = 0x3F80  # no inf / nan patterns
+    wts = rng.uniform(0.0, 1.0, size=(t, k)).astype(np.float32)
+    return topk, lay, y, wts
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_combine_matches_numpy_gather_sum(seed):
+    topk, lay, y, wts = _combine_case(seed)
+    got = oracle.combine(y, wts, lay.expert_slot)
+    yv = _bf16_bits_to_f64(y)
+    slots = lay.expert_slot
+    want = np.zeros((slots.shape[0], y.shape[1]))
+    for kk in range(slots.shape[1]):
+        valid = slots[:, kk] >= 0
+        want[valid] += wts[valid, kk].astype(np.float64)[:, None] * yv[slots[valid, kk]]
+    assert np.allclose(got, want, rtol=1e-13, atol=1e-300)
+
+
+def test_combine_one_hot_weights_give_rows_exactly():
+    topk, lay, y, wts = _combine_case(7)
+    slots = lay.expert_slot
+    one_hot = np.zeros_like(wts)
+    first_valid = np.argmax(slots >= 0, axis=1)
+    has = (slots >= 0).any(axis=1)
+    one_hot[np.arange(len(wts))[has], first_valid[has]] = 1.0
+    got = oracle.combine(y, one_hot, slots)
+    yv = _bf16_bits_to_f64(y)
+    for t in range(len(wts)):
+        want = yv[slots[t, first_valid[t]]] if has[t] else np.zeros(y.shape[1])
+        assert np.array_equal(got[t], want)
+
+
+def test_combine_linearity_masking_and_order():
+    topk, lay, y, wts = _combine_case(8)
+    slots = lay.expert_slot
+    base = oracle.combine(y, wts, slots)
+    assert np.array_equal(oracle.combine(y, wts * 2, slots), base * 2)  # exact in binary
+    assert not oracle.combine(y, wts, np.full_like(slots, -1)).any()
+    perm = np.random.default_rng(1).permutation(slots.shape[1])
+    assert np.allclose(oracle.combine(y, wts[:, perm], slots[:, perm]), base, rtol=1e-13, atol=1e-300)
+
+
+def test_combine_of_scatter_is_weighted_identity():
+    """Expert outputs equal to the dispatched rows (identity experts): combine
+    brings every token back as x[t] times the sum of its routed weights."""
+    w = W.Workload("id", 120, 64, "bf16", False, 32, 4, 4, mask_frac=0.1, alignment=8, seed=13)
+    inp = W.make_inputs(w)
+    lay = oracle.layout(inp.topk_idx, 32, 4, 8)
+    rows = oracle.scatter(lay, inp.x_bytes())
+    y = rows.recv_x.view(np.uint16)
+    wts = W.make_topk_weights(w, inp.topk_idx)
+    got = oracle.combine(y, wts, lay.expert_slot)
+    x = _bf16_bits_to_f64(inp.x_bytes().view(np.uint16))
+    scale = np.where(inp.topk_idx >= 0, wts.astype(np.float64), 0).sum(axis=1, keepdims=True)
+    assert np.allclose(got, x * scale, rtol=1e-12, atol=1e-300)
+    live = (inp.topk_idx >= 0).any(axis=1)
+    assert np.allclose(scale[live], 1.0, atol=1e-6)

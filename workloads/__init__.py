@@ -12,7 +12,8 @@ fp8 e4m3 with one fp32 scale factor per 128 channels.
 
 Random streams: ``numpy.random.default_rng([seed, stream])`` (PCG64) with
 stream 0 = routing noise, 1 = mask positions, 2 = x, 3 = scale factors,
-4 = Zipf expert permutation, 5 = rank-locality choices.
+4 = Zipf expert permutation, 5 = rank-locality choices, 6 = top-k weights,
+7 = expert outputs (for combine).
 """
 
 from __future__ import annotations
@@ -27,7 +28,8 @@ ROUTING_ZIPF = "zipf"            # K distinct experts, Plackett-Luce with Zipf w
 ROUTING_RANK_LOCAL = "ranklocal"  # half uniform, half confined to 2 ranks per token
 ROUTING_SINGLE = "single"        # every token picks expert 0..K-1 (all load on few experts)
 
-_STREAM_ROUTING, _STREAM_MASK, _STREAM_X, _STREAM_SF, _STREAM_PERM, _STREAM_LOCAL = range(6)
+_STREAM_ROUTING, _STREAM_MASK, _STREAM_X, _STREAM_SF, _STREAM_PERM, _STREAM_LOCAL, _STREAM_WEIGHTS, \
+    _STREAM_EXPERT_OUT = range(8)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -185,3 +187,25 @@ def make_inputs(w: Workload, with_x: bool = True) -> Inputs:
 
 def get(name: str) -> Workload:
     return WORKLOADS[name]
+
+
+def make_topk_weights(w: Workload, topk_idx: np.ndarray) -> np.ndarray:
+    """Gate weights [T, K] fp32: positive, uniform in [0.1, 1], normalised (in
+    float64) over each token's routed entries; masked entries get 0."""
+    rng = _rng(w.seed, _STREAM_WEIGHTS)
+    raw = rng.uniform(0.1, 1.0, size=topk_idx.shape)
+    raw = np.where(topk_idx >= 0, raw, 0.0)
+    tot = raw.sum(axis=1, keepdims=True)
+    return (raw / np.where(tot > 0, tot, 1.0)).astype(np.float32)
+
+
+def make_expert_out(w: Workload, rows: int):
+    """Expert outputs [rows, H] as a CPU bf16 tensor, N(0,1) cast with RNE."""
+    import torch
+
+    rng = _rng(w.seed, _STREAM_EXPERT_OUT)
+    y = torch.empty((rows, w.hidden), dtype=torch.bfloat16)
+    for lo in range(0, rows, 4096):
+        hi = min(rows, lo + 4096)
+        y[lo:hi] = torch.from_numpy(rng.standard_normal((hi - lo, w.hidden), dtype=np.float32)).to(torch.bfloat16)
+    return y
