@@ -50,6 +50,8 @@ def parse_args():
     ap.add_argument("--expand", action="store_true",
                     help="measure the receiver-side expand instead: S sources of the workload send to rank 0")
     ap.add_argument("--sources", type=int, default=8, help="sources for --expand")
+    ap.add_argument("--combine", action="store_true",
+                    help="measure the combine instead: weighted gather of the expert-major rows back to tokens")
     return ap.parse_args()
 
 
@@ -236,6 +238,65 @@ def expand_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def combine_bench(args):
+    """Combine: out[t] = sum_k w[t, k] * y[expert_slot[t, k]] over the workload's
+    layout, with y a bf16 expert-output buffer of the expert-major rows."""
+    import numpy as np
+    import torch
+
+    import moe_token_dispatch_amd as M
+    import workloads as W
+
+    dev = "cuda:0"
+    w = W.get(args.workload or W.METRIC_WORKLOAD)
+    if w.dtype != "bf16":
+        raise SystemExit("--combine needs a bf16 workload (expert outputs are bf16)")
+    t, k = w.num_tokens, w.num_topk
+    inp = W.make_inputs(w, with_x=False)
+    prob = M.make_problem(t, k, w.num_experts, w.num_ranks, w.alignment, 8, w.row_bytes, 0,
+                          flags=M.EXPERT_MAJOR)
+    lay, ws = M.alloc_layout(prob, dev), M.alloc_workspace(prob, dev)
+    M.dispatch_layout(prob, torch.from_numpy(inp.topk_idx).to(dev), lay, ws)
+    torch.cuda.synchronize()
+    if int(lay.status.item()) != 0:
+        raise RuntimeError(f"layout status {int(lay.status.item())}")
+    p_rows = int(lay.expert_psum[-1].item())
+    y = W.make_expert_out(w, max(p_rows, 1)).to(dev)
+    wts = torch.from_numpy(W.make_topk_weights(w, inp.topk_idx)).to(dev)
+    slots = lay.expert_slot.view(t, k)
+    out = torch.empty((t, w.hidden), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    lib = M.load_library()
+    import ctypes
+    q = M.CombineProblem(t, k, 0, w.hidden, y.shape[0])
+    argv = (ctypes.byref(q), ctypes.c_void_p(slots.data_ptr()), ctypes.c_void_p(wts.data_ptr()),
+            ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(args.warmup):
+        lib.dispatch_combine(*argv)
+    torch.cuda.synchronize()
+    rc = 0
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        rc |= lib.dispatch_combine(*argv)
+    torch.cuda.synchronize()
+    if rc:
+        raise RuntimeError(f"dispatch_combine returned {rc}")
+    dt = (time.perf_counter() - t0) / args.steps
+    pairs = int((inp.topk_idx >= 0).sum())
+    total_b = t * k * 8 + pairs * w.row_bytes + t * w.row_bytes
+    res = {
+        "metric": "combine GB/s & % HBM peak",
+        "value": round(total_b / dt / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"combine of {w.name}", "num_tokens": t, "hidden": w.hidden, "num_topk": k,
+                   "routed_pairs": pairs, "expert_major_rows": p_rows},
+        "hbm_frac": round(total_b / dt / 1e9 / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": total_b,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -247,6 +308,9 @@ def main():
         return
     if args.expand:
         expand_bench(args)
+        return
+    if args.combine:
+        combine_bench(args)
         return
 
     import numpy as np

@@ -196,6 +196,29 @@ int dispatch_expand_scatter(const dispatch_expand_problem_t* problem, const disp
                             const void* recv_buf, const float* recv_sf_buf, void* recv_x, float* recv_sf,
                             hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Combine: the reverse of the expert-major scatter, reusing the layout's slot
+ * map (the page keeps it for the combine kernel, section 6.2):
+ *   out[t, :] = sum over k with expert_slot[t, k] >= 0 of
+ *               topk_weights[t, k] * y[expert_slot[t, k], :]
+ * y and out are bf16; the sum is taken in fp32 with one fused multiply-add
+ * per routed k in ascending k order from 0, then rounded to bf16 to nearest,
+ * ties to even. A token with no routed entry gets a zero row.
+ * ------------------------------------------------------------------------- */
+typedef struct dispatch_combine_problem {
+    int64_t num_tokens;   /* T >= 0 */
+    int32_t num_topk;     /* K, 1..DISPATCH_MAX_TOPK */
+    uint32_t reserved;    /* must be 0 */
+    int64_t hidden;       /* H: bf16 elements per row, multiple of 8, 8..2^30-8 */
+    int64_t expert_rows;  /* rows of y; every slot must be below it (others are dropped) */
+} dispatch_combine_problem_t;
+
+/* expert_slot: device int32 [T, K] (from dispatch_layout); topk_weights:
+ * device fp32 [T, K]; y: device bf16 [expert_rows, H], 16-byte aligned;
+ * out: device bf16 [T, H], 16-byte aligned. */
+int dispatch_combine(const dispatch_combine_problem_t* problem, const int32_t* expert_slot,
+                     const float* topk_weights, const void* y, void* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

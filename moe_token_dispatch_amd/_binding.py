@@ -93,13 +93,25 @@ class ExpandProblem(ctypes.Structure):
     ]
 
 
+class CombineProblem(ctypes.Structure):
+    """dispatch_combine_problem_t."""
+
+    _fields_ = [
+        ("num_tokens", ctypes.c_int64),
+        ("num_topk", ctypes.c_int32),
+        ("reserved", ctypes.c_uint32),
+        ("hidden", ctypes.c_int64),
+        ("expert_rows", ctypes.c_int64),
+    ]
+
+
 _LIB = None
 
 # Exported symbols of include/moe_dispatch.h.
 SYMBOLS = ("dispatch_abi_version", "dispatch_strerror", "dispatch_workspace_size",
            "dispatch_max_rows", "dispatch_layout", "dispatch_scatter",
            "dispatch_expand_workspace_size", "dispatch_expand_max_rows", "dispatch_expand_layout",
-           "dispatch_expand_scatter")
+           "dispatch_expand_scatter", "dispatch_combine")
 
 
 def load_library(path: str = LIB_PATH):
@@ -133,6 +145,8 @@ def load_library(path: str = LIB_PATH):
     lib.dispatch_expand_layout.restype = i
     lib.dispatch_expand_scatter.argtypes = [ep, ctypes.POINTER(LayoutPtrs), p, p, p, p, p]
     lib.dispatch_expand_scatter.restype = i
+    lib.dispatch_combine.argtypes = [ctypes.POINTER(CombineProblem), p, p, p, p, p]
+    lib.dispatch_combine.restype = i
     if lib.dispatch_abi_version() != ABI_VERSION:
         raise ImportError(f"{path}: ABI version {lib.dispatch_abi_version()} != {ABI_VERSION}")
     _LIB = lib
@@ -445,3 +459,23 @@ def dispatch_expand_scatter(problem: ExpandProblem, layout: ExpandLayoutTensors,
                                                 _stream_handle(stream, recv_buf.device))
     if rc:
         raise DispatchError(rc, "dispatch_expand_scatter")
+
+
+# ------------------------------------------------------------------- combine
+
+
+def dispatch_combine(expert_slot: torch.Tensor, topk_weights: torch.Tensor, y: torch.Tensor,
+                     out: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Enqueue out[t] = sum_k topk_weights[t, k] * y[expert_slot[t, k]] (bf16 rows, fp32 sums)."""
+    _check_device_tensor(expert_slot, "expert_slot", torch.int32)
+    _check_device_tensor(topk_weights, "topk_weights", torch.float32)
+    _check_device_tensor(y, "y", torch.bfloat16)
+    _check_device_tensor(out, "out", torch.bfloat16)
+    t, k = expert_slot.shape
+    if topk_weights.shape != (t, k) or out.shape[0] != t or out.shape[1] != y.shape[1]:
+        raise ValueError("combine: shapes do not line up")
+    problem = CombineProblem(t, k, 0, y.shape[1], y.shape[0])
+    rc = load_library().dispatch_combine(ctypes.byref(problem), _ptr(expert_slot), _ptr(topk_weights), _ptr(y),
+                                         _ptr(out), _stream_handle(stream, y.device))
+    if rc:
+        raise DispatchError(rc, "dispatch_combine")

@@ -20,7 +20,7 @@ LIB_NAME = "libmoe_dispatch.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["dispatch_api.cpp", "dispatch_layout.hip", "dispatch_scatter.hip"]
+SOURCES = ["dispatch_api.cpp", "dispatch_layout.hip", "dispatch_scatter.hip", "dispatch_combine.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -218,4 +218,27 @@ int dispatch_expand_scatter(const dispatch_expand_problem_t* problem, const disp
     return dispatch_scatter(&p, layout, recv_buf, recv_sf_buf, nullptr, nullptr, recv_x, recv_sf, stream);
 }
 
+int dispatch_combine(const dispatch_combine_problem_t* problem, const int32_t* expert_slot,
+                     const float* topk_weights, const void* y, void* out, hipStream_t stream) {
+    if (problem == nullptr) return DISPATCH_ERR_NULL;
+    const dispatch_combine_problem_t& p = *problem;
+    if (p.num_tokens < 0 || p.num_tokens > INT32_MAX || p.num_topk < 1 || p.num_topk > DISPATCH_MAX_TOPK ||
+        p.reserved != 0 || p.expert_rows < 0)
+        return DISPATCH_ERR_ARG;
+    if (p.hidden < 8 || p.hidden > (int64_t(1) << 30) - 8) return DISPATCH_ERR_ARG;
+    if (p.hidden % 8 != 0) return DISPATCH_ERR_ALIGN;
+    if (p.num_tokens > 0 && (!expert_slot || !topk_weights || !out || (p.expert_rows > 0 && !y)))
+        return DISPATCH_ERR_NULL;
+    const void* rows[] = {y, out};
+    for (const void* q : rows)
+        if (q && !aligned_to(q, 16)) return DISPATCH_ERR_ALIGN;
+    const void* words[] = {expert_slot, topk_weights};
+    for (const void* q : words)
+        if (q && !aligned_to(q, 4)) return DISPATCH_ERR_ALIGN;
+    if (moe_dispatch::launch_combine(p.num_tokens, p.num_topk, p.hidden * 2, p.expert_rows, expert_slot,
+                                     topk_weights, y, out, stream) != hipSuccess)
+        return DISPATCH_ERR_HIP;
+    return DISPATCH_OK;
+}
+
 }  // extern "C"

@@ -169,3 +169,30 @@ def test_expand_host_errors():
     assert call(expand_only, 4096, 4096, None) == M.ERR_WORKSPACE
     assert lib.dispatch_expand_scatter(ctypes.byref(q), ctypes.byref(M.LayoutPtrs(*([4096] * 9))),
                                        4096, None, 4096, None, None) == M.ERR_ARG
+
+
+def test_combine_host_errors():
+    lib = M.load_library()
+    assert ctypes.sizeof(M.CombineProblem) == 32
+    good = dict(num_tokens=4, num_topk=8, reserved=0, hidden=7168, expert_rows=64)
+    call = lambda q, slot=4096, w=4096, y=4096, out=4096: lib.dispatch_combine(  # noqa: E731
+        ctypes.byref(q), slot, w, y, out, None)
+    for field, bad in (("num_tokens", -1), ("num_topk", 0), ("num_topk", 33), ("reserved", 1),
+                       ("hidden", 0), ("hidden", 1 << 30), ("expert_rows", -1)):
+        q = M.CombineProblem(**good)
+        setattr(q, field, bad)
+        assert call(q) == M.ERR_ARG, field
+    q = M.CombineProblem(**good)
+    q.hidden = 7164
+    assert call(q) == M.ERR_ALIGN                       # rows must be whole 16-byte vectors
+    q = M.CombineProblem(**good)
+    assert call(q, slot=None) == M.ERR_NULL
+    assert call(q, w=None) == M.ERR_NULL
+    assert call(q, y=None) == M.ERR_NULL
+    assert call(q, out=None) == M.ERR_NULL
+    assert call(q, y=4104) == M.ERR_ALIGN
+    assert call(q, out=4104) == M.ERR_ALIGN
+    assert call(q, slot=4098) == M.ERR_ALIGN
+    assert lib.dispatch_combine(None, 4096, 4096, 4096, 4096, None) == M.ERR_NULL
+    empty = M.CombineProblem(**dict(good, num_tokens=0))
+    assert call(empty, None, None, None, None) == M.OK  # nothing to do, nothing launched
