@@ -8,11 +8,14 @@
 // to fp32, one fused multiply-add per routed k in ascending k order starting
 // from 0, and the fp32 sum rounded to bf16 to nearest, ties to even.
 //
-// One wavefront per (token, row segment of up to 64 x V 16-byte vectors, i.e.
-// 8 bf16 per lane-vector) keeps its segment's sums in registers, gathers the
-// token's K expert rows (wavefront-uniform slots and weights, read once into
-// scalar registers through readlane) and writes the segment once. The kernel
-// reads about K rows per token and writes one, so it is bound by HBM reads.
+// One wavefront per (token, 1 KB row segment: one 16-byte vector of 8 bf16 per
+// lane) keeps its segment's sums in registers. It issues the loads of up to
+// eight of the token's expert rows before the first multiply-add, so a
+// wavefront has 8 KB of independent reads in flight, and writes its segment
+// once. The kernel reads about K rows per token and writes one: it is bound by
+// HBM reads. Every y row is read once per launch, so the loads are marked
+// nontemporal; the output goes out with the sc1 policy (measured best for
+// this kernel among the store policies).
 #include "dispatch_common.hpp"
 
 namespace moe_dispatch {
@@ -20,18 +23,20 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kCombineWaves = 4;
-constexpr int kCombineMaxVecs = 8;
+constexpr int kCombineWaves = 2;         // wavefronts per workgroup
+constexpr int kCombineBatch = 8;         // expert rows loaded before the multiply-adds
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
-constexpr int kStreamingPolicy = 2 | 16;  // nt | sc1
+constexpr int kOutPolicy = 16;            // sc1
+constexpr int64_t kMaxCombineBlocks = int64_t(1) << 16;  // larger grids loop
 
 struct CombineParams {
     int64_t num_tokens;
     int64_t row_vecs;      // 16-byte vectors per row (hidden / 8)
     int64_t expert_rows;   // rows of y
-    int64_t token_waves;   // num_tokens * segments, rounded up to whole workgroups
+    int64_t total_waves;   // num_tokens * segments
+    int64_t wave_stride;   // wavefronts in the grid
     int32_t num_topk;
-    int32_t segments;
+    int32_t segments;      // row segments of kWave vectors
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -44,77 +49,63 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int V>
 __global__ void __launch_bounds__(kCombineWaves * kWave)
 combine_kernel(const u32x4* __restrict__ y, const float* __restrict__ weights,
                const int32_t* __restrict__ expert_slot, CombineParams p, u32x4* __restrict__ out) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave_id = (int64_t)blockIdx.x * kCombineWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    if (wave_id >= p.num_tokens * p.segments) return;
-    const int64_t t = wave_id / p.segments;
-    const int seg = (int)(wave_id - t * p.segments);
     const int K = p.num_topk;
-    int slot = -1;
-    float w = 0.f;
-    if (lane < K) {
-        slot = expert_slot[t * K + lane];
-        w = weights[t * K + lane];
-    }
-    // A slot outside y never occurs for a layout with status 0; it is dropped.
-    if (slot >= p.expert_rows) slot = -1;
-
     const int64_t nv = p.row_vecs;
-    const int64_t base = (int64_t)seg * kWave * V;
-    float acc[V][8];
+    for (int64_t wave_id = (int64_t)blockIdx.x * kCombineWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+         wave_id < p.total_waves; wave_id += p.wave_stride) {
+        const int64_t t = wave_id / p.segments;
+        const int64_t i = (wave_id - t * p.segments) * kWave + lane;  // this lane's vector in the row
+        const bool live = i < nv;
+        float acc[8];
 #pragma unroll
-    for (int j = 0; j < V; ++j)
+        for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+        for (int k0 = 0; k0 < K; k0 += kCombineBatch) {
+            // Lane b of the batch holds entry k0 + b of the token.
+            int slot = -1;
+            float w = 0.f;
+            if (lane < kCombineBatch && k0 + lane < K) {
+                slot = expert_slot[t * K + k0 + lane];
+                w = weights[t * K + k0 + lane];
+            }
+            // A slot outside y never occurs for a layout with status 0; it is dropped.
+            if (slot >= p.expert_rows) slot = -1;
+            int s[kCombineBatch];
+            u32x4 v[kCombineBatch];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[j][q] = 0.f;
-
-    for (int k = 0; k < K; ++k) {
-        const int s = __builtin_amdgcn_readlane(slot, k);
-        if (s < 0) continue;
-        const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(w), k));
-        const u32x4* row = y + (int64_t)s * nv;
-        u32x4 v[V];
+            for (int b = 0; b < kCombineBatch; ++b) {
+                s[b] = __builtin_amdgcn_readlane(slot, b);
+                v[b] = u32x4{0u, 0u, 0u, 0u};
+                if (s[b] >= 0 && live) v[b] = __builtin_nontemporal_load(y + (int64_t)s[b] * nv + i);
+            }
 #pragma unroll
-        for (int j = 0; j < V; ++j) {
-            const int64_t i = base + j * kWave + lane;
-            v[j] = i < nv ? row[i] : u32x4{0u, 0u, 0u, 0u};
+            for (int b = 0; b < kCombineBatch; ++b) {
+                if (s[b] < 0) continue;
+                const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(w), b));
+                acc[0] = __builtin_fmaf(wk, bf16_lo(v[b].x), acc[0]);
+                acc[1] = __builtin_fmaf(wk, bf16_hi(v[b].x), acc[1]);
+                acc[2] = __builtin_fmaf(wk, bf16_lo(v[b].y), acc[2]);
+                acc[3] = __builtin_fmaf(wk, bf16_hi(v[b].y), acc[3]);
+                acc[4] = __builtin_fmaf(wk, bf16_lo(v[b].z), acc[4]);
+                acc[5] = __builtin_fmaf(wk, bf16_hi(v[b].z), acc[5]);
+                acc[6] = __builtin_fmaf(wk, bf16_lo(v[b].w), acc[6]);
+                acc[7] = __builtin_fmaf(wk, bf16_hi(v[b].w), acc[7]);
+            }
         }
-#pragma unroll
-        for (int j = 0; j < V; ++j) {
-            acc[j][0] = __builtin_fmaf(wk, bf16_lo(v[j].x), acc[j][0]);
-            acc[j][1] = __builtin_fmaf(wk, bf16_hi(v[j].x), acc[j][1]);
-            acc[j][2] = __builtin_fmaf(wk, bf16_lo(v[j].y), acc[j][2]);
-            acc[j][3] = __builtin_fmaf(wk, bf16_hi(v[j].y), acc[j][3]);
-            acc[j][4] = __builtin_fmaf(wk, bf16_lo(v[j].z), acc[j][4]);
-            acc[j][5] = __builtin_fmaf(wk, bf16_hi(v[j].z), acc[j][5]);
-            acc[j][6] = __builtin_fmaf(wk, bf16_lo(v[j].w), acc[j][6]);
-            acc[j][7] = __builtin_fmaf(wk, bf16_hi(v[j].w), acc[j][7]);
-        }
-    }
-
-    // One row per token; vectors past the row end fall outside the row's
-    // buffer range and are dropped by the hardware.
-    const __amdgpu_buffer_rsrc_t dst = __builtin_amdgcn_make_buffer_rsrc(out + t * nv, 0, (int)(nv * 16), kBufferWord3);
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
+        // One row per token; a vector past the row end falls outside the
+        // row's buffer range and is dropped by the hardware.
+        const __amdgpu_buffer_rsrc_t dst =
+            __builtin_amdgcn_make_buffer_rsrc(out + t * nv, 0, (int)(nv * 16), kBufferWord3);
         u32x4 o;
-        o.x = to_bf16(acc[j][0]) | (to_bf16(acc[j][1]) << 16);
-        o.y = to_bf16(acc[j][2]) | (to_bf16(acc[j][3]) << 16);
-        o.z = to_bf16(acc[j][4]) | (to_bf16(acc[j][5]) << 16);
-        o.w = to_bf16(acc[j][6]) | (to_bf16(acc[j][7]) << 16);
-        __builtin_amdgcn_raw_buffer_store_b128(o, dst, (int)((base + j * kWave + lane) * 16), 0, kStreamingPolicy);
+        o.x = to_bf16(acc[0]) | (to_bf16(acc[1]) << 16);
+        o.y = to_bf16(acc[2]) | (to_bf16(acc[3]) << 16);
+        o.z = to_bf16(acc[4]) | (to_bf16(acc[5]) << 16);
+        o.w = to_bf16(acc[6]) | (to_bf16(acc[7]) << 16);
+        __builtin_amdgcn_raw_buffer_store_b128(o, dst, live ? (int)(i * 16) : (int)(nv * 16), 0, kOutPolicy);
     }
-}
-
-template <int V>
-hipError_t launch_v(dim3 grid, hipStream_t stream, const u32x4* y, const float* weights, const int32_t* slots,
-                    CombineParams p, u32x4* out) {
-    void* args[] = {&y, &weights, &slots, &p, &out};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&combine_kernel<V>), grid, dim3(kCombineWaves * kWave),
-                           args, 0, stream);
 }
 
 }  // namespace
@@ -127,27 +118,17 @@ hipError_t launch_combine(int64_t num_tokens, int32_t num_topk, int64_t row_byte
     p.row_vecs = row_bytes / 16;
     p.expert_rows = expert_rows;
     p.num_topk = num_topk;
-    p.segments = (int32_t)((p.row_vecs + kWave * kCombineMaxVecs - 1) / (kWave * kCombineMaxVecs));
-    if (p.segments < 1) p.segments = 1;
-    const int64_t seg_vecs = (p.row_vecs + p.segments - 1) / p.segments;
-    const int v = (int)((seg_vecs + kWave - 1) / kWave);
-    const int64_t waves = num_tokens * p.segments;
-    p.token_waves = (waves + kCombineWaves - 1) / kCombineWaves * kCombineWaves;
-    const int64_t blocks = p.token_waves / kCombineWaves;
+    p.segments = (int32_t)((p.row_vecs + kWave - 1) / kWave);
+    p.total_waves = num_tokens * p.segments;
+    int64_t blocks = (p.total_waves + kCombineWaves - 1) / kCombineWaves;
     if (blocks == 0) return hipSuccess;
-    const dim3 grid((unsigned)blocks);
+    if (blocks > kMaxCombineBlocks) blocks = kMaxCombineBlocks;
+    p.wave_stride = blocks * kCombineWaves;
     const auto* ys = static_cast<const u32x4*>(y);
     auto* os = static_cast<u32x4*>(out);
-    switch (v) {
-        case 1: return launch_v<1>(grid, stream, ys, weights, expert_slot, p, os);
-        case 2: return launch_v<2>(grid, stream, ys, weights, expert_slot, p, os);
-        case 3: return launch_v<3>(grid, stream, ys, weights, expert_slot, p, os);
-        case 4: return launch_v<4>(grid, stream, ys, weights, expert_slot, p, os);
-        case 5: return launch_v<5>(grid, stream, ys, weights, expert_slot, p, os);
-        case 6: return launch_v<6>(grid, stream, ys, weights, expert_slot, p, os);
-        case 7: return launch_v<7>(grid, stream, ys, weights, expert_slot, p, os);
-        default: return launch_v<8>(grid, stream, ys, weights, expert_slot, p, os);
-    }
+    void* args[] = {&ys, &weights, &expert_slot, &p, &os};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&combine_kernel), dim3((unsigned)blocks),
+                           dim3(kCombineWaves * kWave), args, 0, stream);
 }
 
 }  // namespace moe_dispatch

@@ -92,12 +92,13 @@ def test_rne_helper_pins():
 
 
 @pytest.mark.parametrize("t,k,e,hidden,mask", [
-    (512, 8, 256, 7168, 0.05),    # two segments of 7 vectors per lane
-    (300, 8, 64, 4096, 0.0),      # exactly one full segment
-    (257, 6, 32, 2056, 0.1),      # ragged: 257 vectors per row
+    (512, 8, 256, 7168, 0.05),    # 14 segments of 64 vectors
+    (300, 8, 64, 4096, 0.0),      # 8 whole segments, no masking
+    (257, 6, 32, 2056, 0.1),      # ragged: 4 segments and a 1-vector tail
     (129, 4, 16, 128, 0.3),       # 16 vectors: most lanes idle
     (65, 1, 8, 8, 0.2),           # one vector per row, top-1
-    (96, 32, 64, 1024, 0.25),     # the largest top-k
+    (96, 32, 64, 1024, 0.25),
+    (100, 11, 64, 512, 0.0),      # a second batch of 3     # the largest top-k: 4 batches of 8 loads
 ])
 def test_combine_matches_oracle(t, k, e, hidden, mask):
     _banner(f"combine T={t} K={k} E={e} H={hidden} mask={mask}")
@@ -176,3 +177,12 @@ def test_combine_drops_slots_outside_y():
     got = _run_combine(slots, wts, y)
     trimmed = np.where(slots >= y.shape[0], -1, slots)
     _check(got, y.view(torch.int16).numpy().view(np.uint16), wts, trimmed)
+
+
+def test_combine_grid_loops_over_many_tokens():
+    """150000 single-segment tokens need more wavefronts than one grid holds,
+    so every wavefront takes several (token, segment) units in turn."""
+    _banner("150000 tokens, grid-stride loop")
+    w, topk, ref, y, wts = _combine_inputs(150000, 8, 64, 64, 0.05, seed=14)
+    got = _run_combine(ref.expert_slot, wts, y)
+    _check(got, y.view(torch.int16).numpy().view(np.uint16), wts, ref.expert_slot)
