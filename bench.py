@@ -33,6 +33,8 @@ METRIC = "dispatch GB/s & % HBM peak, 4096 tok×7168 bf16, top-8 of 256 experts"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scatter_traffic.json")
 SCATTER_SOURCES = [os.path.join(ROOT, "moe_token_dispatch_amd", "csrc", "dispatch_scatter.hip")]
+COMBINE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_traffic.json")
+COMBINE_SOURCES = [os.path.join(ROOT, "moe_token_dispatch_amd", "csrc", "dispatch_combine.hip")]
 
 
 def parse_args():
@@ -83,15 +85,18 @@ def source_digest(paths):
     return h.hexdigest()
 
 
-def load_traffic(launches_per_step=1):
-    """HBM bytes per scatter launch from committed rocprofv3 counters, or None
-    when they are missing or were taken on another version of the kernel."""
+def load_traffic(path=TRAFFIC_FILE, sources=SCATTER_SOURCES, workload=None):
+    """HBM bytes per launch of a kernel from committed rocprofv3 counters, or
+    None when they are missing, were taken on another workload or on another
+    version of the kernel's source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != source_digest(SCATTER_SOURCES):
+    if rec.get("source_sha256") != source_digest(sources):
+        return None
+    if workload is not None and rec.get("workload") != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -275,13 +280,18 @@ def combine_bench(args):
         lib.dispatch_combine(*argv)
     torch.cuda.synchronize()
     rc = 0
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for _ in range(args.steps):
         rc |= lib.dispatch_combine(*argv)
+    ev1.record(stream)
     torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
     if rc:
         raise RuntimeError(f"dispatch_combine returned {rc}")
-    dt = (time.perf_counter() - t0) / args.steps
+    launch_s = ev0.elapsed_time(ev1) / 1e3 / max(args.steps, 1)
     pairs = int((inp.topk_idx >= 0).sum())
     total_b = t * k * 8 + pairs * w.row_bytes + t * w.row_bytes
     res = {
@@ -293,6 +303,13 @@ def combine_bench(args):
                    "routed_pairs": pairs, "expert_major_rows": p_rows},
         "hbm_frac": round(total_b / dt / 1e9 / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": total_b,
+        "roofline": {
+            "kernel": "combine_kernel", "bound": "hbm",
+            "achieved": round(total_b / launch_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(total_b / launch_s / 1e9 / HBM_PEAK_GBPS, 4),
+            "traffic": load_traffic(COMBINE_TRAFFIC_FILE, COMBINE_SOURCES, w.name),
+            "algorithmic_bytes_per_launch": total_b, "launch_us_mean": round(launch_s * 1e6, 2),
+        },
     }
     print(json.dumps(res), flush=True)
 
@@ -381,7 +398,7 @@ def main():
     value = total_b / (wall / args.steps) / 1e9
     sc_mean_ms = statistics.mean(scatter_ms)
     achieved = sc_b / (sc_mean_ms * 1e-3) / 1e9
-    traffic = load_traffic()
+    traffic = load_traffic(workload=w.name)
 
     # Cached dispatch: the same layout replayed, scatter only (the routing is
     # unchanged, so the layout is not recomputed). Timed after, and outside,

@@ -159,3 +159,48 @@ def assert_rows_gather_property(run: GpuRun, ref: oracle.Layout, chunk: int = 81
         if run.x_sf is not None and run.rows.rank_sf is not None:
             assert torch.equal(run.rows.rank_sf[lo:hi].view(torch.int32),
                                run.x_sf.view(torch.int32).index_select(0, src))
+
+
+# ------------------------------------------------------------------ combine
+# The combine kernel widens bf16 to fp32, adds one fused multiply-add per
+# routed k (ascending k, from 0) and rounds the fp32 sum to bf16 once. With
+# A = sum_k |w_k| |y_k| and u = 2^-24, the K-term fp32 chain is within K u A of
+# the exact sum S (each FMA rounds once, to at most u times a partial sum that
+# is at most A), and the final rounding adds at most half a bf16 ulp,
+# 2^-8 |S_fp32|. The accepted bound is
+#     |gpu - S| <= 2^-8 (max(|gpu|, |S|) + (K+1) u A) + (K+1) u A + 2^-133
+# (the last term covers bf16's subnormal spacing).
+
+U = 2.0 ** -24
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_rne(v: np.ndarray) -> np.ndarray:
+    """Round float64 to bf16 bits, to nearest, ties to even, straight from the
+    fp64 significand (no intermediate fp32 rounding). Normal range only."""
+    m, e = np.frexp(v)                        # v = m * 2^e, 0.5 <= |m| < 1
+    q = np.ldexp(np.round(np.ldexp(m, 8)), e - 8)   # 8 significant bits, numpy rounds half to even
+    return (q.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def assert_combine_close(got_bits, y_bits, wts, slots, min_exact=0.99):
+    """Combine output bits against the oracle's exact sums: every output
+    within the bound above, at least `min_exact` of them equal to the exact
+    sum rounded to bf16, and +0 rows for tokens with no routed entry."""
+    s = oracle.combine(y_bits, wts, slots)
+    a = oracle.combine(y_bits & np.uint16(0x7FFF), np.abs(wts), slots)
+    k = slots.shape[1]
+    got = bf16_bits_to_f64(got_bits)
+    assert np.all(np.isfinite(got))
+    err = (k + 1) * U * a
+    bound = 2.0 ** -8 * (np.maximum(np.abs(got), np.abs(s)) + err) + err + 2.0 ** -133
+    bad = np.abs(got - s) > bound
+    assert not bad.any(), f"{int(bad.sum())} outputs outside the fp32-chain bound, first at {np.argwhere(bad)[0]}"
+    exact = got_bits == f64_to_bf16_rne(s)
+    assert exact.mean() >= min_exact, f"only {exact.mean():.5f} of outputs equal bf16(exact sum)"
+    none = (slots < 0).all(axis=1)
+    assert np.all(got_bits[none] == 0), "tokens with no routed entry must get +0 rows"
+    return exact.mean()

@@ -26,24 +26,14 @@ from tests import gpu_harness as H
 
 pytestmark = pytest.mark.gpu
 
-U = 2.0 ** -24
+U = H.U
+_bf16_bits_to_f64 = H.bf16_bits_to_f64
+_f64_to_bf16_rne = H.f64_to_bf16_rne
+_check = H.assert_combine_close
 
 
 def _banner(msg):
     print(f"\n[gpu-combine] {msg}", flush=True)
-
-
-def _bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
-    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-
-
-def _f64_to_bf16_rne(v: np.ndarray) -> np.ndarray:
-    """Round float64 to bf16 bits, to nearest, ties to even (via an exact
-    fp64 -> fp32 step only when that step is exact enough: values are rounded
-    directly from their fp64 significand)."""
-    m, e = np.frexp(v)                        # v = m * 2^e, 0.5 <= |m| < 1
-    q = np.ldexp(np.round(np.ldexp(m, 8)), e - 8)   # 8 significant bits, numpy rounds half to even
-    return (q.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
 def _combine_inputs(t, k, e, hidden, mask, seed, alignment=1):
@@ -66,29 +56,6 @@ def _run_combine(slots: np.ndarray, wts: np.ndarray, y: torch.Tensor) -> np.ndar
                        y.to(H.DEVICE), out)
     torch.cuda.synchronize()
     return out.view(torch.int16).cpu().numpy().view(np.uint16)
-
-
-def _check(got_bits, y_bits, wts, slots, min_exact=0.99):
-    s = oracle.combine(y_bits, wts, slots)
-    a = oracle.combine(y_bits & np.uint16(0x7FFF), np.abs(wts), slots)
-    k = slots.shape[1]
-    got = _bf16_bits_to_f64(got_bits)
-    assert np.all(np.isfinite(got))
-    err = (k + 1) * U * a
-    bound = 2.0 ** -8 * (np.maximum(np.abs(got), np.abs(s)) + err) + err + 2.0 ** -133
-    bad = np.abs(got - s) > bound
-    assert not bad.any(), f"{int(bad.sum())} outputs outside the fp32-chain bound, first at {np.argwhere(bad)[0]}"
-    exact = got_bits == _f64_to_bf16_rne(s)
-    assert exact.mean() >= min_exact, f"only {exact.mean():.5f} of outputs equal bf16(exact sum)"
-    none = (slots < 0).all(axis=1)
-    assert np.all(got_bits[none] == 0), "tokens with no routed entry must get +0 rows"
-    return exact.mean()
-
-
-def test_rne_helper_pins():
-    v = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.5, 1.0 + 2.0 ** -8 + 2.0 ** -30, 0.0])
-    want = np.array([0x3F80, 0x3F80, 0x3F82, 0xC020, 0x3F81, 0x0000], dtype=np.uint16)
-    assert np.array_equal(_f64_to_bf16_rne(v), want)
 
 
 @pytest.mark.parametrize("t,k,e,hidden,mask", [
