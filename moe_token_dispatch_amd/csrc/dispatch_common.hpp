@@ -21,7 +21,7 @@ constexpr int kWave = 64;             // gfx950 wavefront width
 constexpr int kLayoutThreads = 1024;  // at most 16 wavefronts per layout workgroup
 constexpr int kScanThreads = 1024;    // threads per column-scan workgroup
 constexpr int kMaxTilesTarget = 512;  // more chunks per wavefront beyond this many tiles
-constexpr int kFewTiles = 8;          // up to this many tiles, assign reduces the histograms itself
+constexpr int kFromHistMaxInts = 65536; // up to this many histogram ints, assign reduces them itself
 constexpr int kFewTileWaves = 16;     // wavefronts per tile on the few-tiles path
 constexpr int kManyTileWaves = 4;     // wavefronts per tile on the column-scan path
 constexpr int kLdsBudgetInts = 16000; // LDS ints per workgroup for key arrays, under 64 KiB
@@ -36,6 +36,7 @@ struct TileGeometry {
     int32_t tokens_per_tile;    // W * tokens_per_wave
     int32_t num_tiles;          // >= 1
     int32_t num_keys;           // E + R: expert keys first, then rank keys
+    int32_t hist_stride;        // ints per histogram row: num_keys rounded up to a multiple of 4
     bool column_scan;           // false: two kernels (count, assign); true: count, colscan, assign
     size_t ws_tile_hist;        // workspace byte offsets of the arrays below
     size_t ws_tile_prefix;
@@ -57,17 +58,25 @@ inline TileGeometry make_geometry(int64_t num_tokens, int32_t num_topk, int32_t 
     // num_keys ints in LDS.
     const int w_lds = kLdsBudgetInts / g.num_keys - 2;
     auto clamp_w = [&](int cap) { return w_lds < 1 ? 1 : (w_lds > cap ? cap : w_lds); };
-    // One chunk per wavefront keeps the ranking spread over many CUs. With
-    // few tiles of 16 wavefronts, each assign workgroup reduces the tile
-    // histograms itself (two kernels); otherwise tiles of 4 wavefronts and a
+    // Histogram rows are padded to whole 16-byte vectors.
+    g.hist_stride = (g.num_keys + 3) / 4 * 4;
+    // While the tile histograms of 16-wavefront tiles (1, 2, 4 or 8 chunks
+    // per wavefront, the fewest that fit) stay small, every assign workgroup
+    // reduces them itself: two kernels, as a launch costs a few microseconds,
+    // more than that reduction. Otherwise tiles of 4 wavefronts and a
     // column-scan kernel, with more chunks per wavefront once the tile count
     // would make the column scan long.
-    g.chunks_per_wave = 1;
     g.waves_per_tile = clamp_w(kFewTileWaves);
-    const int64_t few_tiles = (num_tokens + (int64_t)g.waves_per_tile * g.tokens_per_chunk - 1) /
-                              ((int64_t)g.waves_per_tile * g.tokens_per_chunk);
-    g.column_scan = few_tiles > kFewTiles;
+    g.column_scan = true;
+    for (g.chunks_per_wave = 1; g.chunks_per_wave <= 8; g.chunks_per_wave *= 2) {
+        const int64_t per_tile = (int64_t)g.waves_per_tile * g.chunks_per_wave * g.tokens_per_chunk;
+        if ((num_tokens + per_tile - 1) / per_tile * g.hist_stride <= kFromHistMaxInts) {
+            g.column_scan = false;
+            break;
+        }
+    }
     if (g.column_scan) {
+        g.chunks_per_wave = 1;
         g.waves_per_tile = clamp_w(kManyTileWaves);
         while (g.chunks_per_wave < 8) {
             const int64_t per_tile = (int64_t)g.waves_per_tile * g.chunks_per_wave * g.tokens_per_chunk;
@@ -79,7 +88,7 @@ inline TileGeometry make_geometry(int64_t num_tokens, int32_t num_topk, int32_t 
     g.tokens_per_tile = g.waves_per_tile * g.tokens_per_wave;
     const int64_t tiles = (num_tokens + g.tokens_per_tile - 1) / g.tokens_per_tile;
     g.num_tiles = tiles < 1 ? 1 : (int32_t)tiles;
-    const size_t table = round_up_256((size_t)g.num_tiles * (size_t)g.num_keys * sizeof(int32_t));
+    const size_t table = round_up_256((size_t)g.num_tiles * (size_t)g.hist_stride * sizeof(int32_t));
     g.ws_tile_hist = 0;
     g.ws_tile_prefix = g.ws_tile_hist + table;
     g.ws_totals = g.ws_tile_prefix + table;
@@ -88,7 +97,7 @@ inline TileGeometry make_geometry(int64_t num_tokens, int32_t num_topk, int32_t 
     return g;
 }
 
-// Workspace: tile_hist[num_tiles][num_keys], tile_prefix[num_tiles][num_keys],
+// Workspace: tile_hist[num_tiles][hist_stride], tile_prefix[num_tiles][hist_stride],
 // totals[num_keys] and tile_err[num_tiles], int32, each 256-byte aligned.
 inline size_t workspace_bytes(const TileGeometry& g) { return g.ws_bytes; }
 

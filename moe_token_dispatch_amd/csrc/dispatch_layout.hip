@@ -40,6 +40,8 @@
 namespace moe_dispatch {
 namespace {
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
 struct LayoutParams {
     int64_t num_tokens;
     int64_t recv_capacity;
@@ -55,6 +57,7 @@ struct LayoutParams {
     int32_t tokens_per_wave;
     int32_t tokens_per_tile;
     int32_t num_keys;
+    int32_t hist_stride;  // ints per histogram row (num_keys padded to a multiple of 4)
     int32_t num_tiles;
     // Receiver-side expand only: the table is a fixed-stride receive buffer
     // of rows_per_source rows per source, source s holding recv_count[s]
@@ -210,8 +213,8 @@ __device__ int block_exclusive_scan(const int* __restrict__ in, int* __restrict_
 
 // Workspace views.
 struct Workspace {
-    int32_t* tile_hist;    // [num_tiles][num_keys]
-    int32_t* tile_prefix;  // [num_tiles][num_keys] pairs of the key in earlier tiles
+    int32_t* tile_hist;    // [num_tiles][hist_stride]
+    int32_t* tile_prefix;  // [num_tiles][hist_stride] pairs of the key in earlier tiles
     int32_t* totals;       // [num_keys]
     int32_t* tile_err;     // [num_tiles] DISPATCH_STATUS_* bits seen by the tile
 };
@@ -243,11 +246,12 @@ count_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws) {
     if (lane == 0 && wave_err) atomicOr(&block_err, wave_err);
     __syncthreads();
 
-    int32_t* row = ws.tile_hist + (int64_t)blockIdx.x * nkeys;
-    for (int j = tid; j < nkeys; j += nthreads) {
+    int32_t* row = ws.tile_hist + (int64_t)blockIdx.x * p.hist_stride;
+    for (int j = tid; j < p.hist_stride; j += nthreads) {
         int s = 0;
-        for (int w = 0; w < nwaves; ++w) s += lds[w * nkeys + j];
-        row[j] = s;
+        if (j < nkeys)
+            for (int w = 0; w < nwaves; ++w) s += lds[w * nkeys + j];
+        row[j] = s;  // the row's padding holds zeros
     }
     if (tid == 0) ws.tile_err[blockIdx.x] = (int32_t)block_err;
 }
@@ -262,14 +266,22 @@ colscan_kernel(LayoutParams p, Workspace ws, int kpb) {
     const int kk = threadIdx.x % kpb, seg = threadIdx.x / kpb;
     const bool active = seg < nseg;
     const int j = blockIdx.x * kpb + kk;
-    const int nkeys = p.num_keys, n = p.num_tiles;
+    const int nkeys = p.num_keys, n = p.num_tiles, stride = p.hist_stride;
     const int per = (n + nseg - 1) / nseg;
     const int lo = active ? min(n, seg * per) : n, hi = active ? min(n, lo + per) : n;
-    // Unrolled so that several independent loads are in flight per thread.
+    // The first kColscanHeld tiles of a segment stay in registers between the
+    // two passes; all loads of a pass are independent, so they overlap.
+    constexpr int kColscanHeld = 8;
+    int held[kColscanHeld];
     int s = 0;
     if (j < nkeys) {
+#pragma unroll
+        for (int q = 0; q < kColscanHeld; ++q) {
+            held[q] = lo + q < hi ? ws.tile_hist[(int64_t)(lo + q) * stride + j] : 0;
+            s += held[q];
+        }
 #pragma unroll 8
-        for (int i = lo; i < hi; ++i) s += ws.tile_hist[(int64_t)i * nkeys + j];
+        for (int i = lo + kColscanHeld; i < hi; ++i) s += ws.tile_hist[(int64_t)i * stride + j];
     }
     if (active) seg_sum[seg * kpb + kk] = s;
     __syncthreads();
@@ -277,10 +289,17 @@ colscan_kernel(LayoutParams p, Workspace ws, int kpb) {
     int run = 0;
     for (int q = 0; q < seg; ++q) run += seg_sum[q * kpb + kk];
     if (j < nkeys) {
+#pragma unroll
+        for (int q = 0; q < kColscanHeld; ++q) {
+            if (lo + q < hi) {
+                ws.tile_prefix[(int64_t)(lo + q) * stride + j] = run;
+                run += held[q];
+            }
+        }
 #pragma unroll 8
-        for (int i = lo; i < hi; ++i) {
-            const int h = ws.tile_hist[(int64_t)i * nkeys + j];
-            ws.tile_prefix[(int64_t)i * nkeys + j] = run;
+        for (int i = lo + kColscanHeld; i < hi; ++i) {
+            const int h = ws.tile_hist[(int64_t)i * stride + j];
+            ws.tile_prefix[(int64_t)i * stride + j] = run;
             run += h;
         }
         if (seg == nseg - 1) ws.totals[j] = run;
@@ -302,37 +321,56 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
     int* counters = lds + wave * nkeys;
     int* totals = lds + nwaves * nkeys;  // per key, over all tiles
     int* first = totals + nkeys;         // per key, first slot (exclusive psum)
-    for (int i = lane; i < nkeys; i += kWave) counters[i] = 0;
-    // totals[] holds each key's pair count over all tiles; first[] holds, for
-    // now, its pairs in tiles before this one.
-    for (int j = tid; j < nkeys; j += nthreads) {
-        if (FROM_HIST) {
-            int before = 0, total = 0;
-#pragma unroll 8
-            for (int i = 0; i < p.num_tiles; ++i) {
-                const int h = ws.tile_hist[(int64_t)i * nkeys + j];
-                before += i < tile ? h : 0;
-                total += h;
-            }
-            totals[j] = total;
-            first[j] = before;
-        } else {
-            totals[j] = ws.totals[j];
-            first[j] = ws.tile_prefix[(int64_t)tile * nkeys + j];
-        }
-    }
-    if (tid == 0) block_err = 0;
-    __syncthreads();
-    uint32_t tile_errs = 0;
-    for (int i = tid; i < p.num_tiles; i += nthreads) tile_errs |= (uint32_t)ws.tile_err[i];
-    if (tile_errs) atomicOr(&block_err, tile_errs);
-
+    // The routing entries and the tiles' error words do not depend on the
+    // histograms: their loads go out first, so the three latencies overlap.
     const int token_in_chunk = lane / K;
     const int k = lane - token_in_chunk * K;
     const int64_t wave_tok0 = (int64_t)tile * p.tokens_per_tile + (int64_t)wave * p.tokens_per_wave;
     int64_t entry[CH];
     uint32_t err = 0;
     load_entries<CH, EXPAND>(topk, wave_tok0, token_in_chunk, k, p, entry, err);
+    uint32_t tile_errs = 0;
+    for (int i = tid; i < p.num_tiles; i += nthreads) tile_errs |= (uint32_t)ws.tile_err[i];
+    for (int i = lane; i < nkeys; i += kWave) counters[i] = 0;
+    // totals[] holds each key's pair count over all tiles; first[] holds, for
+    // now, its pairs in tiles before this one.
+    if (FROM_HIST) {
+        // Every thread sums 16-byte histogram pieces (4 keys) over a strided
+        // set of tiles; the partial sums meet in LDS.
+        for (int j = tid; j < nkeys; j += nthreads) {
+            totals[j] = 0;
+            first[j] = 0;
+        }
+        __syncthreads();
+        const int quads = p.hist_stride / 4;
+        const int groups = nthreads / quads > 1 ? nthreads / quads : 1;
+        const i32x4* hist4 = reinterpret_cast<const i32x4*>(ws.tile_hist);
+        for (int item = tid; item < quads * groups; item += nthreads) {
+            const int q = item % quads, g = item / quads;
+            i32x4 tot = {0, 0, 0, 0}, bef = {0, 0, 0, 0};
+#pragma unroll 4
+            for (int i = g; i < p.num_tiles; i += groups) {
+                const i32x4 h = hist4[(int64_t)i * quads + q];
+                tot += h;
+                if (i < tile) bef += h;
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int j = 4 * q + c;
+                if (j < nkeys && tot[c]) atomicAdd(&totals[j], tot[c]);
+                if (j < nkeys && bef[c]) atomicAdd(&first[j], bef[c]);
+            }
+        }
+    } else {
+        for (int j = tid; j < nkeys; j += nthreads) {
+            totals[j] = ws.totals[j];
+            first[j] = ws.tile_prefix[(int64_t)tile * p.hist_stride + j];
+        }
+    }
+    if (tid == 0) block_err = 0;
+    __syncthreads();
+    if (tile_errs) atomicOr(&block_err, tile_errs);
+
     PairPos pos[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) pos[c] = rank_chunk(entry[c], lane, token_in_chunk, p, counters, err);
@@ -470,6 +508,7 @@ hipError_t launch_layout(const dispatch_problem_t& prob, const TileGeometry& g, 
     p.tokens_per_wave = g.tokens_per_wave;
     p.tokens_per_tile = g.tokens_per_tile;
     p.num_keys = g.num_keys;
+    p.hist_stride = g.hist_stride;
     p.num_tiles = g.num_tiles;
     char* base = static_cast<char*>(workspace);
     Workspace ws;
