@@ -64,8 +64,8 @@ def _run_combine(slots: np.ndarray, wts: np.ndarray, y: torch.Tensor) -> np.ndar
     (257, 6, 32, 2056, 0.1),      # ragged: 4 segments and a 1-vector tail
     (129, 4, 16, 128, 0.3),       # 16 vectors: most lanes idle
     (65, 1, 8, 8, 0.2),           # one vector per row, top-1
-    (96, 32, 64, 1024, 0.25),
-    (100, 11, 64, 512, 0.0),      # a second batch of 3     # the largest top-k: 4 batches of 8 loads
+    (96, 32, 64, 1024, 0.25),     # the largest top-k: 4 batches of 8 loads
+    (100, 11, 64, 512, 0.0),      # a second batch of 3
 ])
 def test_combine_matches_oracle(t, k, e, hidden, mask):
     _banner(f"combine T={t} K={k} E={e} H={hidden} mask={mask}")
