@@ -89,6 +89,30 @@ def test_token_counts_around_tiles(t):
     _edge(_uniform(3, t, 8, 256, 0.05), 256, 8, 4)
 
 
+# Shapes on both sides of every layout geometry switch. Two launches while the
+# tile histograms (16-wavefront tiles, 1/2/4/8 chunks per wavefront) hold at
+# most 65536 ints, else a column scan over 4-wavefront tiles; very wide key
+# sets shrink the tiles to what LDS holds.
+@pytest.mark.parametrize("t,k,e,r", [
+    (31744, 8, 256, 8),     # two launches, 1 chunk per wavefront, 248 tiles (the largest)
+    (31745, 8, 256, 8),     # two launches, 2 chunks
+    (63489, 8, 256, 8),     # two launches, 4 chunks
+    (126977, 8, 256, 8),    # two launches, 8 chunks
+    (253952, 8, 256, 8),    # two launches, 8 chunks, 248 tiles
+    (253953, 8, 256, 8),    # column scan, 8 chunks per wavefront
+    (768, 8, 4096, 1024),   # two launches, 1-wavefront tiles of 8 chunks
+    (769, 8, 4096, 1024),   # column scan, 1 chunk
+    (5000, 8, 4096, 1024),  # column scan, 2 chunks
+    (9000, 8, 4096, 1024),  # column scan, 4 chunks
+    (8000, 8, 2048, 64),    # two launches, 5-wavefront tiles
+    (40000, 8, 2048, 64),   # column scan, 4-wavefront tiles of 4 chunks
+    (70000, 2, 512, 16),    # two launches, top-2: 32 tokens per chunk
+])
+def test_layout_geometry_paths(t, k, e, r):
+    _banner(f"geometry T={t} K={k} E={e} R={r}")
+    _edge(_uniform(11, t, k, e, 0.05), e, r, 2, row_bytes=16)
+
+
 @pytest.mark.parametrize("k,e,r", [(1, 8, 2), (2, 16, 16), (3, 12, 4), (6, 64, 8), (7, 128, 128),
                                    (16, 64, 4), (32, 64, 8), (32, 32, 32), (5, 4096, 64), (8, 4096, 1024)])
 def test_topk_and_expert_shapes(k, e, r):
