@@ -47,6 +47,8 @@ def parse_args():
                     help="bracket the scatter with HIP events on every n-th timed step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=100,
+                    help="steps timed one by one, back to back and after a 512 MiB cache-evicting read (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for counter calibration)")
     ap.add_argument("--expand", action="store_true",
@@ -414,6 +416,48 @@ def main():
               "us_per_step": round(replay_s * 1e6, 2),
               "what": "dispatch_scatter alone on a saved layout (cached dispatch)"}
 
+    # Layout alone, back to back (HIP events on the launch stream).
+    lay_steps = max(1, args.steps // 4)
+    ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev_a.record(stream)
+    for _ in range(lay_steps):
+        plan.layout()
+    ev_b.record(stream)
+    torch.cuda.synchronize()
+    layout_only_us = ev_a.elapsed_time(ev_b) * 1e3 / lay_steps
+
+    # One step at a time, HIP events around each: back to back, and with a
+    # 512 MiB read sweep before every step (outside its events) that pushes
+    # the previous step's data out of the 256 MB Infinity Cache. A read
+    # leaves clean lines behind; a write would leave dirty ones for the
+    # timed step to write back.
+    cold = None
+    if args.cold_steps > 0:
+        scratch = torch.ones(64 << 20, dtype=torch.int64, device=dev)
+        sink = torch.empty((), dtype=torch.int64, device=dev)
+
+        def per_step(evict):
+            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(args.cold_steps)]
+            torch.cuda.synchronize()
+            for e0, e1 in pairs:
+                if evict:
+                    torch.sum(scratch, dim=0, out=sink)
+                e0.record(stream)
+                plan()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
+            q = lambda f: us[min(len(us) - 1, int(f * (len(us) - 1) + 0.5))]  # noqa: E731
+            return {"median_us": round(q(0.5), 2), "p10_us": round(q(0.1), 2), "p90_us": round(q(0.9), 2),
+                    "GBps_at_median": round(total_b / (q(0.5) * 1e-6) / 1e9, 1)}
+
+        cold = {"steps": args.cold_steps, "back_to_back": per_step(False), "after_512MiB_read": per_step(True),
+                "what": "layout + scatter, HIP events around each step"}
+        del scratch, sink
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         med, reps = cpu_baseline(inp, w, args.cpu_seconds)
@@ -448,6 +492,9 @@ def main():
         "pairs_per_s": round(p_valid / (wall / args.steps), 1),
         "layout_and_gaps_us_mean": round(statistics.mean(layout_ms) * 1e3, 2),
         "scatter_us_mean": round(sc_mean_ms * 1e3, 2),
+        "layout_only_us": round(layout_only_us, 2),
+        "payload_GBps": round((n_rank + p_valid) * (w.row_bytes + 4 * s) / (wall / args.steps) / 1e9, 1),
+        "per_step_events": cold,
         "scatter_event_samples": len(scatter_ms),
         "rows": {"expert_major": p_rows, "rank_contig": n_rank, "live_tokens": t_live, "pairs": p_valid},
         "roofline": {
