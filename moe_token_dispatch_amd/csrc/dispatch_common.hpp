@@ -24,7 +24,7 @@ constexpr int kMaxTilesTarget = 512;  // more chunks per wavefront beyond this m
 constexpr int kFromHistMaxInts = 65536; // up to this many histogram ints, assign reduces them itself
 constexpr int kFewTileWaves = 16;     // wavefronts per tile on the few-tiles path
 constexpr int kManyTileWaves = 4;     // wavefronts per tile on the column-scan path
-constexpr int kLdsBudgetInts = 16000; // LDS ints per workgroup for key arrays, under 64 KiB
+constexpr int kLdsBudgetInts = 40000; // LDS ints per workgroup for key arrays (gfx950: 160 KiB per CU)
 
 struct TileGeometry {
     int64_t num_tokens;
