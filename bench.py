@@ -34,6 +34,7 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scatter_traffic.json")
 SCATTER_SOURCES = [os.path.join(ROOT, "moe_token_dispatch_amd", "csrc", "dispatch_scatter.hip")]
 COMBINE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_traffic.json")
+EXPAND_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expand_scatter_traffic.json")
 COMBINE_SOURCES = [os.path.join(ROOT, "moe_token_dispatch_amd", "csrc", "dispatch_combine.hip")]
 
 
@@ -231,6 +232,19 @@ def expand_bench(args):
     row = rb + 4 * s_f
     total_b = received * k * 8 + 4 * s_count + received * row + p_rows * row + \
         4 * (2 * local + 2 + s_count * m * k + p_rows)
+    # The expand's row copy alone on its saved layout, HIP events on the launch
+    # stream: every received row read once, every expert-major row written
+    # (pads as zeros), the slot map read.
+    scatter_b = received * row + p_rows * row + 4 * s_count * m * k + 4 * (2 * local + 1)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_sc = max(1, args.steps // 2)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(n_sc):
+        M.dispatch_expand_scatter(q, elay, recv_buf, recv_sf, recv_x, out_sf, stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    sc_s = ev0.elapsed_time(ev1) / 1e3 / n_sc
     out = {
         "metric": "receiver-side expand GB/s & % HBM peak",
         "value": round(total_b / dt / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -241,6 +255,13 @@ def expand_bench(args):
                    "local_experts": local, "expert_alignment": base.alignment},
         "hbm_frac": round(total_b / dt / 1e9 / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": total_b,
+        "roofline": {
+            "kernel": "scatter_kernel (expand)", "bound": "hbm",
+            "achieved": round(scatter_b / sc_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(scatter_b / sc_s / 1e9 / HBM_PEAK_GBPS, 4),
+            "traffic": load_traffic(EXPAND_TRAFFIC_FILE, SCATTER_SOURCES, base.name),
+            "algorithmic_bytes_per_launch": scatter_b, "launch_us_mean": round(sc_s * 1e6, 2),
+        },
     }
     print(json.dumps(out), flush=True)
 
