@@ -140,7 +140,9 @@ int dispatch_layout(const dispatch_problem_t* problem, const void* topk_idx,
  *   rank_x [rank_psum[R], row_bytes] and rank_sf [rank_psum[R], S];
  *   recv_x [expert_psum[E], row_bytes] and recv_sf [expert_psum[E], S], with
  *   pad rows zeroed under DISPATCH_ZERO_PAD.
- * Copies are bitwise. Writes nothing when the layout's status is non-zero. */
+ * Copies are bitwise. Writes nothing when the layout's status is non-zero.
+ * A layout may be kept and scattered again, for new rows of the same routing,
+ * without recomputing it (the page's cached dispatch, section 6.2). */
 int dispatch_scatter(const dispatch_problem_t* problem, const dispatch_layout_t* layout,
                      const void* x, const float* x_sf, void* rank_x, float* rank_sf,
                      void* recv_x, float* recv_sf, hipStream_t stream);

@@ -153,3 +153,14 @@ def test_combine_grid_loops_over_many_tokens():
     w, topk, ref, y, wts = _combine_inputs(150000, 8, 64, 64, 0.05, seed=14)
     got = _run_combine(ref.expert_slot, wts, y)
     _check(got, y.view(torch.int16).numpy().view(np.uint16), wts, ref.expert_slot)
+
+
+def test_combine_signed_weights():
+    """Weights of both signs (the sum can cancel): the bound uses |w|, and most
+    outputs still equal the exact sum rounded to bf16."""
+    _banner("signed weights")
+    w, topk, ref, y, wts = _combine_inputs(400, 8, 64, 520, 0.1, seed=15)
+    sign = np.where(np.random.default_rng([15, 1]).random(wts.shape) < 0.5, -1.0, 1.0).astype(np.float32)
+    signed = wts * sign
+    got = _run_combine(ref.expert_slot, signed, y)
+    _check(got, y.view(torch.int16).numpy().view(np.uint16), signed, ref.expert_slot, min_exact=0.98)
