@@ -59,6 +59,42 @@ int check_expand(const dispatch_expand_problem_t* q, dispatch_problem_t* p) {
     return check_problem(p);
 }
 
+// Host checks and launch of the row scatter. few_destinations: rows go to
+// about one destination each (the receiver-side expand, a top-1 expert copy).
+int scatter_checked(const dispatch_problem_t* problem, const dispatch_layout_t* layout, const void* x,
+                    const float* x_sf, void* rank_x, float* rank_sf, void* recv_x, float* recv_sf,
+                    hipStream_t stream, bool few_destinations) {
+    int rc = check_problem(problem);
+    if (rc != DISPATCH_OK) return rc;
+    const dispatch_problem_t& p = *problem;
+    if (p.row_bytes <= 0 || p.row_bytes > INT32_MAX) return DISPATCH_ERR_ARG;
+    if (p.row_bytes % 16 != 0) return DISPATCH_ERR_ALIGN;
+    if (layout == nullptr || !layout->status || !layout->expert_count || !layout->expert_psum)
+        return DISPATCH_ERR_NULL;
+    const bool want_rank = (p.flags & DISPATCH_RANK_CONTIG) != 0;
+    const bool want_expert = (p.flags & DISPATCH_EXPERT_MAJOR) != 0;
+    const bool want_sf = p.sf_per_token > 0;
+    if (p.num_tokens > 0) {
+        if (!x || !layout->expert_slot || (want_rank && !layout->rank_slot)) return DISPATCH_ERR_NULL;
+        if (want_sf && !x_sf) return DISPATCH_ERR_NULL;
+    }
+    if (want_rank && p.rank_capacity_rows > 0 && (!rank_x || (want_sf && !rank_sf))) return DISPATCH_ERR_NULL;
+    if (want_expert && p.recv_capacity_rows > 0 && (!recv_x || (want_sf && !recv_sf))) return DISPATCH_ERR_NULL;
+    const void* rows[] = {x, rank_x, recv_x};
+    for (const void* q : rows)
+        if (q && !aligned_to(q, 16)) return DISPATCH_ERR_ALIGN;
+    const void* words[] = {x_sf, rank_sf, recv_sf, layout->expert_slot, layout->rank_slot,
+                           layout->expert_count, layout->expert_psum, layout->status};
+    for (const void* q : words)
+        if (q && !aligned_to(q, 4)) return DISPATCH_ERR_ALIGN;
+
+    if (moe_dispatch::launch_scatter(p, *layout, x, x_sf, rank_x, rank_sf, recv_x, recv_sf, stream,
+                                     few_destinations) != hipSuccess)
+        return DISPATCH_ERR_HIP;
+    return DISPATCH_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -127,36 +163,17 @@ int dispatch_layout(const dispatch_problem_t* problem, const void* topk_idx, con
     return DISPATCH_OK;
 }
 
+
 int dispatch_scatter(const dispatch_problem_t* problem, const dispatch_layout_t* layout, const void* x,
                      const float* x_sf, void* rank_x, float* rank_sf, void* recv_x, float* recv_sf,
                      hipStream_t stream) {
-    int rc = check_problem(problem);
-    if (rc != DISPATCH_OK) return rc;
-    const dispatch_problem_t& p = *problem;
-    if (p.row_bytes <= 0 || p.row_bytes > INT32_MAX) return DISPATCH_ERR_ARG;
-    if (p.row_bytes % 16 != 0) return DISPATCH_ERR_ALIGN;
-    if (layout == nullptr || !layout->status || !layout->expert_count || !layout->expert_psum)
-        return DISPATCH_ERR_NULL;
-    const bool want_rank = (p.flags & DISPATCH_RANK_CONTIG) != 0;
-    const bool want_expert = (p.flags & DISPATCH_EXPERT_MAJOR) != 0;
-    const bool want_sf = p.sf_per_token > 0;
-    if (p.num_tokens > 0) {
-        if (!x || !layout->expert_slot || (want_rank && !layout->rank_slot)) return DISPATCH_ERR_NULL;
-        if (want_sf && !x_sf) return DISPATCH_ERR_NULL;
+    // Destinations per row: K expert rows and one rank row at most.
+    int dests = 0;
+    if (problem != nullptr) {
+        if (problem->flags & DISPATCH_EXPERT_MAJOR) dests += problem->num_topk;
+        if (problem->flags & DISPATCH_RANK_CONTIG) dests += 1;
     }
-    if (want_rank && p.rank_capacity_rows > 0 && (!rank_x || (want_sf && !rank_sf))) return DISPATCH_ERR_NULL;
-    if (want_expert && p.recv_capacity_rows > 0 && (!recv_x || (want_sf && !recv_sf))) return DISPATCH_ERR_NULL;
-    const void* rows[] = {x, rank_x, recv_x};
-    for (const void* q : rows)
-        if (q && !aligned_to(q, 16)) return DISPATCH_ERR_ALIGN;
-    const void* words[] = {x_sf, rank_sf, recv_sf, layout->expert_slot, layout->rank_slot,
-                           layout->expert_count, layout->expert_psum, layout->status};
-    for (const void* q : words)
-        if (q && !aligned_to(q, 4)) return DISPATCH_ERR_ALIGN;
-
-    if (moe_dispatch::launch_scatter(p, *layout, x, x_sf, rank_x, rank_sf, recv_x, recv_sf, stream) != hipSuccess)
-        return DISPATCH_ERR_HIP;
-    return DISPATCH_OK;
+    return scatter_checked(problem, layout, x, x_sf, rank_x, rank_sf, recv_x, recv_sf, stream, dests <= 1);
 }
 
 int dispatch_expand_workspace_size(const dispatch_expand_problem_t* problem, size_t* bytes) {
@@ -215,7 +232,7 @@ int dispatch_expand_scatter(const dispatch_expand_problem_t* problem, const disp
     if (rc != DISPATCH_OK) return rc;
     if (layout != nullptr && (layout->rank_slot || layout->rank_count)) return DISPATCH_ERR_ARG;
     p.rank_capacity_rows = 0;
-    return dispatch_scatter(&p, layout, recv_buf, recv_sf_buf, nullptr, nullptr, recv_x, recv_sf, stream);
+    return scatter_checked(&p, layout, recv_buf, recv_sf_buf, nullptr, nullptr, recv_x, recv_sf, stream, true);
 }
 
 int dispatch_combine(const dispatch_combine_problem_t* problem, const int32_t* expert_slot,

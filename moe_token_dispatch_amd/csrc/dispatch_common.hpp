@@ -114,9 +114,10 @@ struct ExpandView {
 hipError_t launch_layout(const dispatch_problem_t& p, const TileGeometry& g, const void* topk_idx,
                          const dispatch_layout_t& out, void* workspace, hipStream_t stream,
                          const ExpandView* expand = nullptr);
+// few_destinations: rows go to about one destination each (sets the segment width).
 hipError_t launch_scatter(const dispatch_problem_t& p, const dispatch_layout_t& lay, const void* x,
                           const float* x_sf, void* rank_x, float* rank_sf, void* recv_x,
-                          float* recv_sf, hipStream_t stream);
+                          float* recv_sf, hipStream_t stream, bool few_destinations);
 hipError_t launch_combine(int64_t num_tokens, int32_t num_topk, int64_t row_bytes, int64_t expert_rows,
                           const int32_t* expert_slot, const float* weights, const void* y, void* out,
                           hipStream_t stream);

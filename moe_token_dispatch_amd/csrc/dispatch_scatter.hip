@@ -28,7 +28,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kScatterWaves = 4;  // wavefronts per 256-thread workgroup
 constexpr int kPadRowsPerWave = 8;
-constexpr int kMaxVecsPerLane = 8;  // V: 16-byte vectors per lane per row segment
+// V, the 16-byte vectors per lane of one row segment, follows the stores per
+// loaded row (measured on MI355X): with many destinations per row (dispatch:
+// K expert rows and the rank rows) one vector per lane, i.e. many short
+// wavefronts, moves the rows fastest; with about one destination per row
+// (the receiver-side expand, a top-1 copy) four vectors per lane do.
+constexpr int kVecsManyDestinations = 1;
+constexpr int kVecsFewDestinations = 4;
 
 struct ScatterParams {
     int64_t num_tokens;
@@ -173,12 +179,13 @@ hipError_t launch_v(dim3 grid, hipStream_t stream, const u32x4* x, const uint32_
 
 hipError_t launch_scatter(const dispatch_problem_t& prob, const dispatch_layout_t& lay, const void* x,
                           const float* x_sf, void* rank_x, float* rank_sf, void* recv_x, float* recv_sf,
-                          hipStream_t stream) {
+                          hipStream_t stream, bool few_destinations) {
     ScatterParams p{};
     p.num_tokens = prob.num_tokens;
     p.row_vecs = prob.row_bytes / 16;
-    // Segments of about kMaxVecsPerLane vectors per lane, balanced over the row.
-    p.segments = (int32_t)((p.row_vecs + kWave * kMaxVecsPerLane - 1) / (kWave * kMaxVecsPerLane));
+    // Segments of about max_vecs vectors per lane, balanced over the row.
+    const int max_vecs = few_destinations ? kVecsFewDestinations : kVecsManyDestinations;
+    p.segments = (int32_t)((p.row_vecs + kWave * max_vecs - 1) / (kWave * max_vecs));
     if (p.segments < 1) p.segments = 1;
     const int64_t seg_vecs = (p.row_vecs + p.segments - 1) / p.segments;
     const int v = (int)((seg_vecs + kWave - 1) / kWave);
@@ -212,12 +219,8 @@ hipError_t launch_scatter(const dispatch_problem_t& prob, const dispatch_layout_
         MOE_DISPATCH_SCATTER_CASE(1)
         MOE_DISPATCH_SCATTER_CASE(2)
         MOE_DISPATCH_SCATTER_CASE(3)
-        MOE_DISPATCH_SCATTER_CASE(4)
-        MOE_DISPATCH_SCATTER_CASE(5)
-        MOE_DISPATCH_SCATTER_CASE(6)
-        MOE_DISPATCH_SCATTER_CASE(7)
         default:
-            return launch_v<8>(grid, stream, xs, sfs, p, lay.expert_slot, lay.rank_slot, lay.expert_count,
+            return launch_v<4>(grid, stream, xs, sfs, p, lay.expert_slot, lay.rank_slot, lay.expert_count,
                                lay.expert_psum, lay.status, rx, rsf, ex, esf);
     }
 #undef MOE_DISPATCH_SCATTER_CASE
