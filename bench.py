@@ -48,6 +48,8 @@ def parse_args():
                     help="bracket the scatter with HIP events on every n-th timed step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph-steps", type=int, default=1000,
+                    help="steps replayed from a captured HIP graph, reported beside the eager steps (0 = skip)")
     ap.add_argument("--cold-steps", type=int, default=100,
                     help="steps timed one by one, back to back and after a 512 MiB cache-evicting read (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -437,6 +439,35 @@ def main():
               "us_per_step": round(replay_s * 1e6, 2),
               "what": "dispatch_scatter alone on a saved layout (cached dispatch)"}
 
+    # The same step captured once into a HIP graph and replayed: the kernels
+    # and buffers are the eager step's; only the launch path differs.
+    graph_res = None
+    if args.graph_steps > 0:
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            M.dispatch_layout(prob, topk_d, lay, ws)
+            M.dispatch_scatter(prob, lay, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x, rows.recv_sf)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            M.dispatch_layout(prob, topk_d, lay, ws)
+            M.dispatch_scatter(prob, lay, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x, rows.recv_sf)
+        for _ in range(max(1, args.graph_steps // 10)):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        for _ in range(args.graph_steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        g_s = (time.perf_counter() - g0) / args.graph_steps
+        if int(lay.status.item()) != 0:
+            raise RuntimeError("graph replay left a non-zero layout status")
+        graph_res = {"value": round(total_b / g_s / 1e9, 1), "unit": "GB/s", "steps": args.graph_steps,
+                     "us_per_step": round(g_s * 1e6, 2),
+                     "what": "the same layout + scatter step captured into a HIP graph and replayed"}
+        del graph
+
     # Layout alone, back to back (HIP events on the launch stream).
     lay_steps = max(1, args.steps // 4)
     ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -529,6 +560,7 @@ def main():
             "algorithmic_bytes_per_launch": sc_b,
         },
         "replay_scatter_only": replay,
+        "graph_step": graph_res,
         "device_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
