@@ -153,16 +153,20 @@ def cpu_baseline(inp, w, budget_s):
     prep = oracle.Prepared(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment, inp.x_bytes(), inp.x_sf)
     prep.run_layout()
     prep.run_scatter()  # warm-up
-    times = []
+    times, lay_t, sc_t = [], [], []
     t_end = time.perf_counter() + budget_s
     while time.perf_counter() < t_end or len(times) < 3:
         t0 = time.perf_counter()
         rc = prep.run_layout()
+        t1 = time.perf_counter()
         rc |= prep.run_scatter()
-        times.append(time.perf_counter() - t0)
+        t2 = time.perf_counter()
+        times.append(t2 - t0)
+        lay_t.append(t1 - t0)
+        sc_t.append(t2 - t1)
         if rc:
             raise RuntimeError(f"oracle status {rc}")
-    return statistics.median(times), len(times)
+    return statistics.median(times), len(times), statistics.median(lay_t), statistics.median(sc_t)
 
 
 def expand_bench(args):
@@ -512,11 +516,12 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        med, reps = cpu_baseline(inp, w, args.cpu_seconds)
+        med, reps, med_lay, med_sc = cpu_baseline(inp, w, args.cpu_seconds)
         cpu = {"value": round(total_b / med / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": f"full {w.name} step (layout + scatter of all {t} tokens), median of {reps} runs, "
                          "single-threaded C oracle on pre-faulted host buffers",
-               "ms_per_step": round(med * 1e3, 2)}
+               "ms_per_step": round(med * 1e3, 2), "layout_ms": round(med_lay * 1e3, 3),
+               "scatter_ms": round(med_sc * 1e3, 2)}
 
     ceiling = measure_device_ceiling(torch)
     out = {
