@@ -147,10 +147,35 @@ def measure_device_ceiling(torch):
 
 def cpu_baseline(inp, w, budget_s):
     """The CPU oracle as it stands (single-threaded C), layout + scatter of the
-    same input, repeated until the time budget is spent."""
+    same input, repeated until the time budget is spent, on one pinned core.
+    Returns the medians of the step, the layout and the scatter."""
     import oracle
 
     prep = oracle.Prepared(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment, inp.x_bytes(), inp.x_sf)
+    # Pin this thread to one core while the oracle runs (restored afterwards).
+    allowed = os.sched_getaffinity(0)
+    os.sched_setaffinity(0, {min(allowed)})
+    try:
+        return _time_oracle(prep, budget_s)
+    finally:
+        os.sched_setaffinity(0, allowed)
+
+
+def host_cpu():
+    """Model name and logical CPU count of the host the oracle ran on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count(), "allowed_cpus": len(os.sched_getaffinity(0))}
+
+
+def _time_oracle(prep, budget_s):
     prep.run_layout()
     prep.run_scatter()  # warm-up
     times, lay_t, sc_t = [], [], []
@@ -521,7 +546,7 @@ def main():
                "sample": f"full {w.name} step (layout + scatter of all {t} tokens), median of {reps} runs, "
                          "single-threaded C oracle on pre-faulted host buffers",
                "ms_per_step": round(med * 1e3, 2), "layout_ms": round(med_lay * 1e3, 3),
-               "scatter_ms": round(med_sc * 1e3, 2)}
+               "scatter_ms": round(med_sc * 1e3, 2), "pinned_to_one_core": True, "host": host_cpu()}
 
     ceiling = measure_device_ceiling(torch)
     out = {
