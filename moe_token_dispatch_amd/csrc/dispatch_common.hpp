@@ -21,7 +21,8 @@ constexpr int kWave = 64;             // gfx950 wavefront width
 constexpr int kLayoutThreads = 1024;  // at most 16 wavefronts per layout workgroup
 constexpr int kScanThreads = 1024;    // threads per column-scan workgroup
 constexpr int kMaxTilesTarget = 512;  // more chunks per wavefront beyond this many tiles
-constexpr int kFromHistMaxInts = 65536; // up to this many histogram ints, assign reduces them itself
+constexpr int kFromHistMaxInts = 65536;  // up to this many histogram ints, assign reduces them itself
+constexpr int kSingleTileChunks = 2;     // most chunks per wavefront of a one-launch single tile
 constexpr int kFewTileWaves = 16;     // wavefronts per tile on the few-tiles path
 constexpr int kManyTileWaves = 4;     // wavefronts per tile on the column-scan path
 constexpr int kLdsBudgetInts = 40000; // LDS ints per workgroup for key arrays (gfx950: 160 KiB per CU)
@@ -68,6 +69,15 @@ inline TileGeometry make_geometry(int64_t num_tokens, int32_t num_topk, int32_t 
     // would make the column scan long.
     g.waves_per_tile = clamp_w(kFewTileWaves);
     g.column_scan = true;
+    // A batch that one tile of up to kSingleTileChunks chunks per wavefront
+    // holds is laid out by one workgroup in one launch.
+    for (g.chunks_per_wave = 1; g.chunks_per_wave <= kSingleTileChunks; g.chunks_per_wave *= 2) {
+        if (num_tokens <= (int64_t)g.waves_per_tile * g.chunks_per_wave * g.tokens_per_chunk) {
+            g.column_scan = false;
+            break;
+        }
+    }
+    if (g.column_scan)
     for (g.chunks_per_wave = 1; g.chunks_per_wave <= 8; g.chunks_per_wave *= 2) {
         const int64_t per_tile = (int64_t)g.waves_per_tile * g.chunks_per_wave * g.tokens_per_chunk;
         if ((num_tokens + per_tile - 1) / per_tile * g.hist_stride <= kFromHistMaxInts) {

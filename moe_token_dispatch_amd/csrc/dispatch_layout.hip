@@ -306,7 +306,14 @@ colscan_kernel(LayoutParams p, Workspace ws, int kpb) {
     }
 }
 
-template <int CH, bool FROM_HIST, bool EXPAND, typename IdxT>
+// Where assign_kernel takes each key's count in earlier tiles and in all tiles:
+enum AssignMode {
+    kFromColumnScan = 0,  // the column-scan kernel's prefixes and totals
+    kFromHistograms = 1,  // its own reduction of the count kernel's tile histograms
+    kSingleTile = 2,      // one tile holds every pair: its own wavefront counters (no count kernel)
+};
+
+template <int CH, int MODE, bool EXPAND, typename IdxT>
 __global__ void __launch_bounds__(kLayoutThreads)
 assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispatch_layout_t out) {
     // LDS: [W][num_keys] wavefront counters, then totals[num_keys] and first[num_keys].
@@ -330,11 +337,12 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
     uint32_t err = 0;
     load_entries<CH, EXPAND>(topk, wave_tok0, token_in_chunk, k, p, entry, err);
     uint32_t tile_errs = 0;
-    for (int i = tid; i < p.num_tiles; i += nthreads) tile_errs |= (uint32_t)ws.tile_err[i];
+    if (MODE != kSingleTile)
+        for (int i = tid; i < p.num_tiles; i += nthreads) tile_errs |= (uint32_t)ws.tile_err[i];
     for (int i = lane; i < nkeys; i += kWave) counters[i] = 0;
     // totals[] holds each key's pair count over all tiles; first[] holds, for
     // now, its pairs in tiles before this one.
-    if (FROM_HIST) {
+    if (MODE == kFromHistograms) {
         // Every thread sums 16-byte histogram pieces (4 keys) over a strided
         // set of tiles; the partial sums meet in LDS.
         for (int j = tid; j < nkeys; j += nthreads) {
@@ -361,7 +369,7 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
                 if (j < nkeys && bef[c]) atomicAdd(&first[j], bef[c]);
             }
         }
-    } else {
+    } else if (MODE == kFromColumnScan) {
         for (int j = tid; j < nkeys; j += nthreads) {
             totals[j] = ws.totals[j];
             first[j] = ws.tile_prefix[(int64_t)tile * p.hist_stride + j];
@@ -374,20 +382,30 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
     PairPos pos[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) pos[c] = rank_chunk(entry[c], lane, token_in_chunk, p, counters, err);
+    if (MODE == kSingleTile) {
+        // No count kernel ran: this workgroup's own ranking found the errors.
+        uint32_t wave_err = 0;
+        for (uint32_t bit = 1; bit <= DISPATCH_STATUS_BAD_COUNT; bit <<= 1)
+            if (__ballot((err & bit) != 0)) wave_err |= bit;
+        if (lane == 0 && wave_err) atomicOr(&block_err, wave_err);
+    }
 
     // Fold the earlier-tile pairs into the wavefront counters, then scan the
     // totals into the exclusive psums: expert counts aligned up first
     // (section 7.2), rank counts as they are (section 5.2). The scan's
-    // barriers also publish the wavefront counters and block_err.
+    // barriers also publish the wavefront counters and block_err. A single
+    // tile has no earlier tiles, and its totals are its counters' sums.
     __syncthreads();
     for (int j = tid; j < nkeys; j += nthreads) {
-        int run = first[j];
+        int run = MODE == kSingleTile ? 0 : first[j];
         for (int w = 0; w < nwaves; ++w) {
             const int c = lds[w * nkeys + j];
             lds[w * nkeys + j] = run;
             run += c;
         }
+        if (MODE == kSingleTile) totals[j] = run;
     }
+    if (MODE == kSingleTile) __syncthreads();
     const int recv_rows = block_exclusive_scan(totals, first, E, p.alignment, scratch);
     const int rank_rows = block_exclusive_scan(totals + E, first + E, R, 1, scratch);
     uint32_t status = block_err;
@@ -458,23 +476,26 @@ hipError_t launch_typed(const LayoutParams& p, const TileGeometry& g, const void
     LayoutParams pc = p;
     Workspace wc = ws;
     dispatch_layout_t oc = out;
+    const size_t assign_lds = (size_t)(g.waves_per_tile + 2) * g.num_keys * sizeof(int);
+    void* assign_args[] = {&idx, &pc, &wc, &oc};
+    if (g.num_tiles == 1 && !g.column_scan)
+        return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, kSingleTile, EXPAND, IdxT>), grid,
+                               block, assign_args, assign_lds, stream);
     const size_t count_lds = (size_t)g.waves_per_tile * g.num_keys * sizeof(int);
     void* count_args[] = {&idx, &pc, &wc};
     hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&count_kernel<CH, EXPAND, IdxT>), grid, block,
                                      count_args, count_lds, stream);
     if (err != hipSuccess) return err;
-    const size_t assign_lds = (size_t)(g.waves_per_tile + 2) * g.num_keys * sizeof(int);
-    void* assign_args[] = {&idx, &pc, &wc, &oc};
     if (!g.column_scan)
-        return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, true, EXPAND, IdxT>), grid, block,
-                               assign_args, assign_lds, stream);
+        return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, kFromHistograms, EXPAND, IdxT>),
+                               grid, block, assign_args, assign_lds, stream);
     int kpb = g.num_keys < kWave ? g.num_keys : kWave;
     void* scan_args[] = {&pc, &wc, &kpb};
     err = hipLaunchKernel(reinterpret_cast<const void*>(&colscan_kernel),
                           dim3((g.num_keys + kpb - 1) / kpb), dim3(kScanThreads), scan_args, 0, stream);
     if (err != hipSuccess) return err;
-    return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, false, EXPAND, IdxT>), grid, block,
-                           assign_args, assign_lds, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, kFromColumnScan, EXPAND, IdxT>), grid,
+                           block, assign_args, assign_lds, stream);
 }
 
 template <bool EXPAND, typename IdxT>

@@ -83,7 +83,9 @@ def _uniform(seed, t, k, e, mask=0.0):
     return W.make_topk(w)
 
 
-@pytest.mark.parametrize("t", [0, 1, 2, 63, 64, 65, 1023, 1024, 1025])
+# Up to 256 tokens at top-8 one workgroup lays the batch out in one launch
+# (1 or 2 chunks per wavefront); from 257 on, tiles and two launches.
+@pytest.mark.parametrize("t", [0, 1, 2, 63, 64, 65, 128, 129, 200, 256, 257, 1023, 1024, 1025])
 def test_token_counts_around_tiles(t):
     _banner(f"T={t}")
     _edge(_uniform(3, t, 8, 256, 0.05), 256, 8, 4)
