@@ -368,6 +368,38 @@ def combine_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def graph_step(args, dev, stream, prob, topk_d, lay, ws, x_d, sf_d, rows, total_b):
+    """The same step captured once into a HIP graph and replayed: the kernels
+    and buffers are the eager step's; only the launch path differs."""
+    import torch
+
+    import moe_token_dispatch_amd as M
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        M.dispatch_layout(prob, topk_d, lay, ws)
+        M.dispatch_scatter(prob, lay, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x, rows.recv_sf)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        M.dispatch_layout(prob, topk_d, lay, ws)
+        M.dispatch_scatter(prob, lay, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x, rows.recv_sf)
+    for _ in range(max(1, args.graph_steps // 10)):
+        graph.replay()
+    torch.cuda.synchronize()
+    g0 = time.perf_counter()
+    for _ in range(args.graph_steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    g_s = (time.perf_counter() - g0) / args.graph_steps
+    if int(lay.status.item()) != 0:
+        raise RuntimeError("graph replay left a non-zero layout status")
+    return {"value": round(total_b / g_s / 1e9, 1), "unit": "GB/s", "steps": args.graph_steps,
+            "us_per_step": round(g_s * 1e6, 2),
+            "what": "the same layout + scatter step captured into a HIP graph and replayed"}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -468,34 +500,13 @@ def main():
               "us_per_step": round(replay_s * 1e6, 2),
               "what": "dispatch_scatter alone on a saved layout (cached dispatch)"}
 
-    # The same step captured once into a HIP graph and replayed: the kernels
-    # and buffers are the eager step's; only the launch path differs.
     graph_res = None
     if args.graph_steps > 0:
-        side = torch.cuda.Stream(device=dev)
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            M.dispatch_layout(prob, topk_d, lay, ws)
-            M.dispatch_scatter(prob, lay, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x, rows.recv_sf)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=side):
-            M.dispatch_layout(prob, topk_d, lay, ws)
-            M.dispatch_scatter(prob, lay, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x, rows.recv_sf)
-        for _ in range(max(1, args.graph_steps // 10)):
-            graph.replay()
-        torch.cuda.synchronize()
-        g0 = time.perf_counter()
-        for _ in range(args.graph_steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        g_s = (time.perf_counter() - g0) / args.graph_steps
-        if int(lay.status.item()) != 0:
-            raise RuntimeError("graph replay left a non-zero layout status")
-        graph_res = {"value": round(total_b / g_s / 1e9, 1), "unit": "GB/s", "steps": args.graph_steps,
-                     "us_per_step": round(g_s * 1e6, 2),
-                     "what": "the same layout + scatter step captured into a HIP graph and replayed"}
-        del graph
+        try:
+            graph_res = graph_step(args, dev, stream, prob, topk_d, lay, ws, x_d, sf_d, rows, total_b)
+        except Exception as exc:  # an optional figure: report it, keep the contract line
+            torch.cuda.synchronize()
+            graph_res = {"error": f"{type(exc).__name__}: {exc}"}
 
     # Layout alone, back to back (HIP events on the launch stream).
     lay_steps = max(1, args.steps // 4)
