@@ -11,3 +11,9 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: takes more than a few seconds on the CPU")
+    # A fresh checkout has no built library (built files stay out of the
+    # history): build it once, in-tree. An existing build is used as it is.
+    from moe_token_dispatch_amd import build as libbuild
+
+    if not os.path.exists(libbuild.LIB_PATH):
+        libbuild.build()
