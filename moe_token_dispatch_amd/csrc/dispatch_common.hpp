@@ -23,7 +23,8 @@ constexpr int kScanThreads = 1024;    // threads per column-scan workgroup
 constexpr int kMaxTilesTarget = 512;  // more chunks per wavefront beyond this many tiles
 constexpr int kFromHistMaxInts = 65536;  // up to this many histogram ints, assign reduces them itself
 constexpr int kSingleTileChunks = 2;     // most chunks per wavefront of a one-launch single tile
-constexpr int kFewTileWaves = 16;     // wavefronts per tile on the few-tiles path
+constexpr int kFewTileWaves = 16;     // wavefronts per tile on the two-launch path (at most)
+constexpr int kMidTileWaves = 8;      // wavefronts per tile on the two-launch path when the histograms fit
 constexpr int kManyTileWaves = 4;     // wavefronts per tile on the column-scan path
 constexpr int kLdsBudgetInts = 40000; // LDS ints per workgroup for key arrays (gfx950: 160 KiB per CU)
 
@@ -61,28 +62,43 @@ inline TileGeometry make_geometry(int64_t num_tokens, int32_t num_topk, int32_t 
     auto clamp_w = [&](int cap) { return w_lds < 1 ? 1 : (w_lds > cap ? cap : w_lds); };
     // Histogram rows are padded to whole 16-byte vectors.
     g.hist_stride = (g.num_keys + 3) / 4 * 4;
-    // While the tile histograms of 16-wavefront tiles (1, 2, 4 or 8 chunks
-    // per wavefront, the fewest that fit) stay small, every assign workgroup
-    // reduces them itself: two kernels, as a launch costs a few microseconds,
-    // more than that reduction. Otherwise tiles of 4 wavefronts and a
-    // column-scan kernel, with more chunks per wavefront once the tile count
-    // would make the column scan long.
-    g.waves_per_tile = clamp_w(kFewTileWaves);
+    // One launch when a single tile holds the batch: one chunk per wavefront
+    // and just enough wavefronts, else 16 wavefronts of kSingleTileChunks.
+    // Two launches while the tile histograms stay small (every assign
+    // workgroup reduces them itself; a launch costs a few microseconds, more
+    // than that reduction): 8-wavefront tiles, else 16-wavefront tiles of 1,
+    // 2, 4 or 8 chunks per wavefront, the fewest that fit. Otherwise tiles of
+    // 4 wavefronts and a column-scan kernel, with more chunks per wavefront
+    // once the tile count would make the column scan long. (Measured on
+    // MI355X: 8-wavefront tiles lay out 512 to 8192 tokens fastest.)
+    const int w_full = clamp_w(kFewTileWaves);
+    const int64_t tpc = g.tokens_per_chunk;
+    auto tiles_of = [&](int w, int ch) { return (num_tokens + (int64_t)w * ch * tpc - 1) / ((int64_t)w * ch * tpc); };
     g.column_scan = true;
-    // A batch that one tile of up to kSingleTileChunks chunks per wavefront
-    // holds is laid out by one workgroup in one launch.
-    for (g.chunks_per_wave = 1; g.chunks_per_wave <= kSingleTileChunks; g.chunks_per_wave *= 2) {
-        if (num_tokens <= (int64_t)g.waves_per_tile * g.chunks_per_wave * g.tokens_per_chunk) {
+    if (num_tokens <= (int64_t)w_full * tpc) {
+        const int64_t need = (num_tokens + tpc - 1) / tpc;
+        g.waves_per_tile = need < 1 ? 1 : (int32_t)need;
+        g.chunks_per_wave = 1;
+        g.column_scan = false;
+    } else if (num_tokens <= (int64_t)w_full * kSingleTileChunks * tpc) {
+        g.waves_per_tile = w_full;
+        g.chunks_per_wave = kSingleTileChunks;
+        g.column_scan = false;
+    } else {
+        const int w_mid = clamp_w(kMidTileWaves);
+        g.chunks_per_wave = 1;
+        if (tiles_of(w_mid, 1) * g.hist_stride <= kFromHistMaxInts) {
+            g.waves_per_tile = w_mid;
             g.column_scan = false;
-            break;
-        }
-    }
-    if (g.column_scan)
-    for (g.chunks_per_wave = 1; g.chunks_per_wave <= 8; g.chunks_per_wave *= 2) {
-        const int64_t per_tile = (int64_t)g.waves_per_tile * g.chunks_per_wave * g.tokens_per_chunk;
-        if ((num_tokens + per_tile - 1) / per_tile * g.hist_stride <= kFromHistMaxInts) {
-            g.column_scan = false;
-            break;
+        } else {
+            g.waves_per_tile = w_full;
+            for (int ch = 1; ch <= 8; ch *= 2) {
+                if (tiles_of(w_full, ch) * g.hist_stride <= kFromHistMaxInts) {
+                    g.chunks_per_wave = ch;
+                    g.column_scan = false;
+                    break;
+                }
+            }
         }
     }
     if (g.column_scan) {
