@@ -164,3 +164,18 @@ def test_combine_signed_weights():
     signed = wts * sign
     got = _run_combine(ref.expert_slot, signed, y)
     _check(got, y.view(torch.int16).numpy().view(np.uint16), signed, ref.expert_slot, min_exact=0.98)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_combine_random_problem(seed):
+    """Seeded random combines: tokens, top-k, experts, hidden width, masking."""
+    rng = np.random.default_rng([seed, 91])
+    t = int(rng.choice([1, 33, 500, 3000]))
+    k = int(rng.choice([1, 2, 5, 8, 13, 32]))
+    e = int(rng.choice([32, 64, 256]))
+    hidden = 8 * int(rng.choice([1, 16, 65, 300, 896]))
+    mask = float(rng.choice([0.0, 0.1, 0.6]))
+    _banner(f"random seed={seed} T={t} K={k} E={e} H={hidden} mask={mask}")
+    w, topk, ref, y, wts = _combine_inputs(t, min(k, e), e, hidden, mask, seed=300 + seed)
+    got = _run_combine(ref.expert_slot, wts, y)
+    _check(got, y.view(torch.int16).numpy().view(np.uint16), wts, ref.expert_slot)

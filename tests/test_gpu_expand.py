@@ -202,3 +202,37 @@ def test_expand_empty_and_partial(m, counts):
     ref = oracle.expand_layout(recv_topk, c, 2, m, e, r, 0, 4)
     _, lay, recv_x, _ = _run_expand(recv_topk, recv_buf, None, c, m, e, r, 0, 4)
     _compare(lay, recv_x, None, ref, recv_buf, None)
+
+
+def _draw_expand(seed):
+    rng = np.random.default_rng([seed, 77])
+    r = int(rng.choice([1, 2, 4, 8, 16]))
+    e = r * int(rng.choice([1, 2, 8, 32]))
+    k = int(min(e, rng.choice([1, 2, 4, 8, 9])))
+    s_count = int(rng.choice([1, 2, 5, 8]))
+    t = int(rng.choice([1, 30, 300, 1500]))
+    a = int(rng.choice([1, 1, 3, 16, 128]))
+    rank = int(rng.integers(0, r))
+    hidden = int(rng.choice([64, 512, 2048]))
+    dtype = str(rng.choice(["bf16", "fp8"]))
+    with_sf = dtype == "fp8" and bool(rng.integers(0, 2)) and hidden >= 128
+    mask = float(rng.choice([0.0, 0.1]))
+    slack = int(rng.choice([0, 7]))
+    topk_bytes = int(rng.choice([4, 8]))
+    return s_count, t, hidden, dtype, with_sf, e, r, k, mask, rank, a, slack, topk_bytes
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_expand_random_problem(seed):
+    """Seeded random receivers (sources, rows, top-k, experts, ranks, this
+    rank, alignment, row width, scale factors, slack, table width), each
+    bit-exact against the oracle."""
+    s_count, t, hidden, dtype, with_sf, e, r, k, mask, rank, a, slack, ib = _draw_expand(seed)
+    _banner(f"random seed={seed} S={s_count} T={t} H={hidden} {dtype}{'+sf' if with_sf else ''} E={e} R={r} "
+            f"K={k} rank={rank} A={a} slack={slack} idx={ib}")
+    sources = [_source(5000 + 31 * seed + s, t, hidden, dtype, with_sf, e, r, k, mask) for s in range(s_count)]
+    recv_topk, recv_buf, recv_sf, counts, m = _receive_buffer(sources, e, r, rank, slack=slack, seed=seed)
+    ref = oracle.expand_layout(recv_topk, counts, s_count, m, e, r, rank, a)
+    assert ref.status == 0
+    _, lay, recv_x, recv_sf_out = _run_expand(recv_topk, recv_buf, recv_sf, counts, m, e, r, rank, a, topk_bytes=ib)
+    _compare(lay, recv_x, recv_sf_out, ref, recv_buf, recv_sf)
