@@ -8,8 +8,12 @@
  * (sections 6.2 and 6.4) and the row copies with zero padding (sections 6.3,
  * 7.3 and 8.2). Where the page's kernel lets atomics decide the order inside a
  * bucket, this oracle fixes ascending token order, which makes the result
- * unique. Only tests, the smoke check and the benchmark's CPU baseline may call
- * it; the product path never links or loads it.
+ * unique. Two further steps follow the same page: the receiver-side expand
+ * of a fixed-stride receive buffer (its copy epilogue, sections 3, 6.4 and
+ * 8.2-8.3), in (source, row) order, and the combine that the page's slot map
+ * is kept for (section 6.2), summed in double precision. Only tests, the
+ * smoke check and the benchmark's CPU baseline may call it; the product path
+ * never links or loads it.
  */
 #include "dispatch_oracle.h"
 
