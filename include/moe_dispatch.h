@@ -141,6 +141,9 @@ int dispatch_layout(const dispatch_problem_t* problem, const void* topk_idx,
  *   recv_x [expert_psum[E], row_bytes] and recv_sf [expert_psum[E], S], with
  *   pad rows zeroed under DISPATCH_ZERO_PAD.
  * Copies are bitwise. Writes nothing when the layout's status is non-zero.
+ * One wavefront copies each 1 KB of a row (4 KB when rows have about one
+ * destination), so T * ceil(row_bytes / 1024) must stay below 2^31; larger
+ * problems return DISPATCH_ERR_HIP without launching.
  * A layout may be kept and scattered again, for new rows of the same routing,
  * without recomputing it (the page's cached dispatch, section 6.2). */
 int dispatch_scatter(const dispatch_problem_t* problem, const dispatch_layout_t* layout,

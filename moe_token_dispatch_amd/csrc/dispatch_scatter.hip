@@ -26,7 +26,6 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kScatterWaves = 4;  // wavefronts per 256-thread workgroup
 constexpr int kPadRowsPerWave = 8;
 // V, the 16-byte vectors per lane of one row segment, follows the stores per
 // loaded row (measured on MI355X): with many destinations per row (dispatch:
@@ -35,6 +34,10 @@ constexpr int kPadRowsPerWave = 8;
 // (the receiver-side expand, a top-1 copy) four vectors per lane do.
 constexpr int kVecsManyDestinations = 1;
 constexpr int kVecsFewDestinations = 4;
+// Wavefronts per workgroup, measured the same way: 1 with many destinations
+// per row, 4 with about one.
+constexpr int kWavesManyDestinations = 1;
+constexpr int kWavesFewDestinations = 4;
 
 struct ScatterParams {
     int64_t num_tokens;
@@ -143,8 +146,8 @@ __device__ __forceinline__ void zero_pads(const ScatterParams& p, int64_t pad_wa
     }
 }
 
-template <int V>
-__global__ void __launch_bounds__(kScatterWaves * kWave)
+template <int V, int W>
+__global__ void __launch_bounds__(W * kWave)
 scatter_kernel(const u32x4* __restrict__ x, const uint32_t* __restrict__ x_sf, ScatterParams p,
                const int32_t* __restrict__ expert_slot, const int32_t* __restrict__ rank_slot,
                const int32_t* __restrict__ expert_count, const int32_t* __restrict__ expert_psum,
@@ -152,8 +155,7 @@ scatter_kernel(const u32x4* __restrict__ x, const uint32_t* __restrict__ x_sf, S
                uint32_t* __restrict__ rank_sf, u32x4* __restrict__ recv_x, uint32_t* __restrict__ recv_sf) {
     if (*status != 0) return;  // the layout is unspecified: write nothing
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave_id = (int64_t)blockIdx.x * kScatterWaves +
-                            __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t wave_id = (int64_t)blockIdx.x * W + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (wave_id < p.token_waves) {
         const int64_t t = wave_id / p.segments;
         const int seg = (int)(wave_id - t * p.segments);
@@ -164,15 +166,15 @@ scatter_kernel(const u32x4* __restrict__ x, const uint32_t* __restrict__ x_sf, S
     }
 }
 
-template <int V>
+template <int V, int W>
 hipError_t launch_v(dim3 grid, hipStream_t stream, const u32x4* x, const uint32_t* x_sf, ScatterParams p,
                     const int32_t* expert_slot, const int32_t* rank_slot, const int32_t* expert_count,
                     const int32_t* expert_psum, const int32_t* status, u32x4* rank_x, uint32_t* rank_sf,
                     u32x4* recv_x, uint32_t* recv_sf) {
     void* args[] = {&x, &x_sf, &p, &expert_slot, &rank_slot, &expert_count, &expert_psum,
                     &status, &rank_x, &rank_sf, &recv_x, &recv_sf};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&scatter_kernel<V>), grid,
-                           dim3(kScatterWaves * kWave), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&scatter_kernel<V, W>), grid, dim3(W * kWave), args, 0,
+                           stream);
 }
 
 }  // namespace
@@ -189,8 +191,9 @@ hipError_t launch_scatter(const dispatch_problem_t& prob, const dispatch_layout_
     if (p.segments < 1) p.segments = 1;
     const int64_t seg_vecs = (p.row_vecs + p.segments - 1) / p.segments;
     const int v = (int)((seg_vecs + kWave - 1) / kWave);
+    const int w = few_destinations ? kWavesFewDestinations : kWavesManyDestinations;
     const int64_t waves = prob.num_tokens * p.segments;
-    p.token_waves = (waves + kScatterWaves - 1) / kScatterWaves * kScatterWaves;
+    p.token_waves = (waves + w - 1) / w * w;
     p.recv_capacity = prob.recv_capacity_rows;
     p.rank_capacity = prob.rank_capacity_rows;
     p.num_topk = prob.num_topk;
@@ -201,8 +204,9 @@ hipError_t launch_scatter(const dispatch_problem_t& prob, const dispatch_layout_
     const bool pads = p.write_expert && (prob.flags & DISPATCH_ZERO_PAD) && prob.expert_alignment > 1;
     p.pad_waves_per_expert = pads ? (prob.expert_alignment - 1 + kPadRowsPerWave - 1) / kPadRowsPerWave : 1;
     const int64_t pad_waves = pads ? (int64_t)prob.num_experts * p.pad_waves_per_expert : 0;
-    const int64_t blocks = (p.token_waves + pad_waves + kScatterWaves - 1) / kScatterWaves;
+    const int64_t blocks = (p.token_waves + pad_waves + w - 1) / w;
     if (blocks == 0) return hipSuccess;
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;  // beyond one grid: refused, never truncated
     const dim3 grid((unsigned)blocks);
 
     auto* xs = static_cast<const u32x4*>(x);
@@ -211,17 +215,20 @@ hipError_t launch_scatter(const dispatch_problem_t& prob, const dispatch_layout_
     auto* rsf = reinterpret_cast<uint32_t*>(rank_sf);
     auto* ex = static_cast<u32x4*>(recv_x);
     auto* esf = reinterpret_cast<uint32_t*>(recv_sf);
-#define MOE_DISPATCH_SCATTER_CASE(N)                                                                   \
-    case N:                                                                                            \
-        return launch_v<N>(grid, stream, xs, sfs, p, lay.expert_slot, lay.rank_slot, lay.expert_count, \
-                           lay.expert_psum, lay.status, rx, rsf, ex, esf);
+    if (!few_destinations)  // one vector per lane: v == 1
+        return launch_v<1, kWavesManyDestinations>(grid, stream, xs, sfs, p, lay.expert_slot, lay.rank_slot,
+                                                   lay.expert_count, lay.expert_psum, lay.status, rx, rsf, ex, esf);
+#define MOE_DISPATCH_SCATTER_CASE(N)                                                                       \
+    case N:                                                                                                \
+        return launch_v<N, kWavesFewDestinations>(grid, stream, xs, sfs, p, lay.expert_slot, lay.rank_slot, \
+                                                  lay.expert_count, lay.expert_psum, lay.status, rx, rsf, ex, esf);
     switch (v) {
         MOE_DISPATCH_SCATTER_CASE(1)
         MOE_DISPATCH_SCATTER_CASE(2)
         MOE_DISPATCH_SCATTER_CASE(3)
         default:
-            return launch_v<4>(grid, stream, xs, sfs, p, lay.expert_slot, lay.rank_slot, lay.expert_count,
-                               lay.expert_psum, lay.status, rx, rsf, ex, esf);
+            return launch_v<4, kWavesFewDestinations>(grid, stream, xs, sfs, p, lay.expert_slot, lay.rank_slot,
+                                                      lay.expert_count, lay.expert_psum, lay.status, rx, rsf, ex, esf);
     }
 #undef MOE_DISPATCH_SCATTER_CASE
 }
