@@ -168,47 +168,65 @@ __device__ __forceinline__ void load_entries(const IdxT* __restrict__ topk, int6
     }
 }
 
-// Exclusive scan of n LDS values (each rounded up to a multiple of `align`
-// first) from `in` into `out` by the whole workgroup. Returns the total.
-__device__ int block_exclusive_scan(const int* __restrict__ in, int* __restrict__ out, int n, int align,
-                                    int* __restrict__ scratch) {
+// Two exclusive scans in one pass by the whole workgroup: of in[0, n_a),
+// each value rounded up to a multiple of `align` first, and of in[n_a, n),
+// each starting from 0, both into out. Returns the two totals. `scratch`
+// holds 2 * (wavefronts + 1) ints.
+__device__ int2 block_exclusive_scan2(const int* __restrict__ in, int* __restrict__ out, int n_a, int n, int align,
+                                      int* __restrict__ scratch) {
     const int tid = threadIdx.x, nthreads = blockDim.x;
     const int lane = tid & (kWave - 1), wave = tid / kWave, nwaves = nthreads / kWave;
     const int per = (n + nthreads - 1) / nthreads;
     const int lo = min(n, tid * per), hi = min(n, lo + per);
-    int local = 0;
+    int la = 0, lb = 0;
     for (int i = lo; i < hi; ++i) {
         const int c = in[i];
-        local += align > 1 ? (c + align - 1) / align * align : c;
+        if (i < n_a) la += align > 1 ? (c + align - 1) / align * align : c;
+        else lb += c;
     }
-    // Kogge-Stone inclusive scan across the 64 lanes (6 steps).
-    int incl = local;
+    // Kogge-Stone inclusive scans across the 64 lanes (6 steps).
+    int ia = la, ib = lb;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
-        const int up = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += up;
+        const int ua = __shfl_up(ia, off, kWave);
+        const int ub = __shfl_up(ib, off, kWave);
+        if (lane >= off) {
+            ia += ua;
+            ib += ub;
+        }
     }
-    if (lane == kWave - 1) scratch[wave] = incl;
+    if (lane == kWave - 1) {
+        scratch[2 * wave] = ia;
+        scratch[2 * wave + 1] = ib;
+    }
     __syncthreads();
     if (tid == 0) {
-        int run = 0;
+        int ra = 0, rb = 0;
         for (int w = 0; w < nwaves; ++w) {
-            const int t = scratch[w];
-            scratch[w] = run;
-            run += t;
+            const int ta = scratch[2 * w], tb = scratch[2 * w + 1];
+            scratch[2 * w] = ra;
+            scratch[2 * w + 1] = rb;
+            ra += ta;
+            rb += tb;
         }
-        scratch[nwaves] = run;
+        scratch[2 * nwaves] = ra;
+        scratch[2 * nwaves + 1] = rb;
     }
     __syncthreads();
-    int run = scratch[wave] + incl - local;
+    int ra = scratch[2 * wave] + ia - la, rb = scratch[2 * wave + 1] + ib - lb;
     for (int i = lo; i < hi; ++i) {
         const int c = in[i];
-        out[i] = run;
-        run += align > 1 ? (c + align - 1) / align * align : c;
+        if (i < n_a) {
+            out[i] = ra;
+            ra += align > 1 ? (c + align - 1) / align * align : c;
+        } else {
+            out[i] = rb;
+            rb += c;
+        }
     }
-    const int total = scratch[nwaves];
+    const int2 totals = make_int2(scratch[2 * nwaves], scratch[2 * nwaves + 1]);
     __syncthreads();
-    return total;
+    return totals;
 }
 
 // Workspace views.
@@ -318,7 +336,7 @@ __global__ void __launch_bounds__(kLayoutThreads)
 assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispatch_layout_t out) {
     // LDS: [W][num_keys] wavefront counters, then totals[num_keys] and first[num_keys].
     extern __shared__ int lds[];
-    __shared__ int scratch[kLayoutThreads / kWave + 1];
+    __shared__ int scratch[2 * (kLayoutThreads / kWave + 1)];
     __shared__ uint32_t block_err;
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -350,17 +368,27 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
             first[j] = 0;
         }
         __syncthreads();
+        // A thread's loads of one batch are all issued before the first add,
+        // so a batch costs one memory latency.
+        constexpr int kHistBatch = 16;
         const int quads = p.hist_stride / 4;
         const int groups = nthreads / quads > 1 ? nthreads / quads : 1;
         const i32x4* hist4 = reinterpret_cast<const i32x4*>(ws.tile_hist);
         for (int item = tid; item < quads * groups; item += nthreads) {
             const int q = item % quads, g = item / quads;
             i32x4 tot = {0, 0, 0, 0}, bef = {0, 0, 0, 0};
-#pragma unroll 4
-            for (int i = g; i < p.num_tiles; i += groups) {
-                const i32x4 h = hist4[(int64_t)i * quads + q];
-                tot += h;
-                if (i < tile) bef += h;
+            for (int i0 = g; i0 < p.num_tiles; i0 += groups * kHistBatch) {
+                i32x4 h[kHistBatch];
+#pragma unroll
+                for (int b = 0; b < kHistBatch; ++b) {
+                    const int i = i0 + b * groups;
+                    h[b] = i < p.num_tiles ? hist4[(int64_t)i * quads + q] : (i32x4){0, 0, 0, 0};
+                }
+#pragma unroll
+                for (int b = 0; b < kHistBatch; ++b) {
+                    tot += h[b];
+                    if (i0 + b * groups < tile) bef += h[b];
+                }
             }
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -406,8 +434,8 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
         if (MODE == kSingleTile) totals[j] = run;
     }
     if (MODE == kSingleTile) __syncthreads();
-    const int recv_rows = block_exclusive_scan(totals, first, E, p.alignment, scratch);
-    const int rank_rows = block_exclusive_scan(totals + E, first + E, R, 1, scratch);
+    const int2 rows = block_exclusive_scan2(totals, first, E, nkeys, p.alignment, scratch);
+    const int recv_rows = rows.x, rank_rows = rows.y;
     uint32_t status = block_err;
     if (recv_rows > p.recv_capacity) status |= DISPATCH_STATUS_RECV_OVERFLOW;
     if (rank_rows > p.rank_capacity) status |= DISPATCH_STATUS_RANK_OVERFLOW;
