@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define DISPATCH_ABI_VERSION 1
+#define DISPATCH_ABI_VERSION 2
 
 /* Limits. K <= 32 follows the page's bound on the top-k width (section 4.2);
  * R <= 1024 follows its kNumMaxRanks (section 6.2). */
@@ -102,6 +102,12 @@ typedef struct dispatch_layout {
     int32_t* recv_src_token_idx; /* [recv_capacity_rows] token of each recv_x row, -1 on pads */
     int32_t* rank_src_token_idx; /* [rank_capacity_rows] token of each rank_x row */
     int32_t* status;             /* [1]   DISPATCH_STATUS_* bits, 0 = success */
+    /* Optional (NULL = off), caller-owned and kept across calls: [E] running
+     * totals of expert_count. A call that ends with status 0 adds its
+     * expert_count to it with device atomics, so calls on several streams may
+     * share one array; a failed call adds nothing. The page's cumulative
+     * per-expert receive statistics (section 7.2). */
+    int32_t* expert_count_cumulative;
 } dispatch_layout_t;
 
 /* Version of this ABI (DISPATCH_ABI_VERSION). */
@@ -187,7 +193,8 @@ int dispatch_expand_max_rows(const dispatch_expand_problem_t* problem, int64_t* 
  * expert_count[E/R], expert_psum[E/R+1], expert_slot[S*M*K] (-1 for another
  * rank's expert, a masked entry or an unused row), recv_src_token_idx
  * [recv_capacity_rows] holding the receive-buffer row of each slot (-1 on
- * pads), status (DISPATCH_STATUS_*; BAD_EXPERT for an id >= E, DUP_EXPERT for
+ * pads), the optional expert_count_cumulative[E/R] (the local experts' rows
+ * received over all calls), status (DISPATCH_STATUS_*; BAD_EXPERT for an id >= E, DUP_EXPERT for
  * a local expert twice in a row, BAD_COUNT for a count outside [0, M]). */
 int dispatch_expand_layout(const dispatch_expand_problem_t* problem, const void* recv_topk_idx,
                            const int32_t* recv_count, const dispatch_layout_t* out, void* workspace,

@@ -17,7 +17,7 @@ import torch  # load torch's HIP runtime first so the library binds to the same 
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_dispatch.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 MAX_TOPK = 32
 MAX_EXPERTS = 4096
 MAX_RANKS = 1024
@@ -71,7 +71,7 @@ class LayoutPtrs(ctypes.Structure):
 
     _fields_ = [(name, ctypes.c_void_p) for name in (
         "expert_count", "rank_count", "expert_psum", "rank_psum", "expert_slot", "rank_slot",
-        "recv_src_token_idx", "rank_src_token_idx", "status")]
+        "recv_src_token_idx", "rank_src_token_idx", "status", "expert_count_cumulative")]
 
 
 class ExpandProblem(ctypes.Structure):
@@ -203,10 +203,11 @@ class LayoutTensors:
     rank_src_token_idx: torch.Tensor
     status: torch.Tensor
 
-    def ptrs(self) -> LayoutPtrs:
+    def ptrs(self, expert_count_cumulative: Optional[torch.Tensor] = None) -> LayoutPtrs:
         return LayoutPtrs(*[t.data_ptr() for t in (
             self.expert_count, self.rank_count, self.expert_psum, self.rank_psum, self.expert_slot,
-            self.rank_slot, self.recv_src_token_idx, self.rank_src_token_idx, self.status)])
+            self.rank_slot, self.recv_src_token_idx, self.rank_src_token_idx, self.status)],
+            _ptr(expert_count_cumulative))
 
 
 def _check_device_tensor(t: torch.Tensor, name: str, dtype=None):
@@ -218,16 +219,27 @@ def _check_device_tensor(t: torch.Tensor, name: str, dtype=None):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _check_cumulative(t: Optional[torch.Tensor], num_experts: int) -> None:
+    if t is not None:
+        _check_device_tensor(t, "expert_count_cumulative", torch.int32)
+        if t.numel() < num_experts:
+            raise ValueError(f"expert_count_cumulative needs {num_experts} entries, has {t.numel()}")
+
+
 def dispatch_layout(problem: Problem, topk_idx: torch.Tensor, out: LayoutTensors,
-                    workspace: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -> None:
-    """Enqueue Count -> Prefix Sum -> slot assignment on the stream."""
+                    workspace: torch.Tensor, stream: Optional[torch.cuda.Stream] = None,
+                    expert_count_cumulative: Optional[torch.Tensor] = None) -> None:
+    """Enqueue Count -> Prefix Sum -> slot assignment on the stream. When
+    ``expert_count_cumulative`` (device int32 [E], kept by the caller) is given,
+    a successful call adds its expert_count to it."""
     _check_device_tensor(topk_idx, "topk_idx")
     if topk_idx.element_size() != problem.topk_idx_bytes:
         raise ValueError("topk_idx element width does not match problem.topk_idx_bytes")
     _check_device_tensor(workspace, "workspace")
     for f in dataclasses.fields(out):
         _check_device_tensor(getattr(out, f.name), f.name, torch.int32)
-    lay = out.ptrs()
+    _check_cumulative(expert_count_cumulative, problem.num_experts)
+    lay = out.ptrs(expert_count_cumulative)
     rc = load_library().dispatch_layout(ctypes.byref(problem), _ptr(topk_idx), ctypes.byref(lay),
                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
                                         _stream_handle(stream, topk_idx.device))
@@ -324,16 +336,18 @@ class Plan:
     def __init__(self, problem: Problem, topk_idx: torch.Tensor, layout: LayoutTensors,
                  workspace: torch.Tensor, x: Optional[torch.Tensor] = None,
                  x_sf: Optional[torch.Tensor] = None, rows: Optional[RowBuffers] = None,
-                 stream: Optional[torch.cuda.Stream] = None):
+                 stream: Optional[torch.cuda.Stream] = None,
+                 expert_count_cumulative: Optional[torch.Tensor] = None):
         _check_device_tensor(topk_idx, "topk_idx")
         if topk_idx.element_size() != problem.topk_idx_bytes:
             raise ValueError("topk_idx element width does not match problem.topk_idx_bytes")
         _check_device_tensor(workspace, "workspace")
         for f in dataclasses.fields(layout):
             _check_device_tensor(getattr(layout, f.name), f.name, torch.int32)
+        _check_cumulative(expert_count_cumulative, problem.num_experts)
         self._lib = load_library()
-        self._keep = (problem, topk_idx, layout, workspace, x, x_sf, rows)
-        self._lay = layout.ptrs()
+        self._keep = (problem, topk_idx, layout, workspace, x, x_sf, rows, expert_count_cumulative)
+        self._lay = layout.ptrs(expert_count_cumulative)
         handle = _stream_handle(stream, topk_idx.device)
         self._layout_args = (ctypes.byref(problem), _ptr(topk_idx), ctypes.byref(self._lay), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), handle)
@@ -404,10 +418,10 @@ class ExpandLayoutTensors:
     recv_src_row_idx: torch.Tensor    # [recv_capacity_rows]
     status: torch.Tensor              # [1]
 
-    def ptrs(self) -> LayoutPtrs:
+    def ptrs(self, expert_count_cumulative: Optional[torch.Tensor] = None) -> LayoutPtrs:
         return LayoutPtrs(self.expert_count.data_ptr(), None, self.expert_psum.data_ptr(), None,
                           self.expert_slot.data_ptr(), None, self.recv_src_row_idx.data_ptr(), None,
-                          self.status.data_ptr())
+                          self.status.data_ptr(), _ptr(expert_count_cumulative))
 
 
 def alloc_expand_layout(problem: ExpandProblem, device) -> ExpandLayoutTensors:
@@ -428,8 +442,11 @@ def alloc_expand_workspace(problem: ExpandProblem, device) -> torch.Tensor:
 
 def dispatch_expand_layout(problem: ExpandProblem, recv_topk_idx: torch.Tensor, recv_count: torch.Tensor,
                            out: ExpandLayoutTensors, workspace: torch.Tensor,
-                           stream: Optional[torch.cuda.Stream] = None) -> None:
-    """Enqueue the receiver's expert-major layout of a receive buffer."""
+                           stream: Optional[torch.cuda.Stream] = None,
+                           expert_count_cumulative: Optional[torch.Tensor] = None) -> None:
+    """Enqueue the receiver's expert-major layout of a receive buffer. When
+    ``expert_count_cumulative`` (device int32 [E/R], kept by the caller) is
+    given, a successful call adds the local experts' received rows to it."""
     _check_device_tensor(recv_topk_idx, "recv_topk_idx")
     if recv_topk_idx.element_size() != problem.topk_idx_bytes:
         raise ValueError("recv_topk_idx element width does not match problem.topk_idx_bytes")
@@ -437,7 +454,8 @@ def dispatch_expand_layout(problem: ExpandProblem, recv_topk_idx: torch.Tensor, 
     _check_device_tensor(workspace, "workspace")
     for f in dataclasses.fields(out):
         _check_device_tensor(getattr(out, f.name), f.name, torch.int32)
-    lay = out.ptrs()
+    _check_cumulative(expert_count_cumulative, problem.num_experts // problem.num_ranks)
+    lay = out.ptrs(expert_count_cumulative)
     rc = load_library().dispatch_expand_layout(
         ctypes.byref(problem), _ptr(recv_topk_idx), _ptr(recv_count), ctypes.byref(lay), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream_handle(stream, recv_topk_idx.device))

@@ -150,7 +150,7 @@ int dispatch_layout(const dispatch_problem_t* problem, const void* topk_idx, con
     if (topk_idx && !aligned_to(topk_idx, p.topk_idx_bytes)) return DISPATCH_ERR_ALIGN;
     const void* ints[] = {out->expert_count, out->rank_count, out->expert_psum, out->rank_psum,
                           out->expert_slot, out->rank_slot, out->recv_src_token_idx,
-                          out->rank_src_token_idx, out->status};
+                          out->rank_src_token_idx, out->status, out->expert_count_cumulative};
     for (const void* q : ints)
         if (q && !aligned_to(q, 4)) return DISPATCH_ERR_ALIGN;
     if (!aligned_to(workspace, 256)) return DISPATCH_ERR_WORKSPACE;
@@ -208,7 +208,7 @@ int dispatch_expand_layout(const dispatch_expand_problem_t* problem, const void*
     if (workspace == nullptr) return DISPATCH_ERR_WORKSPACE;
     if (recv_topk_idx && !aligned_to(recv_topk_idx, p.topk_idx_bytes)) return DISPATCH_ERR_ALIGN;
     const void* ints[] = {recv_count, out->expert_count, out->expert_psum, out->expert_slot,
-                          out->recv_src_token_idx, out->status};
+                          out->recv_src_token_idx, out->status, out->expert_count_cumulative};
     for (const void* q : ints)
         if (q && !aligned_to(q, 4)) return DISPATCH_ERR_ALIGN;
     if (!aligned_to(workspace, 256)) return DISPATCH_ERR_WORKSPACE;

@@ -450,6 +450,10 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
                 out.rank_psum[j - E] = first[j];
             }
         }
+        // Running per-expert totals over calls, when asked for (section 7.2's
+        // receive statistics): atomics, so concurrent calls may share them.
+        if (status == 0 && out.expert_count_cumulative)
+            for (int j = tid; j < E; j += nthreads) atomicAdd(&out.expert_count_cumulative[j], totals[j]);
         if (tid == 0) {
             out.expert_psum[E] = recv_rows;
             if (out.rank_psum) out.rank_psum[R] = rank_rows;

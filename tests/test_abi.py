@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_binding_constants_match_header():
     d = _defines()
-    assert d["DISPATCH_ABI_VERSION"] == M.dispatch_abi_version() == 1
+    assert d["DISPATCH_ABI_VERSION"] == M.dispatch_abi_version() == 2
     assert (d["DISPATCH_ERR_NULL"], d["DISPATCH_ERR_ARG"], d["DISPATCH_ERR_ALIGN"],
             d["DISPATCH_ERR_WORKSPACE"], d["DISPATCH_ERR_HIP"]) == (
         M.ERR_NULL, M.ERR_ARG, M.ERR_ALIGN, M.ERR_WORKSPACE, M.ERR_HIP)
@@ -47,7 +47,7 @@ def test_binding_constants_match_header():
         M.RANK_CONTIG, M.EXPERT_MAJOR, M.ZERO_PAD)
     assert d["DISPATCH_MAX_TOPK"] == M.MAX_TOPK and d["DISPATCH_MAX_EXPERTS"] == M.MAX_EXPERTS
     assert d["DISPATCH_MAX_RANKS"] == M.MAX_RANKS
-    assert ctypes.sizeof(M.Problem) == 64 and ctypes.sizeof(M.LayoutPtrs) == 9 * 8
+    assert ctypes.sizeof(M.Problem) == 64 and ctypes.sizeof(M.LayoutPtrs) == 10 * 8
 
 
 def test_strerror_covers_codes():
@@ -111,6 +111,9 @@ def test_host_errors_before_launch():
     assert call(p, 4100, good, 4096, ws_need) == M.ERR_ALIGN  # int64 table not 8-byte aligned
     lay = M.LayoutPtrs(*([4096] * 9))
     lay.expert_slot = 4098
+    assert call(p, 4096, lay, 4096, ws_need) == M.ERR_ALIGN
+    lay = M.LayoutPtrs(*([4096] * 9))
+    lay.expert_count_cumulative = 4098  # optional, but 4-byte aligned when given
     assert call(p, 4096, lay, 4096, ws_need) == M.ERR_ALIGN
     assert call(p, 4096, good, None, ws_need) == M.ERR_WORKSPACE
     assert call(p, 4096, good, 4096 + 64, ws_need) == M.ERR_WORKSPACE  # not 256-byte aligned

@@ -236,3 +236,21 @@ def test_expand_random_problem(seed):
     assert ref.status == 0
     _, lay, recv_x, recv_sf_out = _run_expand(recv_topk, recv_buf, recv_sf, counts, m, e, r, rank, a, topk_bytes=ib)
     _compare(lay, recv_x, recv_sf_out, ref, recv_buf, recv_sf)
+
+
+def test_expand_expert_count_cumulative():
+    """Running totals of the local experts' received rows over calls."""
+    _banner("expand expert_count_cumulative")
+    e, r, k, rank, a = 64, 4, 8, 2, 2
+    sources = [_source(60 + s, 300, 64, "bf16", False, e, r, k, 0.05) for s in range(3)]
+    recv_topk, recv_buf, recv_sf, counts, m = _receive_buffer(sources, e, r, rank, 5, 61)
+    q = M.make_expand_problem(3, m, k, e, r, rank, a, 8, recv_buf.shape[1], 0)
+    lay, ws = M.alloc_expand_layout(q, H.DEVICE), M.alloc_expand_workspace(q, H.DEVICE)
+    ref = oracle.expand_layout(recv_topk, counts, 3, m, e, r, rank, a)
+    assert ref.status == 0
+    cum = torch.full((e // r,), 5, dtype=torch.int32, device=H.DEVICE)
+    topk_d, counts_d = torch.from_numpy(recv_topk).to(H.DEVICE), torch.from_numpy(counts).to(H.DEVICE)
+    for _ in range(2):
+        M.dispatch_expand_layout(q, topk_d, counts_d, lay, ws, expert_count_cumulative=cum)
+    torch.cuda.synchronize()
+    assert np.array_equal(cum.cpu().numpy(), 5 + 2 * ref.expert_count.astype(np.int64))

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import moe_token_dispatch_amd as M
 import oracle
 import workloads as W
 from tests import gpu_harness as H
@@ -246,3 +247,34 @@ def test_replay_scatter_with_saved_layout():
         assert np.array_equal(run.rows.rank_sf[:n_rank].cpu().numpy().view(np.int32), want.rank_sf.view(np.int32))
         for name, t in saved.items():
             assert torch.equal(getattr(run.layout, name), t), f"scatter changed layout field {name}"
+
+
+def test_expert_count_cumulative_adds_successful_calls():
+    """The optional running per-expert totals: each call that ends with status 0
+    adds its expert_count (before alignment); a failed call adds nothing."""
+    _banner("expert_count_cumulative")
+    e, r, k, t, a = 64, 8, 6, 700, 4
+    prob = M.make_problem(t, k, e, r, a, 8, 16, 0)
+    lay, ws = M.alloc_layout(prob, H.DEVICE), M.alloc_workspace(prob, H.DEVICE)
+    start = (np.arange(e, dtype=np.int64) * 3 - 50).astype(np.int32)  # any values the caller holds
+    cum = torch.from_numpy(start).to(H.DEVICE)
+    want = start.astype(np.int64)
+    for seed in (41, 42, 43):
+        topk = _uniform(seed, t, k, e, 0.1)
+        M.dispatch_layout(prob, torch.from_numpy(topk).to(H.DEVICE), lay, ws, expert_count_cumulative=cum)
+        want += oracle.layout(topk, e, r, a).expert_count
+    bad = _uniform(44, t, k, e)
+    bad[5, 1] = e
+    M.dispatch_layout(prob, torch.from_numpy(bad).to(H.DEVICE), lay, ws, expert_count_cumulative=cum)
+    torch.cuda.synchronize()
+    assert int(lay.status.item()) == oracle.BAD_EXPERT
+    assert np.array_equal(cum.cpu().numpy(), want)
+    # Through a prepared plan as well: one more successful call.
+    topk = _uniform(45, t, k, e, 0.1)
+    plan = M.Plan(prob, torch.from_numpy(topk).to(H.DEVICE), lay, ws, expert_count_cumulative=cum)
+    plan.layout()
+    torch.cuda.synchronize()
+    assert np.array_equal(cum.cpu().numpy(), want + oracle.layout(topk, e, r, a).expert_count)
+    with pytest.raises(ValueError):
+        M.dispatch_layout(prob, torch.from_numpy(topk).to(H.DEVICE), lay, ws,
+                          expert_count_cumulative=cum[:e - 1])
