@@ -28,9 +28,11 @@ int check_problem(const dispatch_problem_t* p) {
     if (p->sf_per_token < 0) return DISPATCH_ERR_ARG;
     if (p->recv_capacity_rows < 0 || p->rank_capacity_rows < 0) return DISPATCH_ERR_ARG;
     if ((p->flags & ~uint32_t(DISPATCH_ALL_OUTPUTS)) != 0 || p->reserved != 0) return DISPATCH_ERR_ARG;
-    // Slots and row counts are int32: the worst case must fit.
+    // Slots and row counts are int32: the worst case must fit (T is bounded
+    // first, so the product below cannot overflow).
+    if (p->num_tokens > INT32_MAX) return DISPATCH_ERR_ARG;
     const int64_t worst = p->num_tokens * p->num_topk + int64_t(p->num_experts) * (p->expert_alignment - 1);
-    if (p->num_tokens > INT32_MAX || worst > INT32_MAX) return DISPATCH_ERR_ARG;
+    if (worst > INT32_MAX) return DISPATCH_ERR_ARG;
     return DISPATCH_OK;
 }
 
@@ -93,7 +95,6 @@ int scatter_checked(const dispatch_problem_t* problem, const dispatch_layout_t* 
         return DISPATCH_ERR_HIP;
     return DISPATCH_OK;
 }
-
 
 }  // namespace
 

@@ -76,6 +76,7 @@ BAD_PROBLEMS = [
     dict(expert_alignment=0), dict(topk_idx_bytes=2), dict(sf_per_token=-1), dict(flags=8),
     dict(recv_capacity_rows=-1), dict(reserved=1), dict(num_tokens=1 << 31),
     dict(num_tokens=1 << 28, expert_alignment=1 << 20),
+    dict(num_tokens=(1 << 62) + 1),  # rejected before T * K is formed
 ]
 
 
