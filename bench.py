@@ -560,6 +560,11 @@ def main():
                "scatter_ms": round(med_sc * 1e3, 2), "pinned_to_one_core": True, "host": host_cpu()}
 
     ceiling = measure_device_ceiling(torch)
+    # The step and the scatter against the practical ceilings measured on the
+    # same box (torch's own device copy and fill), beside the published peak.
+    ceiling["step_frac_of_copy"] = round(value / ceiling["copy_GBps"], 4)
+    ceiling["step_frac_of_fill"] = round(value / ceiling["fill_GBps"], 4)
+    ceiling["scatter_frac_of_fill"] = round(achieved / ceiling["fill_GBps"], 4)
     out = {
         "metric": METRIC,
         "value": round(value, 1),
