@@ -156,6 +156,28 @@ int dispatch_scatter(const dispatch_problem_t* problem, const dispatch_layout_t*
                      const void* x, const float* x_sf, void* rank_x, float* rank_sf,
                      void* recv_x, float* recv_sf, hipStream_t stream);
 
+/* dispatch_layout followed by dispatch_scatter in one call, with the same
+ * arguments, checks, outputs and status semantics as those two calls made in
+ * turn. A batch that fits one layout tile (T * K up to 2048 pairs, fewer when
+ * E + R is large) is laid out and copied by a single kernel: every workgroup
+ * ranks the whole batch itself, so none waits for another, and each copies
+ * its share of the rows' 1 KB segments. That saves a launch, the dominant
+ * cost of small (decode-sized) batches. Larger batches run the layout and
+ * scatter kernels. */
+int dispatch_layout_and_scatter(const dispatch_problem_t* problem, const void* topk_idx,
+                                const dispatch_layout_t* out, void* workspace, size_t workspace_bytes,
+                                const void* x, const float* x_sf, void* rank_x, float* rank_sf,
+                                void* recv_x, float* recv_sf, hipStream_t stream);
+
+/* Kernels the calls above launch for this problem (its T, K, E, R and
+ * row_bytes are read): *layout_kernels for dispatch_layout (1 when one tile
+ * holds the batch, 2 with the tile histograms reduced in the assign kernel, 3
+ * with the column scan) and *layout_and_scatter_kernels for
+ * dispatch_layout_and_scatter (1 on its one-kernel path, else the layout's
+ * kernels plus the scatter). Either pointer may be NULL. */
+int dispatch_kernel_count(const dispatch_problem_t* problem, int* layout_kernels,
+                          int* layout_and_scatter_kernels);
+
 /* ---------------------------------------------------------------------------
  * Receiver-side expand (the page's copy epilogue: sections 3, 6.4, 8.2, 8.3
  * and 12). A receiver rank holds the rows S source ranks sent it in a receive

@@ -109,7 +109,8 @@ _LIB = None
 
 # Exported symbols of include/moe_dispatch.h.
 SYMBOLS = ("dispatch_abi_version", "dispatch_strerror", "dispatch_workspace_size",
-           "dispatch_max_rows", "dispatch_layout", "dispatch_scatter",
+           "dispatch_max_rows", "dispatch_layout", "dispatch_scatter", "dispatch_layout_and_scatter",
+           "dispatch_kernel_count",
            "dispatch_expand_workspace_size", "dispatch_expand_max_rows", "dispatch_expand_layout",
            "dispatch_expand_scatter", "dispatch_combine")
 
@@ -136,6 +137,11 @@ def load_library(path: str = LIB_PATH):
     lib.dispatch_layout.restype = i
     lib.dispatch_scatter.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(LayoutPtrs), p, p, p, p, p, p, p]
     lib.dispatch_scatter.restype = i
+    lib.dispatch_layout_and_scatter.argtypes = [ctypes.POINTER(Problem), p, ctypes.POINTER(LayoutPtrs), p, sz,
+                                                p, p, p, p, p, p, p]
+    lib.dispatch_layout_and_scatter.restype = i
+    lib.dispatch_kernel_count.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(i), ctypes.POINTER(i)]
+    lib.dispatch_kernel_count.restype = i
     ep = ctypes.POINTER(ExpandProblem)
     lib.dispatch_expand_workspace_size.argtypes = [ep, ctypes.POINTER(sz)]
     lib.dispatch_expand_workspace_size.restype = i
@@ -265,6 +271,44 @@ def dispatch_scatter(problem: Problem, layout: LayoutTensors, x: torch.Tensor,
         raise DispatchError(rc, "dispatch_scatter")
 
 
+def dispatch_kernel_count(problem: Problem) -> tuple:
+    """(kernels of dispatch_layout, kernels of dispatch_layout_and_scatter) for this problem."""
+    lay, both = ctypes.c_int(0), ctypes.c_int(0)
+    rc = load_library().dispatch_kernel_count(ctypes.byref(problem), ctypes.byref(lay), ctypes.byref(both))
+    if rc:
+        raise DispatchError(rc, "dispatch_kernel_count")
+    return lay.value, both.value
+
+
+def dispatch_layout_and_scatter(problem: Problem, topk_idx: torch.Tensor, out: LayoutTensors,
+                                workspace: torch.Tensor, x: torch.Tensor, x_sf: Optional[torch.Tensor],
+                                rank_x: Optional[torch.Tensor], rank_sf: Optional[torch.Tensor],
+                                recv_x: Optional[torch.Tensor], recv_sf: Optional[torch.Tensor],
+                                stream: Optional[torch.cuda.Stream] = None,
+                                expert_count_cumulative: Optional[torch.Tensor] = None) -> None:
+    """Enqueue dispatch_layout then dispatch_scatter as one call (one kernel
+    for a batch that fits one layout tile)."""
+    _check_device_tensor(topk_idx, "topk_idx")
+    if topk_idx.element_size() != problem.topk_idx_bytes:
+        raise ValueError("topk_idx element width does not match problem.topk_idx_bytes")
+    _check_device_tensor(workspace, "workspace")
+    for f in dataclasses.fields(out):
+        _check_device_tensor(getattr(out, f.name), f.name, torch.int32)
+    _check_cumulative(expert_count_cumulative, problem.num_experts)
+    _check_device_tensor(x, "x")
+    for name, t in (("x_sf", x_sf), ("rank_x", rank_x), ("rank_sf", rank_sf), ("recv_x", recv_x),
+                    ("recv_sf", recv_sf)):
+        if t is not None:
+            _check_device_tensor(t, name)
+    lay = out.ptrs(expert_count_cumulative)
+    rc = load_library().dispatch_layout_and_scatter(
+        ctypes.byref(problem), _ptr(topk_idx), ctypes.byref(lay), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(x), _ptr(x_sf), _ptr(rank_x), _ptr(rank_sf),
+        _ptr(recv_x), _ptr(recv_sf), _stream_handle(stream, topk_idx.device))
+    if rc:
+        raise DispatchError(rc, "dispatch_layout_and_scatter")
+
+
 # ------------------------------------------------- allocation helpers (plumbing)
 
 
@@ -329,8 +373,9 @@ class Plan:
     once and the C arguments are built once, so each call is a single C call.
 
     ``layout()`` enqueues dispatch_layout, ``scatter()`` enqueues
-    dispatch_scatter, ``__call__`` does both. The tensors must stay alive and
-    keep their storage while the plan is used.
+    dispatch_scatter, ``__call__`` enqueues both as one
+    dispatch_layout_and_scatter call. The tensors must stay alive and keep
+    their storage while the plan is used.
     """
 
     def __init__(self, problem: Problem, topk_idx: torch.Tensor, layout: LayoutTensors,
@@ -351,7 +396,7 @@ class Plan:
         handle = _stream_handle(stream, topk_idx.device)
         self._layout_args = (ctypes.byref(problem), _ptr(topk_idx), ctypes.byref(self._lay), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), handle)
-        self._scatter_args = None
+        self._scatter_args = self._both_args = None
         if x is not None:
             _check_device_tensor(x, "x")
             rows = rows if rows is not None else RowBuffers(None, None, None, None)
@@ -361,9 +406,10 @@ class Plan:
                     _check_device_tensor(t, name)
             if x_sf is not None:
                 _check_device_tensor(x_sf, "x_sf")
-            self._scatter_args = (ctypes.byref(problem), ctypes.byref(self._lay), _ptr(x), _ptr(x_sf),
-                                  _ptr(rows.rank_x), _ptr(rows.rank_sf), _ptr(rows.recv_x), _ptr(rows.recv_sf),
-                                  handle)
+            row_ptrs = (_ptr(x), _ptr(x_sf), _ptr(rows.rank_x), _ptr(rows.rank_sf), _ptr(rows.recv_x),
+                        _ptr(rows.recv_sf))
+            self._scatter_args = (ctypes.byref(problem), ctypes.byref(self._lay), *row_ptrs, handle)
+            self._both_args = (*self._layout_args[:-1], *row_ptrs, handle)
 
     def layout(self) -> None:
         rc = self._lib.dispatch_layout(*self._layout_args)
@@ -378,8 +424,11 @@ class Plan:
             raise DispatchError(rc, "dispatch_scatter")
 
     def __call__(self) -> None:
-        self.layout()
-        self.scatter()
+        if self._scatter_args is None:
+            raise ValueError("this plan has no token batch to scatter")
+        rc = self._lib.dispatch_layout_and_scatter(*self._both_args)
+        if rc:
+            raise DispatchError(rc, "dispatch_layout_and_scatter")
 
 
 # ------------------------------------------------------------ receiver-side expand

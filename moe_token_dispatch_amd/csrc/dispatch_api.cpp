@@ -61,14 +61,9 @@ int check_expand(const dispatch_expand_problem_t* q, dispatch_problem_t* p) {
     return check_problem(p);
 }
 
-// Host checks and launch of the row scatter. few_destinations: rows go to
-// about one destination each (the receiver-side expand, a top-1 expert copy).
-int scatter_checked(const dispatch_problem_t* problem, const dispatch_layout_t* layout, const void* x,
-                    const float* x_sf, void* rank_x, float* rank_sf, void* recv_x, float* recv_sf,
-                    hipStream_t stream, bool few_destinations) {
-    int rc = check_problem(problem);
-    if (rc != DISPATCH_OK) return rc;
-    const dispatch_problem_t& p = *problem;
+// Host checks of a row scatter's arguments (the problem already checked).
+int check_scatter_args(const dispatch_problem_t& p, const dispatch_layout_t* layout, const void* x,
+                       const float* x_sf, void* rank_x, float* rank_sf, void* recv_x, float* recv_sf) {
     if (p.row_bytes <= 0 || p.row_bytes > INT32_MAX) return DISPATCH_ERR_ARG;
     if (p.row_bytes % 16 != 0) return DISPATCH_ERR_ALIGN;
     if (layout == nullptr || !layout->status || !layout->expert_count || !layout->expert_psum)
@@ -89,10 +84,56 @@ int scatter_checked(const dispatch_problem_t* problem, const dispatch_layout_t* 
                            layout->expert_count, layout->expert_psum, layout->status};
     for (const void* q : words)
         if (q && !aligned_to(q, 4)) return DISPATCH_ERR_ALIGN;
+    return DISPATCH_OK;
+}
 
-    if (moe_dispatch::launch_scatter(p, *layout, x, x_sf, rank_x, rank_sf, recv_x, recv_sf, stream,
+// Host checks and launch of the row scatter. few_destinations: rows go to
+// about one destination each (the receiver-side expand, a top-1 expert copy).
+int scatter_checked(const dispatch_problem_t* problem, const dispatch_layout_t* layout, const void* x,
+                    const float* x_sf, void* rank_x, float* rank_sf, void* recv_x, float* recv_sf,
+                    hipStream_t stream, bool few_destinations) {
+    int rc = check_problem(problem);
+    if (rc != DISPATCH_OK) return rc;
+    rc = check_scatter_args(*problem, layout, x, x_sf, rank_x, rank_sf, recv_x, recv_sf);
+    if (rc != DISPATCH_OK) return rc;
+    if (moe_dispatch::launch_scatter(*problem, *layout, x, x_sf, rank_x, rank_sf, recv_x, recv_sf, stream,
                                      few_destinations) != hipSuccess)
         return DISPATCH_ERR_HIP;
+    return DISPATCH_OK;
+}
+
+// Destinations per loaded row of a dispatch: K expert rows and one rank row
+// at most.
+bool has_few_destinations(const dispatch_problem_t& p) {
+    const int experts = (p.flags & DISPATCH_EXPERT_MAJOR) ? p.num_topk : 0;
+    const int ranks = (p.flags & DISPATCH_RANK_CONTIG) ? 1 : 0;
+    return experts + ranks <= 1;
+}
+
+// Host checks of a layout call's arguments; on success *g is its geometry.
+int check_layout_args(const dispatch_problem_t* problem, const void* topk_idx, const dispatch_layout_t* out,
+                      void* workspace, size_t workspace_bytes, TileGeometry* g) {
+    int rc = check_problem(problem);
+    if (rc != DISPATCH_OK) return rc;
+    const dispatch_problem_t& p = *problem;
+    if (out == nullptr) return DISPATCH_ERR_NULL;
+    if (!out->expert_count || !out->rank_count || !out->expert_psum || !out->rank_psum || !out->status)
+        return DISPATCH_ERR_NULL;
+    if (p.num_tokens > 0 && (!topk_idx || !out->expert_slot || !out->rank_slot)) return DISPATCH_ERR_NULL;
+    if (p.recv_capacity_rows > 0 && !out->recv_src_token_idx) return DISPATCH_ERR_NULL;
+    if (p.rank_capacity_rows > 0 && !out->rank_src_token_idx) return DISPATCH_ERR_NULL;
+    if (workspace == nullptr) return DISPATCH_ERR_WORKSPACE;
+
+    if (topk_idx && !aligned_to(topk_idx, p.topk_idx_bytes)) return DISPATCH_ERR_ALIGN;
+    const void* ints[] = {out->expert_count, out->rank_count, out->expert_psum, out->rank_psum,
+                          out->expert_slot, out->rank_slot, out->recv_src_token_idx,
+                          out->rank_src_token_idx, out->status, out->expert_count_cumulative};
+    for (const void* q : ints)
+        if (q && !aligned_to(q, 4)) return DISPATCH_ERR_ALIGN;
+    if (!aligned_to(workspace, 256)) return DISPATCH_ERR_WORKSPACE;
+
+    *g = moe_dispatch::make_geometry(p.num_tokens, p.num_topk, p.num_experts, p.num_ranks);
+    if (workspace_bytes < moe_dispatch::workspace_bytes(*g)) return DISPATCH_ERR_WORKSPACE;
     return DISPATCH_OK;
 }
 
@@ -137,29 +178,45 @@ int dispatch_max_rows(const dispatch_problem_t* problem, int64_t* max_recv_rows,
 
 int dispatch_layout(const dispatch_problem_t* problem, const void* topk_idx, const dispatch_layout_t* out,
                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    int rc = check_problem(problem);
+    TileGeometry g;
+    const int rc = check_layout_args(problem, topk_idx, out, workspace, workspace_bytes, &g);
+    if (rc != DISPATCH_OK) return rc;
+    if (moe_dispatch::launch_layout(*problem, g, topk_idx, *out, workspace, stream) != hipSuccess)
+        return DISPATCH_ERR_HIP;
+    return DISPATCH_OK;
+}
+
+int dispatch_kernel_count(const dispatch_problem_t* problem, int* layout_kernels, int* layout_and_scatter_kernels) {
+    const int rc = check_problem(problem);
+    if (rc != DISPATCH_OK) return rc;
+    const TileGeometry g = moe_dispatch::make_geometry(problem->num_tokens, problem->num_topk,
+                                                       problem->num_experts, problem->num_ranks);
+    const int layout = g.num_tiles == 1 && !g.column_scan ? 1 : (g.column_scan ? 3 : 2);
+    if (layout_kernels) *layout_kernels = layout;
+    if (layout_and_scatter_kernels)
+        *layout_and_scatter_kernels = moe_dispatch::fused_shape(g, problem->row_bytes).fits ? 1 : layout + 1;
+    return DISPATCH_OK;
+}
+
+int dispatch_layout_and_scatter(const dispatch_problem_t* problem, const void* topk_idx,
+                                const dispatch_layout_t* out, void* workspace, size_t workspace_bytes,
+                                const void* x, const float* x_sf, void* rank_x, float* rank_sf, void* recv_x,
+                                float* recv_sf, hipStream_t stream) {
+    TileGeometry g;
+    int rc = check_layout_args(problem, topk_idx, out, workspace, workspace_bytes, &g);
+    if (rc != DISPATCH_OK) return rc;
+    rc = check_scatter_args(*problem, out, x, x_sf, rank_x, rank_sf, recv_x, recv_sf);
     if (rc != DISPATCH_OK) return rc;
     const dispatch_problem_t& p = *problem;
-    if (out == nullptr) return DISPATCH_ERR_NULL;
-    if (!out->expert_count || !out->rank_count || !out->expert_psum || !out->rank_psum || !out->status)
-        return DISPATCH_ERR_NULL;
-    if (p.num_tokens > 0 && (!topk_idx || !out->expert_slot || !out->rank_slot)) return DISPATCH_ERR_NULL;
-    if (p.recv_capacity_rows > 0 && !out->recv_src_token_idx) return DISPATCH_ERR_NULL;
-    if (p.rank_capacity_rows > 0 && !out->rank_src_token_idx) return DISPATCH_ERR_NULL;
-    if (workspace == nullptr) return DISPATCH_ERR_WORKSPACE;
-
-    if (topk_idx && !aligned_to(topk_idx, p.topk_idx_bytes)) return DISPATCH_ERR_ALIGN;
-    const void* ints[] = {out->expert_count, out->rank_count, out->expert_psum, out->rank_psum,
-                          out->expert_slot, out->rank_slot, out->recv_src_token_idx,
-                          out->rank_src_token_idx, out->status, out->expert_count_cumulative};
-    for (const void* q : ints)
-        if (q && !aligned_to(q, 4)) return DISPATCH_ERR_ALIGN;
-    if (!aligned_to(workspace, 256)) return DISPATCH_ERR_WORKSPACE;
-
-    const TileGeometry g = moe_dispatch::make_geometry(p.num_tokens, p.num_topk, p.num_experts, p.num_ranks);
-    if (workspace_bytes < moe_dispatch::workspace_bytes(g)) return DISPATCH_ERR_WORKSPACE;
-
-    if (moe_dispatch::launch_layout(p, g, topk_idx, *out, workspace, stream) != hipSuccess)
+    if (moe_dispatch::fused_shape(g, p.row_bytes).fits) {
+        if (moe_dispatch::launch_fused_dispatch(p, g, topk_idx, *out, workspace, x, x_sf, rank_x, rank_sf, recv_x,
+                                                recv_sf, stream) != hipSuccess)
+            return DISPATCH_ERR_HIP;
+        return DISPATCH_OK;
+    }
+    if (moe_dispatch::launch_layout(p, g, topk_idx, *out, workspace, stream) != hipSuccess ||
+        moe_dispatch::launch_scatter(p, *out, x, x_sf, rank_x, rank_sf, recv_x, recv_sf, stream,
+                                     has_few_destinations(p)) != hipSuccess)
         return DISPATCH_ERR_HIP;
     return DISPATCH_OK;
 }
@@ -168,13 +225,8 @@ int dispatch_layout(const dispatch_problem_t* problem, const void* topk_idx, con
 int dispatch_scatter(const dispatch_problem_t* problem, const dispatch_layout_t* layout, const void* x,
                      const float* x_sf, void* rank_x, float* rank_sf, void* recv_x, float* recv_sf,
                      hipStream_t stream) {
-    // Destinations per row: K expert rows and one rank row at most.
-    int dests = 0;
-    if (problem != nullptr) {
-        if (problem->flags & DISPATCH_EXPERT_MAJOR) dests += problem->num_topk;
-        if (problem->flags & DISPATCH_RANK_CONTIG) dests += 1;
-    }
-    return scatter_checked(problem, layout, x, x_sf, rank_x, rank_sf, recv_x, recv_sf, stream, dests <= 1);
+    const bool few = problem != nullptr && has_few_destinations(*problem);
+    return scatter_checked(problem, layout, x, x_sf, rank_x, rank_sf, recv_x, recv_sf, stream, few);
 }
 
 int dispatch_expand_workspace_size(const dispatch_expand_problem_t* problem, size_t* bytes) {

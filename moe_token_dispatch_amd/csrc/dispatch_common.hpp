@@ -35,6 +35,7 @@ struct TileGeometry {
     int32_t chunks_per_wave;    // CH: 1, 2, 4 or 8
     int32_t tokens_per_wave;    // tokens_per_chunk * CH
     int32_t waves_per_tile;     // W
+    int32_t max_waves;          // the most wavefronts per workgroup the LDS budget allows (at most 16)
     int32_t tokens_per_tile;    // W * tokens_per_wave
     int32_t num_tiles;          // >= 1
     int32_t num_keys;           // E + R: expert keys first, then rank keys
@@ -72,6 +73,7 @@ inline TileGeometry make_geometry(int64_t num_tokens, int32_t num_topk, int32_t 
     // once the tile count would make the column scan long. (Measured on
     // MI355X: 8-wavefront tiles lay out 512 to 8192 tokens fastest.)
     const int w_full = clamp_w(kFewTileWaves);
+    g.max_waves = w_full;
     const int64_t tpc = g.tokens_per_chunk;
     auto tiles_of = [&](int w, int ch) { return (num_tokens + (int64_t)w * ch * tpc - 1) / ((int64_t)w * ch * tpc); };
     g.column_scan = true;
@@ -144,6 +146,52 @@ hipError_t launch_layout(const dispatch_problem_t& p, const TileGeometry& g, con
 hipError_t launch_scatter(const dispatch_problem_t& p, const dispatch_layout_t& lay, const void* x,
                           const float* x_sf, void* rank_x, float* rank_sf, void* recv_x,
                           float* recv_sf, hipStream_t stream, bool few_destinations);
+// One-launch dispatch of a batch that fits one layout tile: layout and row
+// copies in a single kernel (the assign kernel's fused mode). The row copies
+// are cut into units of one token's 1 KB row segment; workgroup g copies units
+// [g * units_per_group, (g + 1) * units_per_group), so the copies spread over
+// many CUs even when there are few tokens.
+constexpr int kFusedGroups = 256;         // at most this many workgroups
+constexpr int kFusedMaxPairs = 32;        // (token, k) pairs whose slots one workgroup holds
+constexpr int kFusedStoresPerThread = 8;  // 16-byte stores per thread that size the wavefront count
+struct FusedShape {
+    bool fits;
+    int64_t groups;
+    int32_t units_per_group;
+    int32_t segments;  // 1 KB units per row
+    int32_t waves;     // wavefronts per workgroup
+};
+inline FusedShape fused_shape(const TileGeometry& g, int64_t row_bytes) {
+    FusedShape f{};
+    const int64_t t = g.num_tokens;
+    const int64_t vecs = row_bytes / 16;
+    f.segments = (int32_t)(vecs < 1 ? 1 : (vecs + 63) / 64);
+    const int64_t units = t * f.segments;
+    // At least half a row per workgroup (measured on MI355X: one 1 KB unit per
+    // workgroup ranks the batch in too many workgroups at once for wide rows,
+    // a whole row per workgroup leaves CUs idle).
+    const int64_t per = (f.segments + 1) / 2;
+    const int64_t want = (units + per - 1) / per;
+    f.groups = want < 1 ? 1 : (want < kFusedGroups ? want : kFusedGroups);
+    f.units_per_group = (int32_t)(units < 1 ? 1 : (units + f.groups - 1) / f.groups);
+    // A unit range touches at most this many tokens.
+    const int64_t tokens = f.segments == 1 ? f.units_per_group : (f.units_per_group + f.segments - 1) / f.segments + 1;
+    // Enough wavefronts for the copies (K expert rows and one rank row per
+    // unit), at least those the tile's ranking uses, at most what LDS allows.
+    const int64_t unit_vecs = vecs < 64 ? vecs : 64;
+    const int64_t stores = (int64_t)f.units_per_group * unit_vecs * (g.num_topk + 1);
+    int64_t w = (stores + kWave * kFusedStoresPerThread - 1) / (kWave * kFusedStoresPerThread);
+    if (w > g.max_waves) w = g.max_waves;
+    if (w < g.waves_per_tile) w = g.waves_per_tile;
+    f.waves = (int32_t)w;
+    f.fits = g.num_tiles == 1 && !g.column_scan && tokens * g.num_topk <= kFusedMaxPairs;
+    return f;
+}
+// Requires fused_shape(g, row_bytes).fits; the outputs are those of
+// launch_layout followed by launch_scatter.
+hipError_t launch_fused_dispatch(const dispatch_problem_t& p, const TileGeometry& g, const void* topk_idx,
+                                 const dispatch_layout_t& out, void* workspace, const void* x, const float* x_sf,
+                                 void* rank_x, float* rank_sf, void* recv_x, float* recv_sf, hipStream_t stream);
 hipError_t launch_combine(int64_t num_tokens, int32_t num_topk, int64_t row_bytes, int64_t expert_rows,
                           const int32_t* expert_slot, const float* weights, const void* y, void* out,
                           hipStream_t stream);

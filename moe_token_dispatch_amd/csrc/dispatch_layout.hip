@@ -36,6 +36,7 @@
 // instruction, so lanes holding equal keys are found with one ballot per key
 // bit (a wavefront multisplit).
 #include "dispatch_common.hpp"
+#include "dispatch_device.hpp"
 
 namespace moe_dispatch {
 namespace {
@@ -324,6 +325,24 @@ colscan_kernel(LayoutParams p, Workspace ws, int kpb) {
     }
 }
 
+// Rows for the one-launch small-batch dispatch (assign_kernel with FUSED):
+// the token rows and the two output layouts, as dispatch_scatter takes them.
+struct RowArgs {
+    const u32x4* x;
+    const uint32_t* x_sf;
+    u32x4* rank_x;
+    uint32_t* rank_sf;
+    u32x4* recv_x;
+    uint32_t* recv_sf;
+    int64_t row_vecs;         // row_bytes / 16
+    int32_t sf_per_token;
+    int32_t segments;         // 1 KB units per row (64 vectors each)
+    int32_t units_per_group;  // (token, unit) pairs each workgroup copies
+    int32_t write_rank;       // rank_x / rank_sf requested
+    int32_t write_expert;     // recv_x / recv_sf requested
+    int32_t zero_pad;         // pad rows of recv_x / recv_sf zeroed
+};
+
 // Where assign_kernel takes each key's count in earlier tiles and in all tiles:
 enum AssignMode {
     kFromColumnScan = 0,  // the column-scan kernel's prefixes and totals
@@ -331,18 +350,44 @@ enum AssignMode {
     kSingleTile = 2,      // one tile holds every pair: its own wavefront counters (no count kernel)
 };
 
-template <int CH, int MODE, bool EXPAND, typename IdxT>
+// FUSED (with kSingleTile only): the whole dispatch of a batch that fits one
+// tile in one launch. Every workgroup ranks the entire tile itself (a few
+// microseconds of redundant ALU work, no communication between workgroups).
+// Workgroup 0 writes the counts, psums and status. Workgroup g copies the row
+// units [g * units_per_group, (g + 1) * units_per_group), a unit being one
+// token's 1 KB row segment, to the token's destination rows; it writes the
+// slot-map entries and scale factors of the tokens whose first unit it holds,
+// and zeroes the pad rows of experts g, g + G, ... The results equal those of
+// the layout followed by the scatter.
+template <int CH, int MODE, bool EXPAND, typename IdxT, bool FUSED = false>
 __global__ void __launch_bounds__(kLayoutThreads)
-assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispatch_layout_t out) {
+assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispatch_layout_t out, RowArgs rows) {
+    static_assert(!FUSED || (MODE == kSingleTile && !EXPAND), "the fused dispatch covers one-tile batches");
     // LDS: [W][num_keys] wavefront counters, then totals[num_keys] and first[num_keys].
     extern __shared__ int lds[];
     __shared__ int scratch[2 * (kLayoutThreads / kWave + 1)];
     __shared__ uint32_t block_err;
+    __shared__ int dest_expert[FUSED ? kFusedMaxPairs : 1], dest_rank[FUSED ? kFusedMaxPairs : 1];
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int nthreads = blockDim.x, nwaves = nthreads / kWave, nkeys = p.num_keys;
     const int K = p.num_topk, E = p.num_experts, R = p.num_ranks;
-    const int tile = blockIdx.x;
+    const int tile = FUSED ? 0 : blockIdx.x;
+    // The workgroup that writes the counts, psums and status.
+    const bool writes_totals = FUSED ? blockIdx.x == 0 : tile == 0;
+    // FUSED: this workgroup's row units [unit0, unit1) and the tokens they
+    // belong to, [tok_first, tok_first + its slot rows).
+    const int64_t segs = FUSED ? rows.segments : 1;
+    const int64_t unit0 = FUSED ? min((int64_t)blockIdx.x * rows.units_per_group, p.num_tokens * segs) : 0;
+    const int64_t unit1 = FUSED ? min(unit0 + rows.units_per_group, p.num_tokens * segs) : 0;
+    const int64_t tok_first = unit0 / segs;
+    const int64_t tok_end = unit1 > unit0 ? (unit1 - 1) / segs + 1 : tok_first;
+    if constexpr (FUSED) {
+        if (tid < kFusedMaxPairs) {
+            dest_expert[tid] = -1;
+            dest_rank[tid] = -1;
+        }
+    }
     int* counters = lds + wave * nkeys;
     int* totals = lds + nwaves * nkeys;  // per key, over all tiles
     int* first = totals + nkeys;         // per key, first slot (exclusive psum)
@@ -434,13 +479,13 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
         if (MODE == kSingleTile) totals[j] = run;
     }
     if (MODE == kSingleTile) __syncthreads();
-    const int2 rows = block_exclusive_scan2(totals, first, E, nkeys, p.alignment, scratch);
-    const int recv_rows = rows.x, rank_rows = rows.y;
+    const int2 row_totals = block_exclusive_scan2(totals, first, E, nkeys, p.alignment, scratch);
+    const int recv_rows = row_totals.x, rank_rows = row_totals.y;
     uint32_t status = block_err;
     if (recv_rows > p.recv_capacity) status |= DISPATCH_STATUS_RECV_OVERFLOW;
     if (rank_rows > p.rank_capacity) status |= DISPATCH_STATUS_RANK_OVERFLOW;
     // The receiver-side expand has no rank outputs (their pointers are NULL).
-    if (tile == 0) {
+    if (writes_totals) {
         for (int j = tid; j < nkeys; j += nthreads) {
             if (j < E) {
                 out.expert_count[j] = totals[j];
@@ -473,6 +518,15 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
         const int e = pos[c].expert, r = pos[c].rank;
         const int es = e >= 0 ? first[e] + counters[e] + pos[c].expert_pos : -1;
         const int rs = r >= 0 ? first[E + r] + counters[E + r] + pos[c].rank_pos : -1;
+        if constexpr (FUSED) {
+            // Every workgroup knows every slot. It keeps those of its tokens,
+            // and writes the slot-map entries of the tokens whose first unit
+            // is its own.
+            if (tok < tok_first || tok >= tok_end) continue;
+            dest_expert[(tok - tok_first) * K + k] = es;
+            dest_rank[(tok - tok_first) * K + k] = rs;
+            if (tok * segs < unit0) continue;
+        }
         out.expert_slot[tok * K + k] = es;
         // Slots are below the totals, which fit the capacities when the
         // status is 0; the bounds are checked anyway before every store.
@@ -486,10 +540,65 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
     // Alignment pads of recv_src_token_idx (section 7.3): the slots after an
     // expert's real rows up to its aligned end map to no token.
     if (p.alignment > 1) {
-        for (int e = tile; e < E; e += gridDim.x) {
+        for (int e = blockIdx.x; e < E; e += gridDim.x) {
             const int lo = first[e] + totals[e];
             const int hi = (int)min((int64_t)(e + 1 < E ? first[e + 1] : recv_rows), p.recv_capacity);
             for (int s = lo + tid; s < hi; s += nthreads) out.recv_src_token_idx[s] = -1;
+        }
+    }
+    if constexpr (FUSED) {
+        // The row copies of this workgroup's tokens (sections 6.3 and 8.2),
+        // bitwise, each row read once: every thread takes 16-byte vectors of
+        // the row and stores each to all of the token's destination rows.
+        __syncthreads();
+        const int64_t nv = rows.row_vecs;
+        const int S = rows.sf_per_token;
+        for (int64_t t = tok_first; t < tok_end; ++t) {
+            const int64_t m = t - tok_first;
+            // Slots past the capacities never occur with status 0; they are
+            // dropped all the same, so no store can leave the output buffers.
+            bool any = false;
+            for (int kk = 0; kk < K; ++kk) {
+                const int de = dest_expert[m * K + kk], dr = dest_rank[m * K + kk];
+                any |= (rows.write_expert && de >= 0 && de < p.recv_capacity) ||
+                       (rows.write_rank && dr >= 0 && dr < p.rank_capacity);
+            }
+            if (!any) continue;  // a row with no destination is not read
+            // This workgroup's units of the row, as a range of 16-byte vectors.
+            const int64_t u_lo = max(unit0, t * segs) - t * segs, u_hi = min(unit1, (t + 1) * segs) - t * segs;
+            const int64_t v_hi = min(u_hi * kWave, nv);
+            for (int64_t i = u_lo * kWave + tid; i < v_hi; i += nthreads) {
+                const u32x4 v = rows.x[t * nv + i];
+                for (int kk = 0; kk < K; ++kk) {
+                    const int de = dest_expert[m * K + kk], dr = dest_rank[m * K + kk];
+                    if (rows.write_expert && de >= 0 && de < p.recv_capacity)
+                        RowWriter(rows.recv_x + (int64_t)de * nv, (int)(nv * 16)).store(i, v);
+                    if (rows.write_rank && dr >= 0 && dr < p.rank_capacity)
+                        RowWriter(rows.rank_x + (int64_t)dr * nv, (int)(nv * 16)).store(i, v);
+                }
+            }
+            // The scale factors go with the row's first unit.
+            for (int i = tid; i < (u_lo == 0 ? S : 0); i += nthreads) {
+                const uint32_t v = rows.x_sf[t * S + i];
+                for (int kk = 0; kk < K; ++kk) {
+                    const int de = dest_expert[m * K + kk], dr = dest_rank[m * K + kk];
+                    if (rows.write_expert && de >= 0 && de < p.recv_capacity) rows.recv_sf[(int64_t)de * S + i] = v;
+                    if (rows.write_rank && dr >= 0 && dr < p.rank_capacity) rows.rank_sf[(int64_t)dr * S + i] = v;
+                }
+            }
+        }
+        // Pad rows are zero bytes (section 7.3).
+        if (rows.write_expert && rows.zero_pad && p.alignment > 1) {
+            const u32x4 zero = {0u, 0u, 0u, 0u};
+            for (int e = blockIdx.x; e < E; e += gridDim.x) {
+                const int64_t lo = first[e] + totals[e];
+                const int64_t hi = min((int64_t)(e + 1 < E ? first[e + 1] : recv_rows), p.recv_capacity);
+                for (int64_t row = lo; row < hi; ++row) {
+                    const RowWriter dst(rows.recv_x + row * nv, (int)(nv * 16));
+                    for (int64_t i = tid; i < nv; i += nthreads) dst.store(i, zero);
+                    for (int i = tid; i < S; i += nthreads) rows.recv_sf[row * S + i] = 0u;
+                }
+            }
         }
     }
 }
@@ -508,8 +617,9 @@ hipError_t launch_typed(const LayoutParams& p, const TileGeometry& g, const void
     LayoutParams pc = p;
     Workspace wc = ws;
     dispatch_layout_t oc = out;
+    RowArgs rc{};  // no rows: the layout alone
     const size_t assign_lds = (size_t)(g.waves_per_tile + 2) * g.num_keys * sizeof(int);
-    void* assign_args[] = {&idx, &pc, &wc, &oc};
+    void* assign_args[] = {&idx, &pc, &wc, &oc, &rc};
     if (g.num_tiles == 1 && !g.column_scan)
         return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, kSingleTile, EXPAND, IdxT>), grid,
                                block, assign_args, assign_lds, stream);
@@ -541,11 +651,24 @@ hipError_t launch_chunks(const LayoutParams& p, const TileGeometry& g, const voi
     }
 }
 
-}  // namespace
+template <int CH, typename IdxT>
+hipError_t launch_fused_typed(const LayoutParams& p, const TileGeometry& g, const void* topk,
+                              const dispatch_layout_t& out, const Workspace& ws, const RowArgs& rows,
+                              const FusedShape& f, hipStream_t stream) {
+    const auto* idx = static_cast<const IdxT*>(topk);
+    LayoutParams pc = p;
+    Workspace wc = ws;
+    dispatch_layout_t oc = out;
+    RowArgs rc = rows;
+    // f.waves may exceed the tile's wavefronts: the extra ones rank empty
+    // chunks (no change to any count) and add their threads to the copies.
+    const size_t lds = (size_t)(f.waves + 2) * g.num_keys * sizeof(int);
+    void* args[] = {&idx, &pc, &wc, &oc, &rc};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, kSingleTile, false, IdxT, true>),
+                           dim3((unsigned)f.groups), dim3(f.waves * kWave), args, lds, stream);
+}
 
-hipError_t launch_layout(const dispatch_problem_t& prob, const TileGeometry& g, const void* topk_idx,
-                         const dispatch_layout_t& out, void* workspace, hipStream_t stream,
-                         const ExpandView* expand) {
+LayoutParams make_params(const dispatch_problem_t& prob, const TileGeometry& g) {
     LayoutParams p{};
     p.num_tokens = prob.num_tokens;
     p.recv_capacity = prob.recv_capacity_rows;
@@ -563,12 +686,26 @@ hipError_t launch_layout(const dispatch_problem_t& prob, const TileGeometry& g, 
     p.num_keys = g.num_keys;
     p.hist_stride = g.hist_stride;
     p.num_tiles = g.num_tiles;
+    return p;
+}
+
+Workspace make_workspace(const TileGeometry& g, void* workspace) {
     char* base = static_cast<char*>(workspace);
     Workspace ws;
     ws.tile_hist = reinterpret_cast<int32_t*>(base + g.ws_tile_hist);
     ws.tile_prefix = reinterpret_cast<int32_t*>(base + g.ws_tile_prefix);
     ws.totals = reinterpret_cast<int32_t*>(base + g.ws_totals);
     ws.tile_err = reinterpret_cast<int32_t*>(base + g.ws_tile_err);
+    return ws;
+}
+
+}  // namespace
+
+hipError_t launch_layout(const dispatch_problem_t& prob, const TileGeometry& g, const void* topk_idx,
+                         const dispatch_layout_t& out, void* workspace, hipStream_t stream,
+                         const ExpandView* expand) {
+    LayoutParams p = make_params(prob, g);
+    const Workspace ws = make_workspace(g, workspace);
     if (expand != nullptr) {
         p.recv_count = expand->recv_count;
         p.rows_per_source = expand->rows_per_source;
@@ -579,6 +716,36 @@ hipError_t launch_layout(const dispatch_problem_t& prob, const TileGeometry& g, 
     }
     if (prob.topk_idx_bytes == 8) return launch_chunks<false, int64_t>(p, g, topk_idx, out, ws, stream);
     return launch_chunks<false, int32_t>(p, g, topk_idx, out, ws, stream);
+}
+
+
+hipError_t launch_fused_dispatch(const dispatch_problem_t& prob, const TileGeometry& g, const void* topk_idx,
+                                 const dispatch_layout_t& out, void* workspace, const void* x, const float* x_sf,
+                                 void* rank_x, float* rank_sf, void* recv_x, float* recv_sf, hipStream_t stream) {
+    const FusedShape f = fused_shape(g, prob.row_bytes);
+    if (!f.fits) return hipErrorInvalidValue;
+    const LayoutParams p = make_params(prob, g);
+    const Workspace ws = make_workspace(g, workspace);
+    RowArgs rows{};
+    rows.x = static_cast<const u32x4*>(x);
+    rows.x_sf = reinterpret_cast<const uint32_t*>(x_sf);
+    rows.rank_x = static_cast<u32x4*>(rank_x);
+    rows.rank_sf = reinterpret_cast<uint32_t*>(rank_sf);
+    rows.recv_x = static_cast<u32x4*>(recv_x);
+    rows.recv_sf = reinterpret_cast<uint32_t*>(recv_sf);
+    rows.row_vecs = prob.row_bytes / 16;
+    rows.sf_per_token = prob.sf_per_token;
+    rows.segments = f.segments;
+    rows.units_per_group = f.units_per_group;
+    rows.write_rank = (prob.flags & DISPATCH_RANK_CONTIG) != 0;
+    rows.write_expert = (prob.flags & DISPATCH_EXPERT_MAJOR) != 0;
+    rows.zero_pad = (prob.flags & DISPATCH_ZERO_PAD) != 0;
+    const bool wide = prob.topk_idx_bytes == 8;
+    if (g.chunks_per_wave == 1)
+        return wide ? launch_fused_typed<1, int64_t>(p, g, topk_idx, out, ws, rows, f, stream)
+                    : launch_fused_typed<1, int32_t>(p, g, topk_idx, out, ws, rows, f, stream);
+    return wide ? launch_fused_typed<2, int64_t>(p, g, topk_idx, out, ws, rows, f, stream)
+                : launch_fused_typed<2, int32_t>(p, g, topk_idx, out, ws, rows, f, stream);
 }
 
 }  // namespace moe_dispatch

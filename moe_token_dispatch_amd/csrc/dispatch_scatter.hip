@@ -20,11 +20,10 @@
 // caches and is not read back here, and of the store forms measured on MI355X
 // this one moved the rows fastest.
 #include "dispatch_common.hpp"
+#include "dispatch_device.hpp"
 
 namespace moe_dispatch {
 namespace {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPadRowsPerWave = 8;
 // V, the 16-byte vectors per lane of one row segment, follows the stores per
@@ -52,21 +51,6 @@ struct ScatterParams {
     int32_t pad_waves_per_expert;
     int32_t write_rank;      // rank_x / rank_sf requested
     int32_t write_expert;    // recv_x / recv_sf requested
-};
-
-// Buffer descriptor word 3 for gfx9-family raw buffers (32-bit data format,
-// no swizzle) and the nt | sc1 store cache policy.
-constexpr int kBufferWord3 = 0x00020000;
-constexpr int kStreamingPolicy = 2 | 16;
-
-// Stores 16-byte vectors into one row of `row_bytes` bytes.
-struct RowWriter {
-    __amdgpu_buffer_rsrc_t rsrc;
-    __device__ __forceinline__ RowWriter(u32x4* row, int row_bytes)
-        : rsrc(__builtin_amdgcn_make_buffer_rsrc(row, 0, row_bytes, kBufferWord3)) {}
-    __device__ __forceinline__ void store(int64_t vec, const u32x4& v) const {
-        __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, (int)(vec * 16), 0, kStreamingPolicy);
-    }
 };
 
 template <int V>

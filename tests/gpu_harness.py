@@ -47,7 +47,9 @@ def run_gpu(topk: np.ndarray, num_experts: int, num_ranks: int, alignment: int,
             x_bytes: np.ndarray, x_sf: Optional[np.ndarray] = None, *, topk_bytes: int = 8,
             flags: int = M.ALL_OUTPUTS, recv_capacity: Optional[int] = None,
             rank_capacity: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
-            scatter: bool = True) -> GpuRun:
+            scatter: bool = True, combined: bool = False) -> GpuRun:
+    """Layout and scatter of one batch on the GPU: two calls, or with
+    ``combined`` the single dispatch_layout_and_scatter call."""
     t, k = topk.shape
     row_bytes = x_bytes.shape[1]
     s = 0 if x_sf is None else x_sf.shape[1]
@@ -66,9 +68,13 @@ def run_gpu(topk: np.ndarray, num_experts: int, num_ranks: int, alignment: int,
     topk_d = torch.from_numpy(np.ascontiguousarray(topk.astype(np_dtype))).to(DEVICE)
     x_d = torch.from_numpy(np.ascontiguousarray(x_bytes)).to(DEVICE)
     sf_d = None if x_sf is None else torch.from_numpy(np.ascontiguousarray(x_sf, dtype=np.float32)).to(DEVICE)
-    M.dispatch_layout(prob, topk_d, lay, ws)
-    if scatter:
-        M.dispatch_scatter(prob, lay, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x, rows.recv_sf)
+    if combined:
+        M.dispatch_layout_and_scatter(prob, topk_d, lay, ws, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x,
+                                      rows.recv_sf)
+    else:
+        M.dispatch_layout(prob, topk_d, lay, ws)
+        if scatter:
+            M.dispatch_scatter(prob, lay, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x, rows.recv_sf)
     torch.cuda.synchronize()
     return GpuRun(prob, lay, rows, x_d, sf_d, ws)
 

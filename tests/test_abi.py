@@ -141,6 +141,51 @@ def test_host_errors_before_launch():
     assert sc(p4, good, 4096, None, None, None, 4104, None) == M.ERR_ALIGN
 
 
+def test_kernel_counts():
+    """One kernel for a one-tile batch (both calls); two layout kernels with the
+    histograms reduced in the assign kernel; three with the column scan."""
+    mk = M.make_problem
+    assert M.dispatch_kernel_count(mk(256, 8, 256, 8, 1, row_bytes=14336)) == (1, 1)
+    assert M.dispatch_kernel_count(mk(0, 8, 256, 8, 1, row_bytes=64)) == (1, 1)
+    assert M.dispatch_kernel_count(mk(2048, 1, 64, 8, 1, row_bytes=48)) == (1, 1)
+    assert M.dispatch_kernel_count(mk(257, 8, 256, 8, 1, row_bytes=14336)) == (2, 3)
+    assert M.dispatch_kernel_count(mk(4096, 8, 256, 8, 1, row_bytes=14336)) == (2, 3)
+    assert M.dispatch_kernel_count(mk(65536, 8, 256, 8, 128, row_bytes=7168, sf_per_token=56)) == (2, 3)
+    assert M.dispatch_kernel_count(mk(4096, 8, 4096, 1024, 1, row_bytes=64)) == (3, 4)
+    assert M.dispatch_kernel_count(mk(80, 8, 4096, 1024, 1, row_bytes=64)) == (1, 1)
+    assert M.dispatch_kernel_count(mk(81, 8, 4096, 1024, 1, row_bytes=64)) == (2, 3)
+    with pytest.raises(M.DispatchError):
+        M.dispatch_kernel_count(M.Problem(10, 0, 8, 2, 1, 8, 0, 64, 100, 100, M.ALL_OUTPUTS, 0))
+
+
+def test_layout_and_scatter_host_errors_before_launch():
+    """The combined call makes both calls' checks before enqueuing anything."""
+    lib = M.load_library()
+    p = M.Problem(100, 8, 256, 8, 1, 8, 4, 64, 1000, 1000, M.ALL_OUTPUTS, 0)
+    good = M.LayoutPtrs(*([4096] * 9))
+    ws_need = M.dispatch_workspace_size(p)
+
+    def call(prob, topk, lay, ws, n, x, sf, rx, rsf, ex, esf):
+        return lib.dispatch_layout_and_scatter(ctypes.byref(prob) if prob is not None else None, topk,
+                                               ctypes.byref(lay) if lay is not None else None, ws, n,
+                                               x, sf, rx, rsf, ex, esf, None)
+
+    rows = (4096, 4096, 4096, 4096, 4096, 4096)
+    assert call(None, 4096, good, 4096, ws_need, *rows) == M.ERR_NULL
+    assert call(p, None, good, 4096, ws_need, *rows) == M.ERR_NULL
+    assert call(p, 4096, None, 4096, ws_need, *rows) == M.ERR_NULL
+    assert call(p, 4096, good, None, ws_need, *rows) == M.ERR_WORKSPACE
+    assert call(p, 4096, good, 4096, ws_need - 1, *rows) == M.ERR_WORKSPACE
+    assert call(p, 4100, good, 4096, ws_need, *rows) == M.ERR_ALIGN
+    assert call(p, 4096, good, 4096, ws_need, None, 4096, 4096, 4096, 4096, 4096) == M.ERR_NULL  # no x
+    assert call(p, 4096, good, 4096, ws_need, 4096, None, 4096, 4096, 4096, 4096) == M.ERR_NULL  # S > 0
+    assert call(p, 4096, good, 4096, ws_need, 4104, 4096, 4096, 4096, 4096, 4096) == M.ERR_ALIGN
+    bad = M.Problem(100, 8, 256, 8, 1, 8, 4, 72, 1000, 1000, M.ALL_OUTPUTS, 0)  # row_bytes % 16
+    assert call(bad, 4096, good, 4096, ws_need, *rows) == M.ERR_ALIGN
+    bad.row_bytes, bad.num_topk = 64, 0
+    assert call(bad, 4096, good, 4096, ws_need, *rows) == M.ERR_ARG
+
+
 def test_binding_refuses_host_tensors():
     import torch
 
