@@ -32,7 +32,8 @@ if ROOT not in sys.path:
 METRIC = "dispatch GB/s & % HBM peak, 4096 tok×7168 bf16, top-8 of 256 experts"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scatter_traffic.json")
-SCATTER_SOURCES = [os.path.join(ROOT, "moe_token_dispatch_amd", "csrc", "dispatch_scatter.hip")]
+SCATTER_SOURCES = [os.path.join(ROOT, "moe_token_dispatch_amd", "csrc", f)
+                   for f in ("dispatch_scatter.hip", "dispatch_device.hpp")]
 COMBINE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_traffic.json")
 EXPAND_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expand_scatter_traffic.json")
 COMBINE_SOURCES = [os.path.join(ROOT, "moe_token_dispatch_amd", "csrc", "dispatch_combine.hip")]
