@@ -152,18 +152,34 @@ hipError_t launch_scatter(const dispatch_problem_t& p, const dispatch_layout_t& 
 // [g * units_per_group, (g + 1) * units_per_group), so the copies spread over
 // many CUs even when there are few tokens.
 constexpr int kFusedGroups = 256;         // at most this many workgroups
-constexpr int kFusedMaxPairs = 32;        // (token, k) pairs whose slots one workgroup holds
+constexpr int kFusedMaxPairs = 64;        // (token, k) pairs whose slots one workgroup holds
+constexpr int kFusedMaxChunks = 8;        // chunks per wavefront of the one tile every workgroup ranks
+// The most (token, k) pairs of a batch the one kernel takes. Every workgroup
+// ranks them all; measured on MI355X, beyond about 3072 pairs that costs more
+// than the layout and scatter launches it saves (at 4096 pairs: 14.0 against
+// 12.6 us for 256-byte rows, 29.2 against 29.6 us for 14 KB rows).
+constexpr int64_t kFusedMaxBatchPairs = 3072;
 constexpr int kFusedStoresPerThread = 8;  // 16-byte stores per thread that size the wavefront count
 struct FusedShape {
     bool fits;
+    int32_t chunks;      // chunks per wavefront of the tile
+    int32_t tile_waves;  // wavefronts the tile needs
     int64_t groups;
     int32_t units_per_group;
-    int32_t segments;  // 1 KB units per row
-    int32_t waves;     // wavefronts per workgroup
+    int32_t segments;    // 1 KB units per row
+    int32_t waves;       // wavefronts per workgroup (>= tile_waves)
 };
 inline FusedShape fused_shape(const TileGeometry& g, int64_t row_bytes) {
     FusedShape f{};
     const int64_t t = g.num_tokens;
+    // The tile: the fewest chunks per wavefront that fit the batch in the
+    // wavefronts LDS allows, then just enough wavefronts.
+    const int64_t tpc = g.tokens_per_chunk;
+    f.chunks = 1;
+    while (f.chunks < kFusedMaxChunks && (int64_t)g.max_waves * f.chunks * tpc < t) f.chunks *= 2;
+    const int64_t per_wave = (int64_t)f.chunks * tpc;
+    const int64_t tw = (t + per_wave - 1) / per_wave;
+    f.tile_waves = (int32_t)(tw < 1 ? 1 : tw);
     const int64_t vecs = row_bytes / 16;
     f.segments = (int32_t)(vecs < 1 ? 1 : (vecs + 63) / 64);
     const int64_t units = t * f.segments;
@@ -182,9 +198,10 @@ inline FusedShape fused_shape(const TileGeometry& g, int64_t row_bytes) {
     const int64_t stores = (int64_t)f.units_per_group * unit_vecs * (g.num_topk + 1);
     int64_t w = (stores + kWave * kFusedStoresPerThread - 1) / (kWave * kFusedStoresPerThread);
     if (w > g.max_waves) w = g.max_waves;
-    if (w < g.waves_per_tile) w = g.waves_per_tile;
+    if (w < f.tile_waves) w = f.tile_waves;
     f.waves = (int32_t)w;
-    f.fits = g.num_tiles == 1 && !g.column_scan && tokens * g.num_topk <= kFusedMaxPairs;
+    f.fits = f.tile_waves <= g.max_waves && tokens * g.num_topk <= kFusedMaxPairs &&
+             t * g.num_topk <= kFusedMaxBatchPairs;
     return f;
 }
 // Requires fused_shape(g, row_bytes).fits; the outputs are those of

@@ -724,7 +724,16 @@ hipError_t launch_fused_dispatch(const dispatch_problem_t& prob, const TileGeome
                                  void* rank_x, float* rank_sf, void* recv_x, float* recv_sf, hipStream_t stream) {
     const FusedShape f = fused_shape(g, prob.row_bytes);
     if (!f.fits) return hipErrorInvalidValue;
-    const LayoutParams p = make_params(prob, g);
+    // The one tile every workgroup ranks (the layout's own geometry may use
+    // several tiles for this batch).
+    TileGeometry tile = g;
+    tile.chunks_per_wave = f.chunks;
+    tile.waves_per_tile = f.tile_waves;
+    tile.tokens_per_wave = f.chunks * g.tokens_per_chunk;
+    tile.tokens_per_tile = f.tile_waves * tile.tokens_per_wave;
+    tile.num_tiles = 1;
+    tile.column_scan = false;
+    const LayoutParams p = make_params(prob, tile);
     const Workspace ws = make_workspace(g, workspace);
     RowArgs rows{};
     rows.x = static_cast<const u32x4*>(x);
@@ -741,11 +750,16 @@ hipError_t launch_fused_dispatch(const dispatch_problem_t& prob, const TileGeome
     rows.write_expert = (prob.flags & DISPATCH_EXPERT_MAJOR) != 0;
     rows.zero_pad = (prob.flags & DISPATCH_ZERO_PAD) != 0;
     const bool wide = prob.topk_idx_bytes == 8;
-    if (g.chunks_per_wave == 1)
-        return wide ? launch_fused_typed<1, int64_t>(p, g, topk_idx, out, ws, rows, f, stream)
-                    : launch_fused_typed<1, int32_t>(p, g, topk_idx, out, ws, rows, f, stream);
-    return wide ? launch_fused_typed<2, int64_t>(p, g, topk_idx, out, ws, rows, f, stream)
-                : launch_fused_typed<2, int32_t>(p, g, topk_idx, out, ws, rows, f, stream);
+    switch (f.chunks) {
+        case 1: return wide ? launch_fused_typed<1, int64_t>(p, tile, topk_idx, out, ws, rows, f, stream)
+                            : launch_fused_typed<1, int32_t>(p, tile, topk_idx, out, ws, rows, f, stream);
+        case 2: return wide ? launch_fused_typed<2, int64_t>(p, tile, topk_idx, out, ws, rows, f, stream)
+                            : launch_fused_typed<2, int32_t>(p, tile, topk_idx, out, ws, rows, f, stream);
+        case 4: return wide ? launch_fused_typed<4, int64_t>(p, tile, topk_idx, out, ws, rows, f, stream)
+                            : launch_fused_typed<4, int32_t>(p, tile, topk_idx, out, ws, rows, f, stream);
+        default: return wide ? launch_fused_typed<8, int64_t>(p, tile, topk_idx, out, ws, rows, f, stream)
+                             : launch_fused_typed<8, int32_t>(p, tile, topk_idx, out, ws, rows, f, stream);
+    }
 }
 
 }  // namespace moe_dispatch

@@ -142,18 +142,23 @@ def test_host_errors_before_launch():
 
 
 def test_kernel_counts():
-    """One kernel for a one-tile batch (both calls); two layout kernels with the
-    histograms reduced in the assign kernel; three with the column scan."""
+    """The layout: one kernel for a one-tile batch, two with the histograms
+    reduced in the assign kernel, three with the column scan. The combined
+    call: one kernel up to 3072 (token, k) pairs, else the layout's kernels
+    and the scatter."""
     mk = M.make_problem
     assert M.dispatch_kernel_count(mk(256, 8, 256, 8, 1, row_bytes=14336)) == (1, 1)
     assert M.dispatch_kernel_count(mk(0, 8, 256, 8, 1, row_bytes=64)) == (1, 1)
     assert M.dispatch_kernel_count(mk(2048, 1, 64, 8, 1, row_bytes=48)) == (1, 1)
-    assert M.dispatch_kernel_count(mk(257, 8, 256, 8, 1, row_bytes=14336)) == (2, 3)
+    assert M.dispatch_kernel_count(mk(257, 8, 256, 8, 1, row_bytes=14336)) == (2, 1)
+    assert M.dispatch_kernel_count(mk(384, 8, 256, 8, 1, row_bytes=14336)) == (2, 1)
+    assert M.dispatch_kernel_count(mk(385, 8, 256, 8, 1, row_bytes=14336)) == (2, 3)
+    assert M.dispatch_kernel_count(mk(3072, 1, 64, 8, 1, row_bytes=48)) == (2, 1)
     assert M.dispatch_kernel_count(mk(4096, 8, 256, 8, 1, row_bytes=14336)) == (2, 3)
     assert M.dispatch_kernel_count(mk(65536, 8, 256, 8, 128, row_bytes=7168, sf_per_token=56)) == (2, 3)
     assert M.dispatch_kernel_count(mk(4096, 8, 4096, 1024, 1, row_bytes=64)) == (3, 4)
     assert M.dispatch_kernel_count(mk(80, 8, 4096, 1024, 1, row_bytes=64)) == (1, 1)
-    assert M.dispatch_kernel_count(mk(81, 8, 4096, 1024, 1, row_bytes=64)) == (2, 3)
+    assert M.dispatch_kernel_count(mk(300, 8, 4096, 1024, 1, row_bytes=64)) == (2, 1)
     with pytest.raises(M.DispatchError):
         M.dispatch_kernel_count(M.Problem(10, 0, 8, 2, 1, 8, 0, 64, 100, 100, M.ALL_OUTPUTS, 0))
 

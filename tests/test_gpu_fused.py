@@ -1,10 +1,10 @@
 """GPU parity of dispatch_layout_and_scatter against the CPU oracle, bit for
 bit, through the C ABI.
 
-A batch that fits one layout tile (up to 2048 (token, k) pairs, fewer with
-many keys) is laid out and copied by one kernel in which every workgroup ranks
-the whole batch itself and copies its share of the rows' 1 KB segments; larger
-batches run the layout and scatter kernels. Either way the outputs must equal
+A small batch (up to 3072 (token, k) pairs, fewer with many keys) is laid out
+and copied by one kernel in which every workgroup ranks the whole batch itself
+and copies its share of the rows' 1 KB segments; larger batches run the layout
+and scatter kernels. Either way the outputs must equal
 the oracle's layout and scatter: every count, psum, slot, inverse-map entry,
 status bit and row byte, with canary bands past every total left untouched.
 """
@@ -90,15 +90,25 @@ def test_int32_routing_and_fully_masked_tokens():
     _fused(topk, 256, 8, 4, seed=6, topk_bytes=4)
 
 
-def test_many_keys_one_tile_and_just_past_it():
-    """E + R = 5120 keys leave room for 5 wavefronts of counters: one tile holds
-    80 tokens at top-8; 81 takes the two-kernel layout and the scatter."""
-    for t in (80, 81):
+# Past one layout tile, the one kernel ranks a tile of 4 (or, with few
+# wavefronts, 8) chunks per wavefront, up to 3072 pairs.
+@pytest.mark.parametrize("k,t,e,r", [(8, 257, 256, 8), (8, 300, 64, 8), (8, 384, 256, 8), (1, 3072, 64, 8),
+                                     (2, 1536, 64, 4), (3, 1024, 64, 16)])
+def test_batches_past_one_layout_tile(k, t, e, r):
+    _banner(f"K={k} T={t} E={e} R={r}")
+    _fused(_topk(42 + k, t, k, e, 0.05), e, r, 4, row_bytes=144, s=2, seed=t)
+
+
+def test_many_keys_eight_chunks_and_just_past_them():
+    """E + R = 5120 keys leave room for 5 wavefronts of counters: the one
+    kernel's tile holds 5 x 8 chunks x 8 tokens = 320 tokens at top-8; 321
+    take the layout and scatter kernels."""
+    for t in (80, 320, 321):
         _banner(f"E=4096 R=1024 T={t}")
         _fused(_topk(37, t, 8, 4096, 0.05), 4096, 1024, 2, seed=t)
 
 
-@pytest.mark.parametrize("t", [257, 3001])
+@pytest.mark.parametrize("t", [385, 3001])
 def test_larger_batches_take_the_layout_and_scatter_kernels(t):
     _banner(f"T={t}")
     _fused(_topk(38, t, 8, 256, 0.05), 256, 8, 4, seed=t)
