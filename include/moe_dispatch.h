@@ -222,6 +222,15 @@ int dispatch_expand_layout(const dispatch_expand_problem_t* problem, const void*
                            const int32_t* recv_count, const dispatch_layout_t* out, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/* dispatch_expand_layout followed by dispatch_expand_scatter in one call, with
+ * the same arguments, checks and outputs as those two calls made in turn. A
+ * small receive buffer (S * M * K up to 3072 entries) is laid out and copied
+ * by one kernel, as in dispatch_layout_and_scatter. */
+int dispatch_expand_layout_and_scatter(const dispatch_expand_problem_t* problem, const void* recv_topk_idx,
+                                       const int32_t* recv_count, const dispatch_layout_t* out, void* workspace,
+                                       size_t workspace_bytes, const void* recv_buf, const float* recv_sf_buf,
+                                       void* recv_x, float* recv_sf, hipStream_t stream);
+
 /* Copies the received rows (recv_buf [S*M, row_bytes], recv_sf_buf [S*M, sf])
  * into the expert-major recv_x / recv_sf of a layout made by
  * dispatch_expand_layout, zeroing pad rows. Writes nothing when the layout's

@@ -112,7 +112,7 @@ SYMBOLS = ("dispatch_abi_version", "dispatch_strerror", "dispatch_workspace_size
            "dispatch_max_rows", "dispatch_layout", "dispatch_scatter", "dispatch_layout_and_scatter",
            "dispatch_kernel_count",
            "dispatch_expand_workspace_size", "dispatch_expand_max_rows", "dispatch_expand_layout",
-           "dispatch_expand_scatter", "dispatch_combine")
+           "dispatch_expand_scatter", "dispatch_expand_layout_and_scatter", "dispatch_combine")
 
 
 def load_library(path: str = LIB_PATH):
@@ -150,6 +150,8 @@ def load_library(path: str = LIB_PATH):
     lib.dispatch_expand_layout.argtypes = [ep, p, p, ctypes.POINTER(LayoutPtrs), p, sz, p]
     lib.dispatch_expand_layout.restype = i
     lib.dispatch_expand_scatter.argtypes = [ep, ctypes.POINTER(LayoutPtrs), p, p, p, p, p]
+    lib.dispatch_expand_layout_and_scatter.argtypes = [ep, p, p, ctypes.POINTER(LayoutPtrs), p, sz, p, p, p, p, p]
+    lib.dispatch_expand_layout_and_scatter.restype = i
     lib.dispatch_expand_scatter.restype = i
     lib.dispatch_combine.argtypes = [ctypes.POINTER(CombineProblem), p, p, p, p, p]
     lib.dispatch_combine.restype = i
@@ -510,6 +512,35 @@ def dispatch_expand_layout(problem: ExpandProblem, recv_topk_idx: torch.Tensor, 
         workspace.numel() * workspace.element_size(), _stream_handle(stream, recv_topk_idx.device))
     if rc:
         raise DispatchError(rc, "dispatch_expand_layout")
+
+
+def dispatch_expand_layout_and_scatter(problem: ExpandProblem, recv_topk_idx: torch.Tensor,
+                                       recv_count: torch.Tensor, out: ExpandLayoutTensors, workspace: torch.Tensor,
+                                       recv_buf: torch.Tensor, recv_sf_buf: Optional[torch.Tensor],
+                                       recv_x: torch.Tensor, recv_sf: Optional[torch.Tensor],
+                                       stream: Optional[torch.cuda.Stream] = None,
+                                       expert_count_cumulative: Optional[torch.Tensor] = None) -> None:
+    """Enqueue dispatch_expand_layout then dispatch_expand_scatter as one call
+    (one kernel for a small receive buffer)."""
+    _check_device_tensor(recv_topk_idx, "recv_topk_idx")
+    if recv_topk_idx.element_size() != problem.topk_idx_bytes:
+        raise ValueError("recv_topk_idx element width does not match problem.topk_idx_bytes")
+    _check_device_tensor(recv_count, "recv_count", torch.int32)
+    _check_device_tensor(workspace, "workspace")
+    for f in dataclasses.fields(out):
+        _check_device_tensor(getattr(out, f.name), f.name, torch.int32)
+    _check_cumulative(expert_count_cumulative, problem.num_experts // problem.num_ranks)
+    _check_device_tensor(recv_buf, "recv_buf")
+    for name, t in (("recv_sf_buf", recv_sf_buf), ("recv_x", recv_x), ("recv_sf", recv_sf)):
+        if t is not None:
+            _check_device_tensor(t, name)
+    lay = out.ptrs(expert_count_cumulative)
+    rc = load_library().dispatch_expand_layout_and_scatter(
+        ctypes.byref(problem), _ptr(recv_topk_idx), _ptr(recv_count), ctypes.byref(lay), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(recv_buf), _ptr(recv_sf_buf), _ptr(recv_x), _ptr(recv_sf),
+        _stream_handle(stream, recv_topk_idx.device))
+    if rc:
+        raise DispatchError(rc, "dispatch_expand_layout_and_scatter")
 
 
 def dispatch_expand_scatter(problem: ExpandProblem, layout: ExpandLayoutTensors, recv_buf: torch.Tensor,

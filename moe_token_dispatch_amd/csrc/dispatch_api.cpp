@@ -137,6 +137,36 @@ int check_layout_args(const dispatch_problem_t* problem, const void* topk_idx, c
     return DISPATCH_OK;
 }
 
+// Host checks of an expand layout call's arguments; on success *p is the
+// dispatch problem the expand runs as, *g its geometry and *view the
+// receive-buffer view.
+int check_expand_layout_args(const dispatch_expand_problem_t* problem, const void* recv_topk_idx,
+                             const int32_t* recv_count, const dispatch_layout_t* out, void* workspace,
+                             size_t workspace_bytes, dispatch_problem_t* p, TileGeometry* g,
+                             moe_dispatch::ExpandView* view) {
+    int rc = check_expand(problem, p);
+    if (rc != DISPATCH_OK) return rc;
+    if (out == nullptr || !out->expert_count || !out->expert_psum || !out->status) return DISPATCH_ERR_NULL;
+    if (out->rank_count || out->rank_psum || out->rank_slot || out->rank_src_token_idx) return DISPATCH_ERR_ARG;
+    if (p->num_tokens > 0 && (!recv_topk_idx || !out->expert_slot)) return DISPATCH_ERR_NULL;
+    if (!recv_count) return DISPATCH_ERR_NULL;
+    if (p->recv_capacity_rows > 0 && !out->recv_src_token_idx) return DISPATCH_ERR_NULL;
+    if (workspace == nullptr) return DISPATCH_ERR_WORKSPACE;
+    if (recv_topk_idx && !aligned_to(recv_topk_idx, p->topk_idx_bytes)) return DISPATCH_ERR_ALIGN;
+    const void* ints[] = {recv_count, out->expert_count, out->expert_psum, out->expert_slot,
+                          out->recv_src_token_idx, out->status, out->expert_count_cumulative};
+    for (const void* q : ints)
+        if (q && !aligned_to(q, 4)) return DISPATCH_ERR_ALIGN;
+    if (!aligned_to(workspace, 256)) return DISPATCH_ERR_WORKSPACE;
+    *g = moe_dispatch::make_geometry(p->num_tokens, p->num_topk, p->num_experts, p->num_ranks);
+    if (workspace_bytes < moe_dispatch::workspace_bytes(*g)) return DISPATCH_ERR_WORKSPACE;
+    view->recv_count = recv_count;
+    view->rows_per_source = problem->rows_per_source;
+    view->first_expert = problem->local_rank * (problem->num_experts / problem->num_ranks);
+    view->global_experts = problem->num_experts;
+    return DISPATCH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -251,28 +281,37 @@ int dispatch_expand_layout(const dispatch_expand_problem_t* problem, const void*
                            const int32_t* recv_count, const dispatch_layout_t* out, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
     dispatch_problem_t p;
-    int rc = check_expand(problem, &p);
-    if (rc != DISPATCH_OK) return rc;
-    if (out == nullptr || !out->expert_count || !out->expert_psum || !out->status) return DISPATCH_ERR_NULL;
-    if (out->rank_count || out->rank_psum || out->rank_slot || out->rank_src_token_idx) return DISPATCH_ERR_ARG;
-    if (p.num_tokens > 0 && (!recv_topk_idx || !out->expert_slot)) return DISPATCH_ERR_NULL;
-    if (!recv_count) return DISPATCH_ERR_NULL;
-    if (p.recv_capacity_rows > 0 && !out->recv_src_token_idx) return DISPATCH_ERR_NULL;
-    if (workspace == nullptr) return DISPATCH_ERR_WORKSPACE;
-    if (recv_topk_idx && !aligned_to(recv_topk_idx, p.topk_idx_bytes)) return DISPATCH_ERR_ALIGN;
-    const void* ints[] = {recv_count, out->expert_count, out->expert_psum, out->expert_slot,
-                          out->recv_src_token_idx, out->status, out->expert_count_cumulative};
-    for (const void* q : ints)
-        if (q && !aligned_to(q, 4)) return DISPATCH_ERR_ALIGN;
-    if (!aligned_to(workspace, 256)) return DISPATCH_ERR_WORKSPACE;
-    const TileGeometry g = moe_dispatch::make_geometry(p.num_tokens, p.num_topk, p.num_experts, p.num_ranks);
-    if (workspace_bytes < moe_dispatch::workspace_bytes(g)) return DISPATCH_ERR_WORKSPACE;
+    TileGeometry g;
     moe_dispatch::ExpandView view;
-    view.recv_count = recv_count;
-    view.rows_per_source = problem->rows_per_source;
-    view.first_expert = problem->local_rank * (problem->num_experts / problem->num_ranks);
-    view.global_experts = problem->num_experts;
+    const int rc = check_expand_layout_args(problem, recv_topk_idx, recv_count, out, workspace, workspace_bytes,
+                                            &p, &g, &view);
+    if (rc != DISPATCH_OK) return rc;
     if (moe_dispatch::launch_layout(p, g, recv_topk_idx, *out, workspace, stream, &view) != hipSuccess)
+        return DISPATCH_ERR_HIP;
+    return DISPATCH_OK;
+}
+
+int dispatch_expand_layout_and_scatter(const dispatch_expand_problem_t* problem, const void* recv_topk_idx,
+                                       const int32_t* recv_count, const dispatch_layout_t* out, void* workspace,
+                                       size_t workspace_bytes, const void* recv_buf, const float* recv_sf_buf,
+                                       void* recv_x, float* recv_sf, hipStream_t stream) {
+    dispatch_problem_t p;
+    TileGeometry g;
+    moe_dispatch::ExpandView view;
+    int rc = check_expand_layout_args(problem, recv_topk_idx, recv_count, out, workspace, workspace_bytes, &p, &g,
+                                      &view);
+    if (rc != DISPATCH_OK) return rc;
+    rc = check_scatter_args(p, out, recv_buf, recv_sf_buf, nullptr, nullptr, recv_x, recv_sf);
+    if (rc != DISPATCH_OK) return rc;
+    if (moe_dispatch::fused_shape(g, p.row_bytes).fits) {
+        if (moe_dispatch::launch_fused_dispatch(p, g, recv_topk_idx, *out, workspace, recv_buf, recv_sf_buf, nullptr,
+                                                nullptr, recv_x, recv_sf, stream, &view) != hipSuccess)
+            return DISPATCH_ERR_HIP;
+        return DISPATCH_OK;
+    }
+    if (moe_dispatch::launch_layout(p, g, recv_topk_idx, *out, workspace, stream, &view) != hipSuccess ||
+        moe_dispatch::launch_scatter(p, *out, recv_buf, recv_sf_buf, nullptr, nullptr, recv_x, recv_sf, stream,
+                                     true) != hipSuccess)
         return DISPATCH_ERR_HIP;
     return DISPATCH_OK;
 }

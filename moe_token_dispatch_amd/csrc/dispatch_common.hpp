@@ -208,7 +208,8 @@ inline FusedShape fused_shape(const TileGeometry& g, int64_t row_bytes) {
 // launch_layout followed by launch_scatter.
 hipError_t launch_fused_dispatch(const dispatch_problem_t& p, const TileGeometry& g, const void* topk_idx,
                                  const dispatch_layout_t& out, void* workspace, const void* x, const float* x_sf,
-                                 void* rank_x, float* rank_sf, void* recv_x, float* recv_sf, hipStream_t stream);
+                                 void* rank_x, float* rank_sf, void* recv_x, float* recv_sf, hipStream_t stream,
+                                 const ExpandView* expand = nullptr);
 hipError_t launch_combine(int64_t num_tokens, int32_t num_topk, int64_t row_bytes, int64_t expert_rows,
                           const int32_t* expert_slot, const float* weights, const void* y, void* out,
                           hipStream_t stream);

@@ -362,7 +362,7 @@ enum AssignMode {
 template <int CH, int MODE, bool EXPAND, typename IdxT, bool FUSED = false>
 __global__ void __launch_bounds__(kLayoutThreads)
 assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispatch_layout_t out, RowArgs rows) {
-    static_assert(!FUSED || (MODE == kSingleTile && !EXPAND), "the fused dispatch covers one-tile batches");
+    static_assert(!FUSED || MODE == kSingleTile, "the fused dispatch ranks one tile");
     // LDS: [W][num_keys] wavefront counters, then totals[num_keys] and first[num_keys].
     extern __shared__ int lds[];
     __shared__ int scratch[2 * (kLayoutThreads / kWave + 1)];
@@ -651,7 +651,7 @@ hipError_t launch_chunks(const LayoutParams& p, const TileGeometry& g, const voi
     }
 }
 
-template <int CH, typename IdxT>
+template <int CH, bool EXPAND, typename IdxT>
 hipError_t launch_fused_typed(const LayoutParams& p, const TileGeometry& g, const void* topk,
                               const dispatch_layout_t& out, const Workspace& ws, const RowArgs& rows,
                               const FusedShape& f, hipStream_t stream) {
@@ -664,7 +664,7 @@ hipError_t launch_fused_typed(const LayoutParams& p, const TileGeometry& g, cons
     // chunks (no change to any count) and add their threads to the copies.
     const size_t lds = (size_t)(f.waves + 2) * g.num_keys * sizeof(int);
     void* args[] = {&idx, &pc, &wc, &oc, &rc};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, kSingleTile, false, IdxT, true>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, kSingleTile, EXPAND, IdxT, true>),
                            dim3((unsigned)f.groups), dim3(f.waves * kWave), args, lds, stream);
 }
 
@@ -719,9 +719,34 @@ hipError_t launch_layout(const dispatch_problem_t& prob, const TileGeometry& g, 
 }
 
 
+namespace {
+
+template <int CH, bool EXPAND>
+hipError_t launch_fused_width(bool wide, const LayoutParams& p, const TileGeometry& tile, const void* topk,
+                              const dispatch_layout_t& out, const Workspace& ws, const RowArgs& rows,
+                              const FusedShape& f, hipStream_t stream) {
+    return wide ? launch_fused_typed<CH, EXPAND, int64_t>(p, tile, topk, out, ws, rows, f, stream)
+                : launch_fused_typed<CH, EXPAND, int32_t>(p, tile, topk, out, ws, rows, f, stream);
+}
+
+template <bool EXPAND>
+hipError_t launch_fused_chunks(bool wide, const LayoutParams& p, const TileGeometry& tile, const void* topk,
+                               const dispatch_layout_t& out, const Workspace& ws, const RowArgs& rows,
+                               const FusedShape& f, hipStream_t stream) {
+    switch (f.chunks) {
+        case 1: return launch_fused_width<1, EXPAND>(wide, p, tile, topk, out, ws, rows, f, stream);
+        case 2: return launch_fused_width<2, EXPAND>(wide, p, tile, topk, out, ws, rows, f, stream);
+        case 4: return launch_fused_width<4, EXPAND>(wide, p, tile, topk, out, ws, rows, f, stream);
+        default: return launch_fused_width<8, EXPAND>(wide, p, tile, topk, out, ws, rows, f, stream);
+    }
+}
+
+}  // namespace
+
 hipError_t launch_fused_dispatch(const dispatch_problem_t& prob, const TileGeometry& g, const void* topk_idx,
                                  const dispatch_layout_t& out, void* workspace, const void* x, const float* x_sf,
-                                 void* rank_x, float* rank_sf, void* recv_x, float* recv_sf, hipStream_t stream) {
+                                 void* rank_x, float* rank_sf, void* recv_x, float* recv_sf, hipStream_t stream,
+                                 const ExpandView* expand) {
     const FusedShape f = fused_shape(g, prob.row_bytes);
     if (!f.fits) return hipErrorInvalidValue;
     // The one tile every workgroup ranks (the layout's own geometry may use
@@ -733,7 +758,13 @@ hipError_t launch_fused_dispatch(const dispatch_problem_t& prob, const TileGeome
     tile.tokens_per_tile = f.tile_waves * tile.tokens_per_wave;
     tile.num_tiles = 1;
     tile.column_scan = false;
-    const LayoutParams p = make_params(prob, tile);
+    LayoutParams p = make_params(prob, tile);
+    if (expand != nullptr) {
+        p.recv_count = expand->recv_count;
+        p.rows_per_source = expand->rows_per_source;
+        p.first_expert = expand->first_expert;
+        p.global_experts = expand->global_experts;
+    }
     const Workspace ws = make_workspace(g, workspace);
     RowArgs rows{};
     rows.x = static_cast<const u32x4*>(x);
@@ -750,16 +781,8 @@ hipError_t launch_fused_dispatch(const dispatch_problem_t& prob, const TileGeome
     rows.write_expert = (prob.flags & DISPATCH_EXPERT_MAJOR) != 0;
     rows.zero_pad = (prob.flags & DISPATCH_ZERO_PAD) != 0;
     const bool wide = prob.topk_idx_bytes == 8;
-    switch (f.chunks) {
-        case 1: return wide ? launch_fused_typed<1, int64_t>(p, tile, topk_idx, out, ws, rows, f, stream)
-                            : launch_fused_typed<1, int32_t>(p, tile, topk_idx, out, ws, rows, f, stream);
-        case 2: return wide ? launch_fused_typed<2, int64_t>(p, tile, topk_idx, out, ws, rows, f, stream)
-                            : launch_fused_typed<2, int32_t>(p, tile, topk_idx, out, ws, rows, f, stream);
-        case 4: return wide ? launch_fused_typed<4, int64_t>(p, tile, topk_idx, out, ws, rows, f, stream)
-                            : launch_fused_typed<4, int32_t>(p, tile, topk_idx, out, ws, rows, f, stream);
-        default: return wide ? launch_fused_typed<8, int64_t>(p, tile, topk_idx, out, ws, rows, f, stream)
-                             : launch_fused_typed<8, int32_t>(p, tile, topk_idx, out, ws, rows, f, stream);
-    }
+    if (expand != nullptr) return launch_fused_chunks<true>(wide, p, tile, topk_idx, out, ws, rows, f, stream);
+    return launch_fused_chunks<false>(wide, p, tile, topk_idx, out, ws, rows, f, stream);
 }
 
 }  // namespace moe_dispatch

@@ -223,6 +223,15 @@ def test_expand_host_errors():
     assert call(expand_only, 4096, 4096, None) == M.ERR_WORKSPACE
     assert lib.dispatch_expand_scatter(ctypes.byref(q), ctypes.byref(M.LayoutPtrs(*([4096] * 9))),
                                        4096, None, 4096, None, None) == M.ERR_ARG
+    # The one-call form makes both calls' checks.
+    both = lambda lay, topk, counts, ws, buf, rx: lib.dispatch_expand_layout_and_scatter(  # noqa: E731
+        ctypes.byref(q), topk, counts, ctypes.byref(lay), ws, 1 << 20, buf, None, rx, None, None)
+    assert both(expand_only, 4096, None, 4096, 4096, 4096) == M.ERR_NULL
+    assert both(M.LayoutPtrs(*([4096] * 9)), 4096, 4096, 4096, 4096, 4096) == M.ERR_ARG
+    assert both(expand_only, 4096, 4096, None, 4096, 4096) == M.ERR_WORKSPACE
+    assert both(expand_only, 4096, 4096, 4096, None, 4096) == M.ERR_NULL   # received rows required
+    assert both(expand_only, 4096, 4096, 4096, 4104, 4096) == M.ERR_ALIGN  # rows 16-byte aligned
+    assert both(expand_only, 4096, 4096, 4096, 4096, None) == M.ERR_NULL   # expert-major output required
 
 
 def test_combine_host_errors():

@@ -59,7 +59,8 @@ def _receive_buffer(sources, e, r, rank, slack, seed):
     return recv_topk, recv_buf, recv_sf, counts, m
 
 
-def _run_expand(recv_topk, recv_buf, recv_sf, counts, m, e, r, rank, a, topk_bytes=8, capacity=None):
+def _run_expand(recv_topk, recv_buf, recv_sf, counts, m, e, r, rank, a, topk_bytes=8, capacity=None,
+                combined=False):
     s_count, k = len(counts), recv_topk.shape[1]
     q = M.make_expand_problem(s_count, m, k, e, r, rank, a, topk_bytes, recv_buf.shape[1],
                               0 if recv_sf is None else recv_sf.shape[1], capacity)
@@ -79,8 +80,11 @@ def _run_expand(recv_topk, recv_buf, recv_sf, counts, m, e, r, rank, a, topk_byt
     counts_d = torch.from_numpy(counts.astype(np.int32)).to(H.DEVICE)
     buf_d = torch.from_numpy(recv_buf).to(H.DEVICE)
     sf_d = None if recv_sf is None else torch.from_numpy(recv_sf).to(H.DEVICE)
-    M.dispatch_expand_layout(q, topk_d, counts_d, lay, ws)
-    M.dispatch_expand_scatter(q, lay, buf_d, sf_d, recv_x, recv_sf_out)
+    if combined:
+        M.dispatch_expand_layout_and_scatter(q, topk_d, counts_d, lay, ws, buf_d, sf_d, recv_x, recv_sf_out)
+    else:
+        M.dispatch_expand_layout(q, topk_d, counts_d, lay, ws)
+        M.dispatch_expand_scatter(q, lay, buf_d, sf_d, recv_x, recv_sf_out)
     torch.cuda.synchronize()
     return q, lay, recv_x, recv_sf_out
 
@@ -254,3 +258,38 @@ def test_expand_expert_count_cumulative():
         M.dispatch_expand_layout(q, topk_d, counts_d, lay, ws, expert_count_cumulative=cum)
     torch.cuda.synchronize()
     assert np.array_equal(cum.cpu().numpy(), 5 + 2 * ref.expert_count.astype(np.int64))
+
+
+# dispatch_expand_layout_and_scatter: one kernel for a small receive buffer
+# (S * M * K up to 3072 entries), else the layout and scatter kernels.
+@pytest.mark.parametrize("s_count,t,a,dtype,with_sf,rank", [
+    (8, 40, 1, "bf16", False, 3),    # 8 x ~30 rows x top-8: one kernel
+    (3, 100, 16, "fp8", True, 1),    # one kernel, pads and scale factors
+    (1, 300, 4, "bf16", False, 0),   # one kernel
+    (4, 300, 2, "fp8", True, 2),     # past 3072 entries: the layout and scatter kernels
+])
+def test_expand_layout_and_scatter_in_one_call(s_count, t, a, dtype, with_sf, rank):
+    _banner(f"one call: S={s_count} T={t} A={a} {dtype} sf={with_sf} rank={rank}")
+    e, r, k = 64, 4, 8
+    sources = [_source(70 + i, t, 128, dtype, with_sf, e, r, k, 0.05) for i in range(s_count)]
+    recv_topk, recv_buf, recv_sf, counts, m = _receive_buffer(sources, e, r, rank, 3, 71)
+    ref = oracle.expand_layout(recv_topk, counts, s_count, m, e, r, rank, a)
+    q, lay, recv_x, recv_sf_out = _run_expand(recv_topk, recv_buf, recv_sf, counts, m, e, r, rank, a,
+                                              combined=True)
+    _compare(lay, recv_x, recv_sf_out, ref, recv_buf, recv_sf)
+
+
+def test_expand_one_call_bad_count_writes_nothing():
+    _banner("one call: bad count")
+    e, r, k = 32, 4, 4
+    sources = [_source(80 + i, 60, 64, "bf16", False, e, r, k, 0.0) for i in range(2)]
+    recv_topk, recv_buf, recv_sf, counts, m = _receive_buffer(sources, e, r, 1, 2, 81)
+    bad = counts.copy()
+    bad[1] = m + 1
+    ref = oracle.expand_layout(recv_topk, bad, 2, m, e, r, 1, 1)
+    # The count past M flags BAD_COUNT (and, through the junk rows it then
+    # covers, possibly BAD_EXPERT too); either way nothing is written.
+    assert ref.status & oracle.BAD_COUNT
+    q, lay, recv_x, _ = _run_expand(recv_topk, recv_buf, None, bad, m, e, r, 1, 1, combined=True)
+    _compare(lay, recv_x, None, ref, recv_buf, None)
+    assert np.all(recv_x.cpu().numpy() == H.ROW_FILL)
