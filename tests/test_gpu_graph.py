@@ -22,10 +22,14 @@ from tests import gpu_harness as H
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("dtype,with_sf,alignment", [("bf16", False, 1), ("fp8", True, 16)])
-def test_captured_dispatch_replays_match_oracle(dtype, with_sf, alignment):
-    print(f"\n[gpu-graph] capture dtype={dtype} sf={with_sf} A={alignment}", flush=True)
-    base = W.Workload("graph", 1500, 512, dtype, with_sf, 64, 8, 8, mask_frac=0.05, alignment=alignment, seed=31)
+# The layout and scatter calls on a batch of several tiles, and the combined
+# call on small batches, where it is one kernel.
+@pytest.mark.parametrize("dtype,with_sf,alignment,t,combined", [
+    ("bf16", False, 1, 1500, False), ("fp8", True, 16, 1500, False),
+    ("bf16", False, 1, 200, True), ("fp8", True, 16, 300, True)])
+def test_captured_dispatch_replays_match_oracle(dtype, with_sf, alignment, t, combined):
+    print(f"\n[gpu-graph] capture dtype={dtype} sf={with_sf} A={alignment} T={t} combined={combined}", flush=True)
+    base = W.Workload("graph", t, 512, dtype, with_sf, 64, 8, 8, mask_frac=0.05, alignment=alignment, seed=31)
     t, k, e, r = base.num_tokens, base.num_topk, base.num_experts, base.num_ranks
     prob = M.make_problem(t, k, e, r, alignment, 8, base.row_bytes, base.sf_per_token)
     lay = M.alloc_layout(prob, H.DEVICE)
@@ -55,9 +59,16 @@ def test_captured_dispatch_replays_match_oracle(dtype, with_sf, alignment):
     wts_d = torch.zeros((t, k), dtype=torch.float32, device=H.DEVICE)
     out_d = torch.zeros((t, base.hidden), dtype=torch.bfloat16, device=H.DEVICE)
 
+    if combined:
+        assert M.dispatch_kernel_count(prob)[1] == 1
+
     def step():
-        M.dispatch_layout(prob, topk_d, lay, ws)
-        M.dispatch_scatter(prob, lay, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x, rows.recv_sf)
+        if combined:
+            M.dispatch_layout_and_scatter(prob, topk_d, lay, ws, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x,
+                                          rows.recv_sf)
+        else:
+            M.dispatch_layout(prob, topk_d, lay, ws)
+            M.dispatch_scatter(prob, lay, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x, rows.recv_sf)
         if combine:
             M.dispatch_combine(lay.expert_slot.view(t, k), wts_d, rows.recv_x.view(torch.bfloat16), out_d)
 
