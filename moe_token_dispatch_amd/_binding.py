@@ -559,6 +559,56 @@ def dispatch_expand_scatter(problem: ExpandProblem, layout: ExpandLayoutTensors,
         raise DispatchError(rc, "dispatch_expand_scatter")
 
 
+class ExpandPlan:
+    """A prepared receiver-side expand, like Plan: the tensors and the stream
+    are checked once and the C arguments built once. ``layout()`` enqueues
+    dispatch_expand_layout, ``scatter()`` dispatch_expand_scatter and
+    ``__call__`` both as one dispatch_expand_layout_and_scatter call."""
+
+    def __init__(self, problem: ExpandProblem, recv_topk_idx: torch.Tensor, recv_count: torch.Tensor,
+                 layout: ExpandLayoutTensors, workspace: torch.Tensor, recv_buf: torch.Tensor,
+                 recv_sf_buf: Optional[torch.Tensor], recv_x: torch.Tensor, recv_sf: Optional[torch.Tensor],
+                 stream: Optional[torch.cuda.Stream] = None,
+                 expert_count_cumulative: Optional[torch.Tensor] = None):
+        _check_device_tensor(recv_topk_idx, "recv_topk_idx")
+        if recv_topk_idx.element_size() != problem.topk_idx_bytes:
+            raise ValueError("recv_topk_idx element width does not match problem.topk_idx_bytes")
+        _check_device_tensor(recv_count, "recv_count", torch.int32)
+        _check_device_tensor(workspace, "workspace")
+        for f in dataclasses.fields(layout):
+            _check_device_tensor(getattr(layout, f.name), f.name, torch.int32)
+        _check_cumulative(expert_count_cumulative, problem.num_experts // problem.num_ranks)
+        _check_device_tensor(recv_buf, "recv_buf")
+        for name, t in (("recv_sf_buf", recv_sf_buf), ("recv_x", recv_x), ("recv_sf", recv_sf)):
+            if t is not None:
+                _check_device_tensor(t, name)
+        self._lib = load_library()
+        self._keep = (problem, recv_topk_idx, recv_count, layout, workspace, recv_buf, recv_sf_buf, recv_x, recv_sf,
+                      expert_count_cumulative)
+        self._lay = layout.ptrs(expert_count_cumulative)
+        handle = _stream_handle(stream, recv_topk_idx.device)
+        rows = (_ptr(recv_buf), _ptr(recv_sf_buf), _ptr(recv_x), _ptr(recv_sf))
+        self._layout_args = (ctypes.byref(problem), _ptr(recv_topk_idx), _ptr(recv_count), ctypes.byref(self._lay),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(), handle)
+        self._scatter_args = (ctypes.byref(problem), ctypes.byref(self._lay), *rows, handle)
+        self._both_args = (*self._layout_args[:-1], *rows, handle)
+
+    def layout(self) -> None:
+        rc = self._lib.dispatch_expand_layout(*self._layout_args)
+        if rc:
+            raise DispatchError(rc, "dispatch_expand_layout")
+
+    def scatter(self) -> None:
+        rc = self._lib.dispatch_expand_scatter(*self._scatter_args)
+        if rc:
+            raise DispatchError(rc, "dispatch_expand_scatter")
+
+    def __call__(self) -> None:
+        rc = self._lib.dispatch_expand_layout_and_scatter(*self._both_args)
+        if rc:
+            raise DispatchError(rc, "dispatch_expand_layout_and_scatter")
+
+
 # ------------------------------------------------------------------- combine
 
 
@@ -577,3 +627,28 @@ def dispatch_combine(expert_slot: torch.Tensor, topk_weights: torch.Tensor, y: t
                                          _ptr(out), _stream_handle(stream, y.device))
     if rc:
         raise DispatchError(rc, "dispatch_combine")
+
+
+class CombinePlan:
+    """A prepared combine: the tensors and the stream are checked once and the
+    C arguments built once, so each call is a single C call."""
+
+    def __init__(self, expert_slot: torch.Tensor, topk_weights: torch.Tensor, y: torch.Tensor, out: torch.Tensor,
+                 stream: Optional[torch.cuda.Stream] = None):
+        _check_device_tensor(expert_slot, "expert_slot", torch.int32)
+        _check_device_tensor(topk_weights, "topk_weights", torch.float32)
+        _check_device_tensor(y, "y", torch.bfloat16)
+        _check_device_tensor(out, "out", torch.bfloat16)
+        t, k = expert_slot.shape
+        if topk_weights.shape != (t, k) or out.shape[0] != t or out.shape[1] != y.shape[1]:
+            raise ValueError("combine: shapes do not line up")
+        self._lib = load_library()
+        self._problem = CombineProblem(t, k, 0, y.shape[1], y.shape[0])
+        self._keep = (expert_slot, topk_weights, y, out)
+        self._args = (ctypes.byref(self._problem), _ptr(expert_slot), _ptr(topk_weights), _ptr(y), _ptr(out),
+                      _stream_handle(stream, y.device))
+
+    def __call__(self) -> None:
+        rc = self._lib.dispatch_combine(*self._args)
+        if rc:
+            raise DispatchError(rc, "dispatch_combine")

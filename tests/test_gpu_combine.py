@@ -179,3 +179,19 @@ def test_combine_random_problem(seed):
     w, topk, ref, y, wts = _combine_inputs(t, min(k, e), e, hidden, mask, seed=300 + seed)
     got = _run_combine(ref.expert_slot, wts, y)
     _check(got, y.view(torch.int16).numpy().view(np.uint16), wts, ref.expert_slot)
+
+
+def test_combine_plan_equals_the_direct_call():
+    _banner("combine plan")
+    w, topk, ref, y, wts = _combine_inputs(300, 8, 64, 1024, 0.1, seed=16)
+    slots_d = torch.from_numpy(np.ascontiguousarray(ref.expert_slot, dtype=np.int32)).to(H.DEVICE)
+    wts_d = torch.from_numpy(np.ascontiguousarray(wts, dtype=np.float32)).to(H.DEVICE)
+    y_d = y.to(H.DEVICE)
+    out = torch.full((300, 1024), -123.0, dtype=torch.bfloat16, device=H.DEVICE)
+    plan = M.CombinePlan(slots_d, wts_d, y_d, out)
+    plan()
+    plan()
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, _run_combine(ref.expert_slot, wts, y))
+    _check(got, y.view(torch.int16).numpy().view(np.uint16), wts, ref.expert_slot)

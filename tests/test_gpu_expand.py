@@ -293,3 +293,31 @@ def test_expand_one_call_bad_count_writes_nothing():
     q, lay, recv_x, _ = _run_expand(recv_topk, recv_buf, None, bad, m, e, r, 1, 1, combined=True)
     _compare(lay, recv_x, None, ref, recv_buf, None)
     assert np.all(recv_x.cpu().numpy() == H.ROW_FILL)
+
+
+def test_expand_plan_layout_scatter_and_one_call():
+    """The prepared expand: two calls, then the one call, both equal the oracle."""
+    _banner("expand plan")
+    e, r, k, rank, a = 64, 4, 8, 2, 4
+    sources = [_source(90 + i, 120, 128, "fp8", True, e, r, k, 0.05) for i in range(3)]
+    recv_topk, recv_buf, recv_sf, counts, m = _receive_buffer(sources, e, r, rank, 2, 91)
+    ref = oracle.expand_layout(recv_topk, counts, 3, m, e, r, rank, a)
+    q = M.make_expand_problem(3, m, k, e, r, rank, a, 8, recv_buf.shape[1], recv_sf.shape[1])
+    lay, ws = M.alloc_expand_layout(q, H.DEVICE), M.alloc_expand_workspace(q, H.DEVICE)
+    cap = max(q.recv_capacity_rows, 1)
+    for one_call in (False, True):
+        for f in dataclasses.fields(lay):
+            getattr(lay, f.name).fill_(H.CANARY)
+        recv_x = torch.full((cap, recv_buf.shape[1]), H.ROW_FILL, dtype=torch.uint8, device=H.DEVICE)
+        recv_sf_out = torch.empty((cap, recv_sf.shape[1]), dtype=torch.float32, device=H.DEVICE)
+        recv_sf_out.view(torch.uint8).fill_(H.ROW_FILL)
+        plan = M.ExpandPlan(q, torch.from_numpy(recv_topk).to(H.DEVICE), torch.from_numpy(counts).to(H.DEVICE), lay,
+                            ws, torch.from_numpy(recv_buf).to(H.DEVICE), torch.from_numpy(recv_sf).to(H.DEVICE),
+                            recv_x, recv_sf_out)
+        if one_call:
+            plan()
+        else:
+            plan.layout()
+            plan.scatter()
+        torch.cuda.synchronize()
+        _compare(lay, recv_x, recv_sf_out, ref, recv_buf, recv_sf)
