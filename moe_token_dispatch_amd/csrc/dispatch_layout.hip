@@ -350,9 +350,10 @@ enum AssignMode {
     kSingleTile = 2,      // one tile holds every pair: its own wavefront counters (no count kernel)
 };
 
-// FUSED (with kSingleTile only): the whole dispatch of a batch that fits one
-// tile in one launch. Every workgroup ranks the entire tile itself (a few
-// microseconds of redundant ALU work, no communication between workgroups).
+// FUSED (with kSingleTile only): the whole dispatch of a small batch in one
+// launch. The batch is one tile of up to 8 chunks per wavefront, and every
+// workgroup ranks the entire tile itself (a few microseconds of redundant ALU
+// work, no communication between workgroups).
 // Workgroup 0 writes the counts, psums and status. Workgroup g copies the row
 // units [g * units_per_group, (g + 1) * units_per_group), a unit being one
 // token's 1 KB row segment, to the token's destination rows; it writes the
@@ -376,7 +377,7 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
     // The workgroup that writes the counts, psums and status.
     const bool writes_totals = FUSED ? blockIdx.x == 0 : tile == 0;
     // FUSED: this workgroup's row units [unit0, unit1) and the tokens they
-    // belong to, [tok_first, tok_first + its slot rows).
+    // belong to, [tok_first, tok_end).
     const int64_t segs = FUSED ? rows.segments : 1;
     const int64_t unit0 = FUSED ? min((int64_t)blockIdx.x * rows.units_per_group, p.num_tokens * segs) : 0;
     const int64_t unit1 = FUSED ? min(unit0 + rows.units_per_group, p.num_tokens * segs) : 0;
