@@ -64,10 +64,19 @@ def test_largest_one_tile_batch_per_topk(k, t, e, r):
     _fused(_topk(32 + k, t, k, e, 0.1), e, r, 3, row_bytes=48, seed=k)
 
 
-@pytest.mark.parametrize("row_bytes,s", [(16, 0), (4096, 0), (14336, 0), (7168, 56), (112, 1)])
+# Rows of whole 1 KB units, rows whose last unit is partial (1040 and 2064 B),
+# and rows shorter than one unit.
+@pytest.mark.parametrize("row_bytes,s", [(16, 0), (4096, 0), (14336, 0), (7168, 56), (112, 1), (1040, 0),
+                                         (2064, 3)])
 def test_row_and_scale_factor_widths(row_bytes, s):
     _banner(f"row_bytes={row_bytes} S={s}")
     _fused(_topk(33, 256, 8, 256, 0.05), 256, 8, 1, row_bytes=row_bytes, s=s, seed=3)
+
+
+def test_wide_pad_rows_with_scale_factors():
+    """Alignment 128 on 7 KB rows with 56 scale factors: many zeroed pad rows."""
+    _banner("A=128, 7168 B rows, S=56")
+    _fused(_topk(43, 256, 8, 256, 0.05), 256, 8, 128, row_bytes=7168, s=56, seed=10)
 
 
 @pytest.mark.parametrize("a", [1, 2, 3, 128])
