@@ -60,6 +60,9 @@ def parse_args():
     ap.add_argument("--sources", type=int, default=8, help="sources for --expand")
     ap.add_argument("--combine", action="store_true",
                     help="measure the combine instead: weighted gather of the expert-major rows back to tokens")
+    ap.add_argument("--latency", action="store_true",
+                    help="per-step latency of small (decode-sized) batches of the workload's shape: "
+                         "the one call against the layout and scatter calls")
     return ap.parse_args()
 
 
@@ -369,6 +372,55 @@ def combine_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def latency_bench(args):
+    """Microseconds per step for small batches of the workload's shape (its
+    experts, ranks, top-k and row width), through a prepared plan: the one
+    call (one kernel up to 3072 (token, k) pairs) and the layout and scatter
+    calls. HIP events on the launch stream around many back-to-back steps."""
+    import dataclasses
+
+    import torch
+
+    import moe_token_dispatch_amd as M
+    import workloads as W
+
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream(dev)
+    base = W.get(args.workload or W.METRIC_WORKLOAD)
+    reps = max(100, args.steps)
+
+    def per_step_us(fn):
+        for _ in range(max(20, args.warmup)):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    rows_out = []
+    for t in (1, 16, 64, 128, 256, 384):
+        w = dataclasses.replace(base, num_tokens=t)
+        inp = W.make_inputs(w)
+        prob = M.make_problem(t, w.num_topk, w.num_experts, w.num_ranks, w.alignment, 8, w.row_bytes,
+                              w.sf_per_token)
+        lay, ws, rows = M.alloc_layout(prob, dev), M.alloc_workspace(prob, dev), M.alloc_rows(prob, dev)
+        sf = None if inp.x_sf is None else torch.from_numpy(inp.x_sf).to(dev)
+        plan = M.Plan(prob, torch.from_numpy(inp.topk_idx).to(dev), lay, ws, inp.x.view(torch.uint8).to(dev), sf,
+                      rows, stream)
+        two = per_step_us(lambda: (plan.layout(), plan.scatter()))
+        one = per_step_us(plan)
+        rows_out.append({"tokens": t, "kernels_one_call": M.dispatch_kernel_count(prob)[1],
+                         "us_two_calls": round(two, 2), "us_one_call": round(one, 2)})
+    print(json.dumps({"metric": "dispatch step latency of small batches", "unit": "us per step",
+                      "higher_is_better": False, "workload": base.name, "steps": reps,
+                      "what": "HIP events around back-to-back steps of a prepared plan", "batches": rows_out}),
+          flush=True)
+
+
 def graph_step(args, dev, stream, prob, topk_d, lay, ws, x_d, sf_d, rows, total_b):
     """The same step captured once into a HIP graph and replayed: the kernels
     and buffers are the eager step's; only the launch path differs."""
@@ -415,6 +467,9 @@ def main():
         return
     if args.combine:
         combine_bench(args)
+        return
+    if args.latency:
+        latency_bench(args)
         return
 
     import numpy as np

@@ -224,7 +224,7 @@ int dispatch_kernel_count(const dispatch_problem_t* problem, int* layout_kernels
     const int layout = g.num_tiles == 1 && !g.column_scan ? 1 : (g.column_scan ? 3 : 2);
     if (layout_kernels) *layout_kernels = layout;
     if (layout_and_scatter_kernels)
-        *layout_and_scatter_kernels = moe_dispatch::fused_shape(g, problem->row_bytes).fits ? 1 : layout + 1;
+        *layout_and_scatter_kernels = moe_dispatch::fused_shape(*problem, g).fits ? 1 : layout + 1;
     return DISPATCH_OK;
 }
 
@@ -238,7 +238,7 @@ int dispatch_layout_and_scatter(const dispatch_problem_t* problem, const void* t
     rc = check_scatter_args(*problem, out, x, x_sf, rank_x, rank_sf, recv_x, recv_sf);
     if (rc != DISPATCH_OK) return rc;
     const dispatch_problem_t& p = *problem;
-    if (moe_dispatch::fused_shape(g, p.row_bytes).fits) {
+    if (moe_dispatch::fused_shape(p, g).fits) {
         if (moe_dispatch::launch_fused_dispatch(p, g, topk_idx, *out, workspace, x, x_sf, rank_x, rank_sf, recv_x,
                                                 recv_sf, stream) != hipSuccess)
             return DISPATCH_ERR_HIP;
@@ -303,7 +303,7 @@ int dispatch_expand_layout_and_scatter(const dispatch_expand_problem_t* problem,
     if (rc != DISPATCH_OK) return rc;
     rc = check_scatter_args(p, out, recv_buf, recv_sf_buf, nullptr, nullptr, recv_x, recv_sf);
     if (rc != DISPATCH_OK) return rc;
-    if (moe_dispatch::fused_shape(g, p.row_bytes).fits) {
+    if (moe_dispatch::fused_shape(p, g).fits) {
         if (moe_dispatch::launch_fused_dispatch(p, g, recv_topk_idx, *out, workspace, recv_buf, recv_sf_buf, nullptr,
                                                 nullptr, recv_x, recv_sf, stream, &view) != hipSuccess)
             return DISPATCH_ERR_HIP;

@@ -159,6 +159,10 @@ constexpr int kFusedMaxChunks = 8;        // chunks per wavefront of the one til
 // than the layout and scatter launches it saves (at 4096 pairs: 14.0 against
 // 12.6 us for 256-byte rows, 29.2 against 29.6 us for 14 KB rows).
 constexpr int64_t kFusedMaxBatchPairs = 3072;
+// The most (expert, pad row) items, E * (A - 1), the one kernel walks, and
+// the consecutive pad rows it deals to a workgroup at a time.
+constexpr int64_t kFusedMaxPadItems = int64_t(1) << 20;
+constexpr int kFusedPadChunk = 8;
 constexpr int kFusedStoresPerThread = 8;  // 16-byte stores per thread that size the wavefront count
 struct FusedShape {
     bool fits;
@@ -169,9 +173,14 @@ struct FusedShape {
     int32_t segments;    // 1 KB units per row
     int32_t waves;       // wavefronts per workgroup (>= tile_waves)
 };
-inline FusedShape fused_shape(const TileGeometry& g, int64_t row_bytes) {
+inline FusedShape fused_shape(const dispatch_problem_t& prob, const TileGeometry& g) {
     FusedShape f{};
     const int64_t t = g.num_tokens;
+    const int64_t row_bytes = prob.row_bytes;
+    // Zeroed pad rows: up to A - 1 per expert, dealt over all the workgroups.
+    const bool pads = (prob.flags & DISPATCH_EXPERT_MAJOR) && (prob.flags & DISPATCH_ZERO_PAD) &&
+                      prob.expert_alignment > 1;
+    const int64_t pad_items = pads ? (int64_t)prob.num_experts * (prob.expert_alignment - 1) : 0;
     // The tile: the fewest chunks per wavefront that fit the batch in the
     // wavefronts LDS allows, then just enough wavefronts.
     const int64_t tpc = g.tokens_per_chunk;
@@ -189,6 +198,7 @@ inline FusedShape fused_shape(const TileGeometry& g, int64_t row_bytes) {
     const int64_t per = (f.segments + 1) / 2;
     const int64_t want = (units + per - 1) / per;
     f.groups = want < 1 ? 1 : (want < kFusedGroups ? want : kFusedGroups);
+    if (pads) f.groups = kFusedGroups;  // the pad rows need the whole GPU
     f.units_per_group = (int32_t)(units < 1 ? 1 : (units + f.groups - 1) / f.groups);
     // A unit range touches at most this many tokens.
     const int64_t tokens = f.segments == 1 ? f.units_per_group : (f.units_per_group + f.segments - 1) / f.segments + 1;
@@ -201,10 +211,10 @@ inline FusedShape fused_shape(const TileGeometry& g, int64_t row_bytes) {
     if (w < f.tile_waves) w = f.tile_waves;
     f.waves = (int32_t)w;
     f.fits = f.tile_waves <= g.max_waves && tokens * g.num_topk <= kFusedMaxPairs &&
-             t * g.num_topk <= kFusedMaxBatchPairs;
+             t * g.num_topk <= kFusedMaxBatchPairs && pad_items <= kFusedMaxPadItems;
     return f;
 }
-// Requires fused_shape(g, row_bytes).fits; the outputs are those of
+// Requires fused_shape(p, g).fits; the outputs are those of
 // launch_layout followed by launch_scatter.
 hipError_t launch_fused_dispatch(const dispatch_problem_t& p, const TileGeometry& g, const void* topk_idx,
                                  const dispatch_layout_t& out, void* workspace, const void* x, const float* x_sf,

@@ -588,12 +588,18 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
                 }
             }
         }
-        // Pad rows are zero bytes (section 7.3).
+        // Pad rows are zero bytes (section 7.3). Expert e has at most A - 1 of
+        // them, cut into chunks of kFusedPadChunk consecutive rows; the chunks
+        // are dealt round-robin over all workgroups, so the pads of a few
+        // experts still spread out, and each chunk is written contiguously.
         if (rows.write_expert && rows.zero_pad && p.alignment > 1) {
             const u32x4 zero = {0u, 0u, 0u, 0u};
-            for (int e = blockIdx.x; e < E; e += gridDim.x) {
-                const int64_t lo = first[e] + totals[e];
-                const int64_t hi = min((int64_t)(e + 1 < E ? first[e + 1] : recv_rows), p.recv_capacity);
+            const int64_t chunks = (p.alignment - 1 + kFusedPadChunk - 1) / kFusedPadChunk;
+            for (int64_t c = blockIdx.x; c < (int64_t)E * chunks; c += gridDim.x) {
+                const int e = (int)(c / chunks);
+                const int64_t lo = first[e] + totals[e] + (c - e * chunks) * kFusedPadChunk;
+                const int64_t hi = min(min(lo + kFusedPadChunk, (int64_t)(e + 1 < E ? first[e + 1] : recv_rows)),
+                                       p.recv_capacity);
                 for (int64_t row = lo; row < hi; ++row) {
                     const RowWriter dst(rows.recv_x + row * nv, (int)(nv * 16));
                     for (int64_t i = tid; i < nv; i += nthreads) dst.store(i, zero);
@@ -748,7 +754,7 @@ hipError_t launch_fused_dispatch(const dispatch_problem_t& prob, const TileGeome
                                  const dispatch_layout_t& out, void* workspace, const void* x, const float* x_sf,
                                  void* rank_x, float* rank_sf, void* recv_x, float* recv_sf, hipStream_t stream,
                                  const ExpandView* expand) {
-    const FusedShape f = fused_shape(g, prob.row_bytes);
+    const FusedShape f = fused_shape(prob, g);
     if (!f.fits) return hipErrorInvalidValue;
     // The one tile every workgroup ranks (the layout's own geometry may use
     // several tiles for this batch).

@@ -25,7 +25,7 @@
 namespace moe_dispatch {
 namespace {
 
-constexpr int kPadRowsPerWave = 8;
+constexpr int kPadRowsPerWave = 1;
 // V, the 16-byte vectors per lane of one row segment, follows the stores per
 // loaded row (measured on MI355X): with many destinations per row (dispatch:
 // K expert rows and the rank rows) one vector per lane, i.e. many short
