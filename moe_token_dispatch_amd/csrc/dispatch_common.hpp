@@ -203,9 +203,15 @@ inline FusedShape fused_shape(const dispatch_problem_t& prob, const TileGeometry
     // A unit range touches at most this many tokens.
     const int64_t tokens = f.segments == 1 ? f.units_per_group : (f.units_per_group + f.segments - 1) / f.segments + 1;
     // Enough wavefronts for the copies (K expert rows and one rank row per
-    // unit), at least those the tile's ranking uses, at most what LDS allows.
+    // unit) and for this workgroup's share of the pad rows (only experts that
+    // receive a pair have any: at most min(E, T*K) of them), at least those
+    // the tile's ranking uses, at most what LDS allows.
     const int64_t unit_vecs = vecs < 64 ? vecs : 64;
-    const int64_t stores = (int64_t)f.units_per_group * unit_vecs * (g.num_topk + 1);
+    const int64_t pairs = t * g.num_topk;
+    const int64_t pad_rows = pads ? (pairs < prob.num_experts ? pairs : prob.num_experts) *
+                                        (prob.expert_alignment - 1) : 0;
+    const int64_t stores = (int64_t)f.units_per_group * unit_vecs * (g.num_topk + 1) +
+                           (pad_rows + f.groups - 1) / f.groups * (vecs < 1 ? 1 : vecs);
     int64_t w = (stores + kWave * kFusedStoresPerThread - 1) / (kWave * kFusedStoresPerThread);
     if (w > g.max_waves) w = g.max_waves;
     if (w < f.tile_waves) w = f.tile_waves;

@@ -12,7 +12,7 @@
 // page's sender warp, here to local rows). Destination slots come from the
 // layout's expert_slot / rank_slot, which are wavefront-uniform, so the
 // destination loop runs on scalar registers. Pad rows are cleared by extra
-// wavefronts after the token wavefronts, a few rows each.
+// wavefronts after the token wavefronts, one row each.
 //
 // Row stores go through a buffer resource that spans exactly one destination
 // row, so the hardware drops any offset outside that row, and carry the
@@ -25,7 +25,7 @@
 namespace moe_dispatch {
 namespace {
 
-constexpr int kPadRowsPerWave = 1;
+static_assert(DISPATCH_MAX_EXPERTS <= kWave * kWave, "expert_of_row searches two rounds of 64 samples");
 // V, the 16-byte vectors per lane of one row segment, follows the stores per
 // loaded row (measured on MI355X): with many destinations per row (dispatch:
 // K expert rows and the rank rows) one vector per lane, i.e. many short
@@ -48,7 +48,9 @@ struct ScatterParams {
     int32_t segments;        // row segments per token
     int32_t sf_per_token;
     int32_t num_experts;
-    int32_t pad_waves_per_expert;
+    int32_t pad_waves_per_expert;  // alignment - 1 with pads, else 1
+    int32_t pad_by_block;          // pad wavefronts mapped per row block (else per expert)
+    int32_t alignment;
     int32_t write_rank;      // rank_x / rank_sf requested
     int32_t write_expert;    // recv_x / recv_sf requested
 };
@@ -112,22 +114,57 @@ __device__ __forceinline__ void copy_token(const u32x4* __restrict__ x, const ui
     }
 }
 
+// The expert whose receive rows hold `row`: the largest e with
+// expert_psum[e] <= row, found by the whole wavefront in two rounds over the
+// non-decreasing psums (64 evenly spaced samples, then the chunk between two
+// samples), since E <= 64 * 64. -1 if expert_psum[0] > row (never for a
+// valid layout, whose psums start at 0).
+__device__ __forceinline__ int expert_of_row(int64_t row, int num_experts, int lane,
+                                             const int32_t* __restrict__ expert_psum) {
+    const int step = (num_experts + kWave - 1) / kWave;
+    const int i1 = lane * step;
+    const int c1 = __popcll(__ballot(i1 < num_experts && expert_psum[i1] <= row));
+    if (c1 == 0) return -1;
+    const int base = (c1 - 1) * step;
+    const int i2 = base + lane;
+    return base + __popcll(__ballot(lane < step && i2 < num_experts && expert_psum[i2] <= row)) - 1;
+}
+
+// Pad rows (section 7.3): the rows after an expert's routed rows up to its
+// aligned end, at most alignment - 1 of them, all in the expert's last
+// block of `alignment` rows (the aligned psums are multiples of it). One
+// wavefront zeroes one row, under one of two mappings; the launcher takes the
+// one with fewer wavefronts:
+//  - per expert: wavefront (e, j) zeroes the j-th pad row of expert e;
+//  - per block: wavefront (b, j) zeroes row b * alignment + 1 + j if block b
+//    is the last of its expert and that row is past the expert's routed rows.
+//    Routed rows span at most min(E, T*K) + T*K / alignment blocks, far fewer
+//    than E experts when the batch is small: then most per-expert wavefronts
+//    would find no pad row and only cost their launch.
 __device__ __forceinline__ void zero_pads(const ScatterParams& p, int64_t pad_wave, int lane,
                                           const int32_t* __restrict__ expert_count,
                                           const int32_t* __restrict__ expert_psum,
                                           u32x4* __restrict__ recv_x, uint32_t* __restrict__ recv_sf) {
-    const int e = (int)(pad_wave / p.pad_waves_per_expert);
-    if (e >= p.num_experts) return;
-    const int sub = (int)(pad_wave - (int64_t)e * p.pad_waves_per_expert);
-    const int64_t first = (int64_t)expert_psum[e] + expert_count[e] + (int64_t)sub * kPadRowsPerWave;
-    const int64_t end = min(min(first + kPadRowsPerWave, (int64_t)expert_psum[e + 1]), p.recv_capacity);
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    const int S = p.sf_per_token;
-    for (int64_t row = first; row < end; ++row) {
-        const RowWriter dst(recv_x + row * p.row_vecs, (int)(p.row_vecs * 16));
-        for (int64_t i = lane; i < p.row_vecs; i += kWave) dst.store(i, zero);
-        for (int i = lane; i < S; i += kWave) recv_sf[row * S + i] = 0u;
+    int64_t row;
+    int e;
+    if (p.pad_by_block) {
+        const int64_t b = pad_wave / p.pad_waves_per_expert;
+        const int64_t block0 = b * p.alignment;
+        e = expert_of_row(block0, p.num_experts, lane, expert_psum);
+        if (e < 0 || expert_psum[e + 1] != block0 + p.alignment) return;  // not the expert's last block
+        row = block0 + 1 + (pad_wave - b * p.pad_waves_per_expert);
+    } else {
+        e = (int)(pad_wave / p.pad_waves_per_expert);
+        if (e >= p.num_experts) return;
+        row = (int64_t)expert_psum[e] + expert_count[e] + (pad_wave - (int64_t)e * p.pad_waves_per_expert);
     }
+    if (row < (int64_t)expert_psum[e] + expert_count[e] || row >= expert_psum[e + 1] || row >= p.recv_capacity)
+        return;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const RowWriter dst(recv_x + row * p.row_vecs, (int)(p.row_vecs * 16));
+    for (int64_t i = lane; i < p.row_vecs; i += kWave) dst.store(i, zero);
+    const int S = p.sf_per_token;
+    for (int i = lane; i < S; i += kWave) recv_sf[row * S + i] = 0u;
 }
 
 template <int V, int W>
@@ -186,8 +223,16 @@ hipError_t launch_scatter(const dispatch_problem_t& prob, const dispatch_layout_
     p.write_rank = (prob.flags & DISPATCH_RANK_CONTIG) != 0;
     p.write_expert = (prob.flags & DISPATCH_EXPERT_MAJOR) != 0;
     const bool pads = p.write_expert && (prob.flags & DISPATCH_ZERO_PAD) && prob.expert_alignment > 1;
-    p.pad_waves_per_expert = pads ? (prob.expert_alignment - 1 + kPadRowsPerWave - 1) / kPadRowsPerWave : 1;
-    const int64_t pad_waves = pads ? (int64_t)prob.num_experts * p.pad_waves_per_expert : 0;
+    p.alignment = prob.expert_alignment;
+    p.pad_waves_per_expert = pads ? prob.expert_alignment - 1 : 1;
+    // Blocks of `alignment` receive rows that routed rows can reach: each
+    // routed expert ends in one partly filled block, the rest are full.
+    const int64_t pairs = prob.num_tokens * prob.num_topk;
+    const int64_t blocks_reached = (pairs < prob.num_experts ? pairs : prob.num_experts) +
+                                   pairs / prob.expert_alignment;
+    p.pad_by_block = blocks_reached < prob.num_experts;
+    const int64_t pad_waves =
+        pads ? (p.pad_by_block ? blocks_reached : (int64_t)prob.num_experts) * p.pad_waves_per_expert : 0;
     const int64_t blocks = (p.token_waves + pad_waves + w - 1) / w;
     if (blocks == 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;  // beyond one grid: refused, never truncated

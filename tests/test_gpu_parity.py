@@ -130,6 +130,38 @@ def test_alignments(a):
     _edge(_uniform(6, 900, 8, 64, 0.02), 64, 8, a, row_bytes=80, s=5)
 
 
+# Pad rows of small batches. While the routed rows can reach fewer blocks of
+# A rows than there are experts (min(E, T*K) + T*K // A < E), the scatter maps
+# its pad wavefronts to row blocks and finds each block's expert by a search
+# over the psums (64 samples, then one chunk); otherwise one set of
+# wavefronts per expert. Both sides of the switch, search chunks of 1, 2 and
+# 64 experts, and scale factors in the pad rows.
+@pytest.mark.parametrize("t,k,e,r,a", [
+    (1, 8, 256, 8, 128),     # per block: 8 blocks of 256 experts
+    (16, 8, 256, 8, 128),    # per block
+    (31, 8, 256, 8, 128),    # per block: 249 blocks, the largest below 256
+    (32, 8, 256, 8, 128),    # per expert: 258 blocks
+    (3, 2, 65, 5, 7),        # per block, search chunks of 2 experts
+    (40, 1, 64, 8, 2),       # per block, search chunks of 1 expert
+    (100, 8, 4096, 8, 128),  # per block, search chunks of 64 experts
+    (200, 8, 4096, 64, 3),   # per block, many partly filled blocks
+    (511, 8, 4096, 8, 2),    # per expert: 6132 blocks
+    (5, 1, 1, 1, 4),         # one expert: per expert
+])
+def test_pad_rows_of_small_batches(t, k, e, r, a):
+    _banner(f"pads T={t} K={k} E={e} A={a}")
+    _edge(_uniform(15, t, k, e, 0.1), e, r, a, row_bytes=80, s=3, seed=t)
+
+
+def test_pad_rows_of_a_small_batch_at_exact_capacity():
+    topk = _uniform(16, 12, 8, 256, 0.05)
+    full = oracle.layout(topk, 256, 8, 128)
+    _edge(topk, 256, 8, 128, row_bytes=80, s=3, recv_capacity=full.num_recv_rows)
+    run, ref = _edge(topk, 256, 8, 128, row_bytes=80, s=3, recv_capacity=full.num_recv_rows - 1)
+    assert ref.status == oracle.RECV_OVERFLOW
+    assert np.all(run.rows.recv_x.cpu().numpy() == H.ROW_FILL)
+
+
 def test_fully_masked_tokens():
     topk = _uniform(7, 500, 4, 32)
     topk[::3] = -1
