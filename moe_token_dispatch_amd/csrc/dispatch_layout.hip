@@ -358,7 +358,8 @@ enum AssignMode {
 // units [g * units_per_group, (g + 1) * units_per_group), a unit being one
 // token's 1 KB row segment, to the token's destination rows; it writes the
 // slot-map entries and scale factors of the tokens whose first unit it holds,
-// and zeroes the pad rows of experts g, g + G, ... The results equal those of
+// and zeroes its share of the pad rows (chunks of an expert's consecutive pad
+// rows, dealt round-robin over the workgroups). The results equal those of
 // the layout followed by the scatter.
 template <int CH, int MODE, bool EXPAND, typename IdxT, bool FUSED = false>
 __global__ void __launch_bounds__(kLayoutThreads)

@@ -208,6 +208,22 @@ def test_expand_empty_and_partial(m, counts):
     _compare(lay, recv_x, None, ref, recv_buf, None)
 
 
+# Receive buffers so small that their routed rows reach fewer blocks of A
+# rows than the receiver has experts: the scatter maps its pad wavefronts to
+# row blocks (the assert below checks that the case is one).
+@pytest.mark.parametrize("s_count,t,a,rank", [(1, 3, 128, 3), (2, 1, 128, 0), (2, 1, 3, 6)])
+def test_expand_pads_of_a_small_receive_buffer(s_count, t, a, rank):
+    _banner(f"small receive buffer S={s_count} T={t} A={a} rank={rank}")
+    e, r, k = 256, 8, 8
+    sources = [_source(900 + 7 * s + t, t, 512, "fp8", True, e, r, k, 0.0) for s in range(s_count)]
+    recv_topk, recv_buf, recv_sf, counts, m = _receive_buffer(sources, e, r, rank, slack=0, seed=t)
+    pairs = s_count * m * k
+    assert counts.sum() > 0 and min(pairs, e // r) + pairs // a < e // r
+    ref = oracle.expand_layout(recv_topk, counts, s_count, m, e, r, rank, a)
+    _, lay, recv_x, recv_sf_out = _run_expand(recv_topk, recv_buf, recv_sf, counts, m, e, r, rank, a)
+    _compare(lay, recv_x, recv_sf_out, ref, recv_buf, recv_sf)
+
+
 def _draw_expand(seed):
     rng = np.random.default_rng([seed, 77])
     r = int(rng.choice([1, 2, 4, 8, 16]))
