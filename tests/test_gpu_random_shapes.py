@@ -76,3 +76,40 @@ def test_random_problem_through_the_one_call(seed):
     run = H.run_gpu(topk, e, r, a, xb, sf, topk_bytes=topk_bytes, flags=flags, combined=True)
     H.assert_layout_equal(run, ref)
     H.assert_rows_full(run, ref, xb, sf)
+
+
+SMALL_ALIGNED_CASES = 12
+
+
+def _draw_small_aligned(seed):
+    """Small batches over many experts with alignment: most fall where the
+    scatter maps its pad wavefronts to row blocks, the rest just past it."""
+    rng = np.random.default_rng([seed, 4242])
+    r = int(rng.choice([1, 4, 8, 64]))
+    e = int(rng.choice([64, 256, 1024, 4096]))
+    e -= e % r
+    k = int(rng.choice([1, 2, 4, 8]))
+    t = int(rng.choice([1, 2, 5, 17, 40, 130]))
+    a = int(rng.choice([2, 3, 16, 128]))
+    row_bytes = int(rng.choice([16, 272, 1040, 7168]))
+    s = int(rng.choice([0, 3, 56]))
+    topk_bytes = int(rng.choice([4, 8]))
+    mask = float(rng.choice([0.0, 0.2]))
+    flags = int(rng.choice([M.ALL_OUTPUTS, M.EXPERT_MAJOR | M.ZERO_PAD]))
+    return t, k, e, r, a, row_bytes, s, topk_bytes, mask, flags
+
+
+@pytest.mark.parametrize("seed", range(SMALL_ALIGNED_CASES))
+def test_random_small_aligned_batch(seed):
+    t, k, e, r, a, row_bytes, s, topk_bytes, mask, flags = _draw_small_aligned(seed)
+    print(f"\n[gpu-random] small aligned seed={seed} T={t} K={k} E={e} R={r} A={a} row={row_bytes} S={s} "
+          f"idx={topk_bytes} mask={mask} flags={flags}", flush=True)
+    w = W.Workload(f"randsa{seed}", t, 64, "bf16", False, e, r, k, mask_frac=mask, seed=3000 + seed)
+    topk = W.make_topk(w)
+    xb = H.random_rows(seed, t, row_bytes)
+    sf = None if s == 0 else np.random.default_rng([seed, 9]).uniform(0.5, 2, (t, s)).astype(np.float32)
+    ref = oracle.layout(topk, e, r, a)
+    assert ref.status == 0
+    run = H.run_gpu(topk, e, r, a, xb, sf, topk_bytes=topk_bytes, flags=flags)
+    H.assert_layout_equal(run, ref)
+    H.assert_rows_full(run, ref, xb, sf)
