@@ -1,0 +1,60 @@
+"""A broad seeded sweep of small and mid-sized problems, bit for bit against
+the CPU oracle, through both call forms.
+
+Each seed draws every parameter at once (tokens across the tile, chunk,
+one-kernel and pad-mapping boundaries; top-k; experts and ranks; alignment;
+routing width; masking; output selection; row and scale-factor widths) with
+narrow rows, so that a few hundred problems run in seconds. Every problem is
+printed before it runs.
+"""
+
+import numpy as np
+import pytest
+
+import moe_token_dispatch_amd as M
+import oracle
+import workloads as W
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+BATCHES = 8
+PER_BATCH = 100
+
+
+def _draw(seed):
+    rng = np.random.default_rng([seed, 9090])
+    r = int(rng.choice([1, 2, 3, 4, 8, 16, 64, 256, 1024]))
+    epr = int(rng.choice([1, 1, 2, 4, 8, 16, 32]))
+    e = min(r * epr, 4096) // r * r
+    k = int(min(e, rng.choice([1, 2, 3, 4, 5, 8, 8, 12, 16, 32])))
+    t = int(rng.choice([0, 1, 2, 3, 8, 15, 31, 63, 64, 65, 100, 127, 128, 129, 255, 256, 257, 300, 384, 385,
+                        511, 512, 513, 777, 1023, 1024, 1025, 1500, 2047, 2500]))
+    a = int(rng.choice([1, 1, 2, 3, 7, 64, 128]))
+    row_bytes = int(rng.choice([16, 32, 48, 64, 1040]))
+    s = int(rng.choice([0, 0, 1, 2, 5]))
+    topk_bytes = int(rng.choice([4, 8]))
+    mask = float(rng.choice([0.0, 0.0, 0.03, 0.3, 1.0]))
+    flags = int(rng.choice([M.ALL_OUTPUTS, M.ALL_OUTPUTS, M.EXPERT_MAJOR | M.ZERO_PAD, M.EXPERT_MAJOR,
+                            M.RANK_CONTIG, M.RANK_CONTIG | M.EXPERT_MAJOR]))
+    combined = bool(rng.integers(0, 2))
+    if (t * k + e * (a - 1)) * (row_bytes + 4 * s) > 64 << 20:  # keep every case quick to check
+        row_bytes, s = 16, 0
+    return t, k, e, r, a, row_bytes, s, topk_bytes, mask, flags, combined
+
+
+@pytest.mark.parametrize("batch", range(BATCHES))
+def test_seeded_sweep(batch):
+    for seed in range(batch * PER_BATCH, (batch + 1) * PER_BATCH):
+        t, k, e, r, a, row_bytes, s, topk_bytes, mask, flags, combined = _draw(seed)
+        print(f"[gpu-sweep] seed={seed} T={t} K={k} E={e} R={r} A={a} row={row_bytes} S={s} idx={topk_bytes} "
+              f"mask={mask} flags={flags} one_call={combined}", flush=True)
+        w = W.Workload(f"sweep{seed}", t, 64, "bf16", False, e, r, k, mask_frac=mask, seed=5000 + seed)
+        topk = W.make_topk(w)
+        xb = H.random_rows(seed, t, row_bytes)
+        sf = None if s == 0 else np.random.default_rng([seed, 11]).uniform(0.5, 2, (t, s)).astype(np.float32)
+        ref = oracle.layout(topk, e, r, a)
+        assert ref.status == 0
+        run = H.run_gpu(topk, e, r, a, xb, sf, topk_bytes=topk_bytes, flags=flags, combined=combined)
+        H.assert_layout_equal(run, ref)
+        H.assert_rows_full(run, ref, xb, sf)
