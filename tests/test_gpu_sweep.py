@@ -58,3 +58,43 @@ def test_seeded_sweep(batch):
         run = H.run_gpu(topk, e, r, a, xb, sf, topk_bytes=topk_bytes, flags=flags, combined=combined)
         H.assert_layout_equal(run, ref)
         H.assert_rows_full(run, ref, xb, sf)
+
+
+EXPAND_BATCHES = 4
+EXPAND_PER_BATCH = 50
+
+
+def _draw_expand(seed):
+    rng = np.random.default_rng([seed, 9191])
+    r = int(rng.choice([1, 2, 4, 8, 16, 64]))
+    e = r * int(rng.choice([1, 2, 4, 8, 32]))
+    k = int(min(e, rng.choice([1, 2, 3, 4, 8, 9])))
+    s_count = int(rng.choice([1, 2, 3, 5, 8]))
+    t = int(rng.choice([1, 3, 17, 64, 200, 600]))
+    a = int(rng.choice([1, 1, 2, 3, 16, 128]))
+    rank = int(rng.integers(0, r))
+    hidden = int(rng.choice([64, 128, 512]))
+    dtype = str(rng.choice(["bf16", "fp8"]))
+    with_sf = dtype == "fp8" and hidden >= 128 and bool(rng.integers(0, 2))
+    mask = float(rng.choice([0.0, 0.1, 0.5]))
+    slack = int(rng.choice([0, 0, 5]))
+    topk_bytes = int(rng.choice([4, 8]))
+    combined = bool(rng.integers(0, 2))
+    return s_count, t, hidden, dtype, with_sf, e, r, k, mask, rank, a, slack, topk_bytes, combined
+
+
+@pytest.mark.parametrize("batch", range(EXPAND_BATCHES))
+def test_seeded_expand_sweep(batch):
+    from tests.test_gpu_expand import _compare, _receive_buffer, _run_expand, _source
+
+    for seed in range(batch * EXPAND_PER_BATCH, (batch + 1) * EXPAND_PER_BATCH):
+        s_count, t, hidden, dtype, with_sf, e, r, k, mask, rank, a, slack, ib, combined = _draw_expand(seed)
+        print(f"[gpu-sweep] expand seed={seed} S={s_count} T={t} H={hidden} {dtype}{'+sf' if with_sf else ''} "
+              f"E={e} R={r} K={k} rank={rank} A={a} slack={slack} idx={ib} one_call={combined}", flush=True)
+        sources = [_source(70000 + 17 * seed + s, t, hidden, dtype, with_sf, e, r, k, mask) for s in range(s_count)]
+        recv_topk, recv_buf, recv_sf, counts, m = _receive_buffer(sources, e, r, rank, slack=slack, seed=seed)
+        ref = oracle.expand_layout(recv_topk, counts, s_count, m, e, r, rank, a)
+        assert ref.status == 0
+        _, lay, recv_x, recv_sf_out = _run_expand(recv_topk, recv_buf, recv_sf, counts, m, e, r, rank, a,
+                                                  topk_bytes=ib, combined=combined)
+        _compare(lay, recv_x, recv_sf_out, ref, recv_buf, recv_sf)
