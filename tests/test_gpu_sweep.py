@@ -1,5 +1,6 @@
-"""A broad seeded sweep of small and mid-sized problems, bit for bit against
-the CPU oracle, through both call forms.
+"""Broad seeded sweeps of small and mid-sized problems against the CPU oracle:
+the dispatch and the receiver-side expand bit for bit through both call
+forms, and the combine within its bound.
 
 Each seed draws every parameter at once (tokens across the tile, chunk,
 one-kernel and pad-mapping boundaries; top-k; experts and ranks; alignment;
@@ -10,6 +11,7 @@ printed before it runs.
 
 import numpy as np
 import pytest
+import torch
 
 import moe_token_dispatch_amd as M
 import oracle
@@ -98,3 +100,30 @@ def test_seeded_expand_sweep(batch):
         _, lay, recv_x, recv_sf_out = _run_expand(recv_topk, recv_buf, recv_sf, counts, m, e, r, rank, a,
                                                   topk_bytes=ib, combined=combined)
         _compare(lay, recv_x, recv_sf_out, ref, recv_buf, recv_sf)
+
+
+COMBINE_BATCHES = 2
+COMBINE_PER_BATCH = 50
+
+
+def _draw_combine(seed):
+    rng = np.random.default_rng([seed, 9292])
+    t = int(rng.choice([1, 2, 31, 64, 65, 300, 1000]))
+    e = int(rng.choice([8, 32, 64, 256]))
+    k = int(min(e, rng.choice([1, 2, 3, 6, 8, 9, 16, 32])))
+    hidden = 8 * int(rng.choice([1, 7, 16, 63, 64, 65, 128, 256]))
+    mask = float(rng.choice([0.0, 0.05, 0.5, 1.0]))
+    alignment = int(rng.choice([1, 1, 4, 16]))
+    return t, k, e, hidden, mask, alignment
+
+
+@pytest.mark.parametrize("batch", range(COMBINE_BATCHES))
+def test_seeded_combine_sweep(batch):
+    from tests.test_gpu_combine import _combine_inputs, _run_combine
+
+    for seed in range(batch * COMBINE_PER_BATCH, (batch + 1) * COMBINE_PER_BATCH):
+        t, k, e, hidden, mask, alignment = _draw_combine(seed)
+        print(f"[gpu-sweep] combine seed={seed} T={t} K={k} E={e} H={hidden} mask={mask} A={alignment}", flush=True)
+        w, topk, ref, y, wts = _combine_inputs(t, k, e, hidden, mask, seed=90000 + seed, alignment=alignment)
+        got = _run_combine(ref.expert_slot, wts, y)
+        H.assert_combine_close(got, y.view(torch.int16).numpy().view(np.uint16), wts, ref.expert_slot)
