@@ -34,6 +34,9 @@
  *     rank_psum[R]) up to the capacities are never written.
  *   - Reentrancy: the library is stateless; concurrent calls need their own
  *     workspaces and outputs.
+ *   - Language: the header is plain C (C99) as well as C++. A compiler other
+ *     than hipcc must define __HIP_PLATFORM_AMD__, as HIP's own runtime header
+ *     included below requires.
  */
 #ifndef MOE_DISPATCH_H
 #define MOE_DISPATCH_H
