@@ -655,7 +655,7 @@ def main():
             "sf_per_token": s, "experts": w.num_experts, "ranks": w.num_ranks, "topk": k,
             "routing": w.routing, "mask_frac": w.mask_frac, "expert_alignment": w.alignment,
             "outputs": "rank-contiguous + expert-major (zero pads)", "parallelism": "single GPU",
-            "kernels_per_step": step_kernels,
+            "kernels_per_step": step_kernels, "seed": w.seed,
         },
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": total_b,
