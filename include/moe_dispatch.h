@@ -109,7 +109,9 @@ typedef struct dispatch_layout {
      * totals of expert_count. A call that ends with status 0 adds its
      * expert_count to it with device atomics, so calls on several streams may
      * share one array; a failed call adds nothing. The page's cumulative
-     * per-expert receive statistics (section 7.2). */
+     * per-expert receive statistics (section 7.2), an int32 counter there too:
+     * it wraps modulo 2^32, so a caller that keeps it over more than 2^31 rows
+     * per expert reads and clears it from time to time. */
     int32_t* expert_count_cumulative;
 } dispatch_layout_t;
 
