@@ -234,6 +234,52 @@ def _check_cumulative(t: Optional[torch.Tensor], num_experts: int) -> None:
             raise ValueError(f"expert_count_cumulative needs {num_experts} entries, has {t.numel()}")
 
 
+# The C ABI takes raw pointers and trusts their sizes; the binding knows every
+# size from the problem and refuses a tensor too small for it, before any call.
+def _need(t: Optional[torch.Tensor], name: str, nbytes: int) -> None:
+    if t is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes; the problem needs {nbytes}")
+
+
+def _check_dispatch_sizes(problem: Problem, topk_idx: Optional[torch.Tensor], layout: "LayoutTensors") -> None:
+    t, k, e, r = problem.num_tokens, problem.num_topk, problem.num_experts, problem.num_ranks
+    _need(topk_idx, "topk_idx", t * k * problem.topk_idx_bytes)
+    for name, n in (("expert_count", e), ("rank_count", r), ("expert_psum", e + 1), ("rank_psum", r + 1),
+                    ("expert_slot", t * k), ("rank_slot", t * k),
+                    ("recv_src_token_idx", problem.recv_capacity_rows),
+                    ("rank_src_token_idx", problem.rank_capacity_rows), ("status", 1)):
+        _need(getattr(layout, name), name, 4 * n)
+
+
+def _check_dispatch_rows(problem: Problem, x, x_sf, rank_x, rank_sf, recv_x, recv_sf) -> None:
+    t, rb, s = problem.num_tokens, problem.row_bytes, problem.sf_per_token
+    _need(x, "x", t * rb)
+    _need(x_sf, "x_sf", 4 * t * s)
+    if problem.flags & RANK_CONTIG:
+        _need(rank_x, "rank_x", problem.rank_capacity_rows * rb)
+        _need(rank_sf, "rank_sf", 4 * problem.rank_capacity_rows * s)
+    if problem.flags & EXPERT_MAJOR:
+        _need(recv_x, "recv_x", problem.recv_capacity_rows * rb)
+        _need(recv_sf, "recv_sf", 4 * problem.recv_capacity_rows * s)
+
+
+def _check_expand_sizes(problem: "ExpandProblem", recv_topk_idx, recv_count, layout, recv_buf, recv_sf_buf,
+                        recv_x, recv_sf) -> None:
+    rows = problem.num_sources * problem.rows_per_source
+    local = problem.num_experts // problem.num_ranks
+    cap, rb, s = problem.recv_capacity_rows, problem.row_bytes, problem.sf_per_token
+    _need(recv_topk_idx, "recv_topk_idx", rows * problem.num_topk * problem.topk_idx_bytes)
+    _need(recv_count, "recv_count", 4 * problem.num_sources)
+    if layout is not None:
+        for name, n in (("expert_count", local), ("expert_psum", local + 1), ("expert_slot", rows * problem.num_topk),
+                        ("recv_src_row_idx", cap), ("status", 1)):
+            _need(getattr(layout, name), name, 4 * n)
+    _need(recv_buf, "recv_buf", rows * rb)
+    _need(recv_sf_buf, "recv_sf_buf", 4 * rows * s)
+    _need(recv_x, "recv_x", cap * rb)
+    _need(recv_sf, "recv_sf", 4 * cap * s)
+
+
 def dispatch_layout(problem: Problem, topk_idx: torch.Tensor, out: LayoutTensors,
                     workspace: torch.Tensor, stream: Optional[torch.cuda.Stream] = None,
                     expert_count_cumulative: Optional[torch.Tensor] = None) -> None:
@@ -247,6 +293,7 @@ def dispatch_layout(problem: Problem, topk_idx: torch.Tensor, out: LayoutTensors
     for f in dataclasses.fields(out):
         _check_device_tensor(getattr(out, f.name), f.name, torch.int32)
     _check_cumulative(expert_count_cumulative, problem.num_experts)
+    _check_dispatch_sizes(problem, topk_idx, out)
     lay = out.ptrs(expert_count_cumulative)
     rc = load_library().dispatch_layout(ctypes.byref(problem), _ptr(topk_idx), ctypes.byref(lay),
                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -265,6 +312,10 @@ def dispatch_scatter(problem: Problem, layout: LayoutTensors, x: torch.Tensor,
                     ("recv_sf", recv_sf)):
         if t is not None:
             _check_device_tensor(t, name)
+    for f in dataclasses.fields(layout):
+        _check_device_tensor(getattr(layout, f.name), f.name, torch.int32)
+    _check_dispatch_sizes(problem, None, layout)
+    _check_dispatch_rows(problem, x, x_sf, rank_x, rank_sf, recv_x, recv_sf)
     lay = layout.ptrs()
     rc = load_library().dispatch_scatter(ctypes.byref(problem), ctypes.byref(lay), _ptr(x), _ptr(x_sf),
                                          _ptr(rank_x), _ptr(rank_sf), _ptr(recv_x), _ptr(recv_sf),
@@ -302,6 +353,8 @@ def dispatch_layout_and_scatter(problem: Problem, topk_idx: torch.Tensor, out: L
                     ("recv_sf", recv_sf)):
         if t is not None:
             _check_device_tensor(t, name)
+    _check_dispatch_sizes(problem, topk_idx, out)
+    _check_dispatch_rows(problem, x, x_sf, rank_x, rank_sf, recv_x, recv_sf)
     lay = out.ptrs(expert_count_cumulative)
     rc = load_library().dispatch_layout_and_scatter(
         ctypes.byref(problem), _ptr(topk_idx), ctypes.byref(lay), _ptr(workspace),
@@ -392,6 +445,7 @@ class Plan:
         for f in dataclasses.fields(layout):
             _check_device_tensor(getattr(layout, f.name), f.name, torch.int32)
         _check_cumulative(expert_count_cumulative, problem.num_experts)
+        _check_dispatch_sizes(problem, topk_idx, layout)
         self._lib = load_library()
         self._keep = (problem, topk_idx, layout, workspace, x, x_sf, rows, expert_count_cumulative)
         self._lay = layout.ptrs(expert_count_cumulative)
@@ -408,6 +462,7 @@ class Plan:
                     _check_device_tensor(t, name)
             if x_sf is not None:
                 _check_device_tensor(x_sf, "x_sf")
+            _check_dispatch_rows(problem, x, x_sf, rows.rank_x, rows.rank_sf, rows.recv_x, rows.recv_sf)
             row_ptrs = (_ptr(x), _ptr(x_sf), _ptr(rows.rank_x), _ptr(rows.rank_sf), _ptr(rows.recv_x),
                         _ptr(rows.recv_sf))
             self._scatter_args = (ctypes.byref(problem), ctypes.byref(self._lay), *row_ptrs, handle)
@@ -506,6 +561,7 @@ def dispatch_expand_layout(problem: ExpandProblem, recv_topk_idx: torch.Tensor, 
     for f in dataclasses.fields(out):
         _check_device_tensor(getattr(out, f.name), f.name, torch.int32)
     _check_cumulative(expert_count_cumulative, problem.num_experts // problem.num_ranks)
+    _check_expand_sizes(problem, recv_topk_idx, recv_count, out, None, None, None, None)
     lay = out.ptrs(expert_count_cumulative)
     rc = load_library().dispatch_expand_layout(
         ctypes.byref(problem), _ptr(recv_topk_idx), _ptr(recv_count), ctypes.byref(lay), _ptr(workspace),
@@ -534,6 +590,7 @@ def dispatch_expand_layout_and_scatter(problem: ExpandProblem, recv_topk_idx: to
     for name, t in (("recv_sf_buf", recv_sf_buf), ("recv_x", recv_x), ("recv_sf", recv_sf)):
         if t is not None:
             _check_device_tensor(t, name)
+    _check_expand_sizes(problem, recv_topk_idx, recv_count, out, recv_buf, recv_sf_buf, recv_x, recv_sf)
     lay = out.ptrs(expert_count_cumulative)
     rc = load_library().dispatch_expand_layout_and_scatter(
         ctypes.byref(problem), _ptr(recv_topk_idx), _ptr(recv_count), ctypes.byref(lay), _ptr(workspace),
@@ -551,6 +608,9 @@ def dispatch_expand_scatter(problem: ExpandProblem, layout: ExpandLayoutTensors,
     for name, t in (("recv_sf_buf", recv_sf_buf), ("recv_x", recv_x), ("recv_sf", recv_sf)):
         if t is not None:
             _check_device_tensor(t, name)
+    for f in dataclasses.fields(layout):
+        _check_device_tensor(getattr(layout, f.name), f.name, torch.int32)
+    _check_expand_sizes(problem, None, None, layout, recv_buf, recv_sf_buf, recv_x, recv_sf)
     lay = layout.ptrs()
     rc = load_library().dispatch_expand_scatter(ctypes.byref(problem), ctypes.byref(lay), _ptr(recv_buf),
                                                 _ptr(recv_sf_buf), _ptr(recv_x), _ptr(recv_sf),
@@ -582,6 +642,7 @@ class ExpandPlan:
         for name, t in (("recv_sf_buf", recv_sf_buf), ("recv_x", recv_x), ("recv_sf", recv_sf)):
             if t is not None:
                 _check_device_tensor(t, name)
+        _check_expand_sizes(problem, recv_topk_idx, recv_count, layout, recv_buf, recv_sf_buf, recv_x, recv_sf)
         self._lib = load_library()
         self._keep = (problem, recv_topk_idx, recv_count, layout, workspace, recv_buf, recv_sf_buf, recv_x, recv_sf,
                       expert_count_cumulative)
