@@ -62,7 +62,8 @@ def parse_args():
                     help="measure the combine instead: weighted gather of the expert-major rows back to tokens")
     ap.add_argument("--latency", action="store_true",
                     help="per-step latency of small (decode-sized) batches of the workload's shape: "
-                         "the one call against the layout and scatter calls")
+                         "the one call against the layout and scatter calls (with --expand: small "
+                         "receive buffers of --sources sources)")
     return ap.parse_args()
 
 
@@ -198,23 +199,19 @@ def _time_oracle(prep, budget_s):
     return statistics.median(times), len(times), statistics.median(lay_t), statistics.median(sc_t)
 
 
-def expand_bench(args):
-    """Receiver-side expand: S sources, each the chosen workload with its own
-    seed, run the sender path on the GPU; receiver rank 0 gets every source's
-    rank-0 block in a fixed-stride receive buffer (T rows per source, the
-    most a source can send) and expands it into its expert-major buffer."""
+def receive_buffer(base, s_count, t, rank, dev):
+    """S sources, each the workload's shape at t tokens with its own seed, run
+    the sender path on the GPU; receiver `rank` gets every source's block in a
+    fixed-stride receive buffer of t rows per source (the most a source can
+    send). Returns (recv_topk, counts, recv_buf, recv_sf, rows per source)."""
     import dataclasses
 
-    import numpy as np
     import torch
 
     import moe_token_dispatch_amd as M
     import workloads as W
 
-    dev = "cuda:0"
-    base = W.get(args.workload or W.METRIC_WORKLOAD)
-    s_count, rank = args.sources, 0
-    t, k, e, r = base.num_tokens, base.num_topk, base.num_experts, base.num_ranks
+    k, e, r = base.num_topk, base.num_experts, base.num_ranks
     s_f, rb = base.sf_per_token, base.row_bytes
     m = t
     recv_buf = torch.zeros((s_count * m, rb), dtype=torch.uint8, device=dev)
@@ -222,7 +219,7 @@ def expand_bench(args):
     recv_topk = torch.full((s_count * m, k), -1, dtype=torch.int64, device=dev)
     counts = torch.zeros(s_count, dtype=torch.int32, device=dev)
     for s in range(s_count):
-        w = dataclasses.replace(base, seed=base.seed * 1000 + s)
+        w = dataclasses.replace(base, num_tokens=t, seed=base.seed * 1000 + s)
         inp = W.make_inputs(w)
         prob = M.make_problem(t, k, e, r, w.alignment, 8, rb, s_f)
         lay, ws, rows = M.alloc_layout(prob, dev), M.alloc_workspace(prob, dev), M.alloc_rows(prob, dev)
@@ -240,6 +237,25 @@ def expand_bench(args):
         recv_topk[s * m:s * m + n] = topk_d.index_select(0, lay.rank_src_token_idx[lo:hi].long())
         counts[s] = n
         del lay, ws, rows, topk_d, x_d, sf_d
+    return recv_topk, counts, recv_buf, recv_sf, m
+
+
+def expand_bench(args):
+    """Receiver-side expand: S sources, each the chosen workload with its own
+    seed, run the sender path on the GPU; receiver rank 0 gets every source's
+    rank-0 block in a fixed-stride receive buffer (T rows per source, the
+    most a source can send) and expands it into its expert-major buffer."""
+    import torch
+
+    import moe_token_dispatch_amd as M
+    import workloads as W
+
+    dev = "cuda:0"
+    base = W.get(args.workload or W.METRIC_WORKLOAD)
+    s_count, rank = args.sources, 0
+    t, k, e, r = base.num_tokens, base.num_topk, base.num_experts, base.num_ranks
+    s_f, rb = base.sf_per_token, base.row_bytes
+    recv_topk, counts, recv_buf, recv_sf, m = receive_buffer(base, s_count, t, rank, dev)
     q = M.make_expand_problem(s_count, m, k, e, r, rank, base.alignment, 8, rb, s_f)
     elay = M.alloc_expand_layout(q, dev)
     ews = M.alloc_expand_workspace(q, dev)
@@ -372,11 +388,63 @@ def combine_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def expand_latency_bench(args):
+    """Microseconds per step of the receiver-side expand for small receive
+    buffers: S sources of t tokens of the workload's shape into rank 0,
+    through a prepared plan; the layout and scatter calls against the one
+    call (one kernel up to 2048 routing entries). HIP events on the launch
+    stream around many back-to-back steps."""
+    import torch
+
+    import moe_token_dispatch_amd as M
+    import workloads as W
+
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream(dev)
+    base = W.get(args.workload or W.METRIC_WORKLOAD)
+    s_count, rank, reps = args.sources, 0, max(100, args.steps)
+    k, e, r = base.num_topk, base.num_experts, base.num_ranks
+
+    def per_step_us(fn):
+        for _ in range(max(20, args.warmup)):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    rows_out = []
+    for t in (1, 4, 16, 32, 48, 64):
+        recv_topk, counts, recv_buf, recv_sf, m = receive_buffer(base, s_count, t, rank, dev)
+        q = M.make_expand_problem(s_count, m, k, e, r, rank, base.alignment, 8, base.row_bytes, base.sf_per_token)
+        lay, ws = M.alloc_expand_layout(q, dev), M.alloc_expand_workspace(q, dev)
+        cap = max(q.recv_capacity_rows, 1)
+        recv_x = torch.empty((cap, base.row_bytes), dtype=torch.uint8, device=dev)
+        out_sf = torch.empty((cap, base.sf_per_token), dtype=torch.float32, device=dev) if base.sf_per_token else None
+        plan = M.ExpandPlan(q, recv_topk, counts, lay, ws, recv_buf, recv_sf, recv_x, out_sf, stream)
+        two = per_step_us(lambda: (plan.layout(), plan.scatter()))
+        one = per_step_us(plan)
+        if int(lay.status.item()) != 0:
+            raise RuntimeError(f"expand status {int(lay.status.item())}")
+        rows_out.append({"tokens_per_source": t, "receive_rows": s_count * m,
+                         "received_rows": int(counts.sum().item()),
+                         "us_two_calls": round(two, 2), "us_one_call": round(one, 2)})
+    print(json.dumps({"metric": "receiver-side expand latency of small receive buffers", "unit": "us per step",
+                      "higher_is_better": False, "workload": base.name, "sources": s_count, "steps": reps,
+                      "what": "HIP events around back-to-back steps of a prepared expand plan",
+                      "batches": rows_out}), flush=True)
+
+
 def latency_bench(args):
     """Microseconds per step for small batches of the workload's shape (its
     experts, ranks, top-k and row width), through a prepared plan: the one
-    call (one kernel up to 3072 (token, k) pairs) and the layout and scatter
-    calls. HIP events on the launch stream around many back-to-back steps."""
+    call (one kernel up to 3072 (token, k) pairs, 2048 with zeroed pad rows)
+    and the layout and scatter calls. HIP events on the launch stream around
+    many back-to-back steps."""
     import dataclasses
 
     import torch
@@ -462,14 +530,14 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.latency:
+        expand_latency_bench(args) if args.expand else latency_bench(args)
+        return
     if args.expand:
         expand_bench(args)
         return
     if args.combine:
         combine_bench(args)
-        return
-    if args.latency:
-        latency_bench(args)
         return
 
     import numpy as np

@@ -163,12 +163,12 @@ int dispatch_scatter(const dispatch_problem_t* problem, const dispatch_layout_t*
 
 /* dispatch_layout followed by dispatch_scatter in one call, with the same
  * arguments, checks, outputs and status semantics as those two calls made in
- * turn. A small batch (T * K up to 3072 pairs, fewer when E + R is large) is
- * laid out and copied by a single kernel: every workgroup ranks the whole
- * batch itself, so none waits for another, and each copies its share of the
- * rows' 1 KB segments. That saves one or two launches, the dominant cost of
- * small (decode-sized) batches. Larger batches run the layout and scatter
- * kernels. */
+ * turn. A small batch (T * K up to 3072 pairs, or 2048 when pad rows are
+ * zeroed; fewer when E + R is large) is laid out and copied by a single
+ * kernel: every workgroup ranks the whole batch itself, so none waits for
+ * another, and each copies its share of the rows' 1 KB segments. That saves
+ * one or two launches, the dominant cost of small (decode-sized) batches.
+ * Larger batches run the layout and scatter kernels. */
 int dispatch_layout_and_scatter(const dispatch_problem_t* problem, const void* topk_idx,
                                 const dispatch_layout_t* out, void* workspace, size_t workspace_bytes,
                                 const void* x, const float* x_sf, void* rank_x, float* rank_sf,
@@ -229,7 +229,7 @@ int dispatch_expand_layout(const dispatch_expand_problem_t* problem, const void*
 
 /* dispatch_expand_layout followed by dispatch_expand_scatter in one call, with
  * the same arguments, checks and outputs as those two calls made in turn. A
- * small receive buffer (S * M * K up to 3072 entries) is laid out and copied
+ * small receive buffer (S * M * K up to 2048 entries) is laid out and copied
  * by one kernel, as in dispatch_layout_and_scatter. */
 int dispatch_expand_layout_and_scatter(const dispatch_expand_problem_t* problem, const void* recv_topk_idx,
                                        const int32_t* recv_count, const dispatch_layout_t* out, void* workspace,

@@ -303,7 +303,7 @@ int dispatch_expand_layout_and_scatter(const dispatch_expand_problem_t* problem,
     if (rc != DISPATCH_OK) return rc;
     rc = check_scatter_args(p, out, recv_buf, recv_sf_buf, nullptr, nullptr, recv_x, recv_sf);
     if (rc != DISPATCH_OK) return rc;
-    if (moe_dispatch::fused_shape(p, g).fits) {
+    if (moe_dispatch::fused_shape(p, g, true).fits) {
         if (moe_dispatch::launch_fused_dispatch(p, g, recv_topk_idx, *out, workspace, recv_buf, recv_sf_buf, nullptr,
                                                 nullptr, recv_x, recv_sf, stream, &view) != hipSuccess)
             return DISPATCH_ERR_HIP;

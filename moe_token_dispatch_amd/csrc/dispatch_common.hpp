@@ -159,6 +159,15 @@ constexpr int kFusedMaxChunks = 8;        // chunks per wavefront of the one til
 // than the layout and scatter launches it saves (at 4096 pairs: 14.0 against
 // 12.6 us for 256-byte rows, 29.2 against 29.6 us for 14 KB rows).
 constexpr int64_t kFusedMaxBatchPairs = 3072;
+// A lower limit where the one kernel's own copies are light against its
+// ranking: a batch with zero pad rows to write (the scatter's one-row pad
+// wavefronts write them faster), and the receiver-side expand (about one
+// destination per row). Measured on MI355X: with alignment 128 on 7 KB rows,
+// 384 tokens took 61.0 us in one kernel against 58.0 in the layout and
+// scatter kernels (256 tokens: 55.5 against 56.9); the expand of 8 sources
+// took 14.6 against 13.2 us at 3072 entries of bf16 rows (10.4 against 10.8
+// at 2048). Past 2048 pairs at top-8 every wavefront ranks 4 chunks.
+constexpr int64_t kFusedMaxBatchPairsPadsOrExpand = 2048;
 // The most (expert, pad row) items, E * (A - 1), the one kernel walks, and
 // the consecutive pad rows it deals to a workgroup at a time.
 constexpr int64_t kFusedMaxPadItems = int64_t(1) << 20;
@@ -173,7 +182,8 @@ struct FusedShape {
     int32_t segments;    // 1 KB units per row
     int32_t waves;       // wavefronts per workgroup (>= tile_waves)
 };
-inline FusedShape fused_shape(const dispatch_problem_t& prob, const TileGeometry& g) {
+// expand: the problem is a receiver-side expand seen as a dispatch.
+inline FusedShape fused_shape(const dispatch_problem_t& prob, const TileGeometry& g, bool expand = false) {
     FusedShape f{};
     const int64_t t = g.num_tokens;
     const int64_t row_bytes = prob.row_bytes;
@@ -216,8 +226,9 @@ inline FusedShape fused_shape(const dispatch_problem_t& prob, const TileGeometry
     if (w > g.max_waves) w = g.max_waves;
     if (w < f.tile_waves) w = f.tile_waves;
     f.waves = (int32_t)w;
+    const int64_t max_pairs = pads || expand ? kFusedMaxBatchPairsPadsOrExpand : kFusedMaxBatchPairs;
     f.fits = f.tile_waves <= g.max_waves && tokens * g.num_topk <= kFusedMaxPairs &&
-             t * g.num_topk <= kFusedMaxBatchPairs && pad_items <= kFusedMaxPadItems;
+             t * g.num_topk <= max_pairs && pad_items <= kFusedMaxPadItems;
     return f;
 }
 // Requires fused_shape(p, g).fits; the outputs are those of

@@ -795,7 +795,7 @@ hipError_t launch_fused_dispatch(const dispatch_problem_t& prob, const TileGeome
                                  const dispatch_layout_t& out, void* workspace, const void* x, const float* x_sf,
                                  void* rank_x, float* rank_sf, void* recv_x, float* recv_sf, hipStream_t stream,
                                  const ExpandView* expand) {
-    const FusedShape f = fused_shape(prob, g);
+    const FusedShape f = fused_shape(prob, g, expand != nullptr);
     if (!f.fits) return hipErrorInvalidValue;
     // The one tile every workgroup ranks (the layout's own geometry may use
     // several tiles for this batch).

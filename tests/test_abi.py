@@ -144,8 +144,8 @@ def test_host_errors_before_launch():
 def test_kernel_counts():
     """The layout: one kernel for a one-tile batch, two with the histograms
     reduced in the assign kernel, three with the column scan. The combined
-    call: one kernel up to 3072 (token, k) pairs, else the layout's kernels
-    and the scatter."""
+    call: one kernel up to 3072 (token, k) pairs (2048 when pad rows are
+    zeroed), else the layout's kernels and the scatter."""
     mk = M.make_problem
     assert M.dispatch_kernel_count(mk(256, 8, 256, 8, 1, row_bytes=14336)) == (1, 1)
     assert M.dispatch_kernel_count(mk(0, 8, 256, 8, 1, row_bytes=64)) == (1, 1)
@@ -153,6 +153,12 @@ def test_kernel_counts():
     assert M.dispatch_kernel_count(mk(257, 8, 256, 8, 1, row_bytes=14336)) == (2, 1)
     assert M.dispatch_kernel_count(mk(384, 8, 256, 8, 1, row_bytes=14336)) == (2, 1)
     assert M.dispatch_kernel_count(mk(385, 8, 256, 8, 1, row_bytes=14336)) == (2, 3)
+    assert M.dispatch_kernel_count(mk(256, 8, 256, 8, 128, row_bytes=7168, sf_per_token=56)) == (1, 1)
+    assert M.dispatch_kernel_count(mk(257, 8, 256, 8, 128, row_bytes=7168, sf_per_token=56)) == (2, 3)
+    assert M.dispatch_kernel_count(mk(384, 8, 256, 8, 2, row_bytes=64)) == (2, 3)
+    # Without the zero-pad flag nothing is padded, and the 3072-pair limit holds.
+    assert M.dispatch_kernel_count(mk(384, 8, 256, 8, 2, row_bytes=64,
+                                      flags=M.RANK_CONTIG | M.EXPERT_MAJOR)) == (2, 1)
     assert M.dispatch_kernel_count(mk(3072, 1, 64, 8, 1, row_bytes=48)) == (2, 1)
     assert M.dispatch_kernel_count(mk(4096, 8, 256, 8, 1, row_bytes=14336)) == (2, 3)
     assert M.dispatch_kernel_count(mk(65536, 8, 256, 8, 128, row_bytes=7168, sf_per_token=56)) == (2, 3)

@@ -277,12 +277,13 @@ def test_expand_expert_count_cumulative():
 
 
 # dispatch_expand_layout_and_scatter: one kernel for a small receive buffer
-# (S * M * K up to 3072 entries), else the layout and scatter kernels.
+# (S * M * K up to 2048 entries), else the layout and scatter kernels.
 @pytest.mark.parametrize("s_count,t,a,dtype,with_sf,rank", [
-    (8, 40, 1, "bf16", False, 3),    # 8 x ~30 rows x top-8: one kernel
-    (3, 100, 16, "fp8", True, 1),    # one kernel, pads and scale factors
-    (1, 300, 4, "bf16", False, 0),   # one kernel
-    (4, 300, 2, "fp8", True, 2),     # past 3072 entries: the layout and scatter kernels
+    (8, 28, 1, "bf16", False, 3),    # 8 x 31 rows x top-8 = 1984 entries: one kernel
+    (8, 30, 1, "bf16", False, 3),    # 8 x 33 rows x top-8 = 2112 entries: the layout and scatter kernels
+    (3, 80, 16, "fp8", True, 1),     # 1848 entries: one kernel, pads and scale factors
+    (1, 250, 4, "bf16", False, 0),   # 1800 entries: one kernel
+    (4, 300, 2, "fp8", True, 2),     # 8800 entries: the layout and scatter kernels
 ])
 def test_expand_layout_and_scatter_in_one_call(s_count, t, a, dtype, with_sf, rank):
     _banner(f"one call: S={s_count} T={t} A={a} {dtype} sf={with_sf} rank={rank}")

@@ -1,7 +1,8 @@
 """GPU parity of dispatch_layout_and_scatter against the CPU oracle, bit for
 bit, through the C ABI.
 
-A small batch (up to 3072 (token, k) pairs, fewer with many keys) is laid out
+A small batch (up to 3072 (token, k) pairs, 2048 with pad rows, fewer with
+many keys) is laid out
 and copied by one kernel in which every workgroup ranks the whole batch itself
 and copies its share of the rows' 1 KB segments; larger batches run the layout
 and scatter kernels. Either way the outputs must equal
@@ -100,12 +101,25 @@ def test_int32_routing_and_fully_masked_tokens():
 
 
 # Past one layout tile, the one kernel ranks a tile of 4 (or, with few
-# wavefronts, 8) chunks per wavefront, up to 3072 pairs.
+# wavefronts, 8) chunks per wavefront, up to 3072 pairs without pad rows
+# (with them, up to 2048).
 @pytest.mark.parametrize("k,t,e,r", [(8, 257, 256, 8), (8, 300, 64, 8), (8, 384, 256, 8), (1, 3072, 64, 8),
                                      (2, 1536, 64, 4), (3, 1024, 64, 16)])
 def test_batches_past_one_layout_tile(k, t, e, r):
     _banner(f"K={k} T={t} E={e} R={r}")
-    _fused(_topk(42 + k, t, k, e, 0.05), e, r, 4, row_bytes=144, s=2, seed=t)
+    prob = M.make_problem(t, k, e, r, 1, 8, 144, 2)
+    assert M.dispatch_kernel_count(prob)[1] == 1
+    _fused(_topk(42 + k, t, k, e, 0.05), e, r, 1, row_bytes=144, s=2, seed=t)
+
+
+# With zero pad rows to write, the one kernel stops at 2048 pairs: 256 tokens
+# at top-8 take it, 257 take the layout and scatter kernels.
+@pytest.mark.parametrize("t,kernels", [(256, 1), (257, 3)])
+def test_pad_rows_limit_of_the_one_kernel(t, kernels):
+    _banner(f"A=16 T={t}")
+    prob = M.make_problem(t, 8, 256, 8, 16, 8, 144, 2)
+    assert M.dispatch_kernel_count(prob)[1] == kernels
+    _fused(_topk(44, t, 8, 256, 0.05), 256, 8, 16, row_bytes=144, s=2, seed=t)
 
 
 def test_many_keys_eight_chunks_and_just_past_them():
@@ -114,7 +128,8 @@ def test_many_keys_eight_chunks_and_just_past_them():
     take the layout and scatter kernels."""
     for t in (80, 320, 321):
         _banner(f"E=4096 R=1024 T={t}")
-        _fused(_topk(37, t, 8, 4096, 0.05), 4096, 1024, 2, seed=t)
+        assert M.dispatch_kernel_count(M.make_problem(t, 8, 4096, 1024, 1, 8, 64, 0))[1] == (1 if t <= 320 else 3)
+        _fused(_topk(37, t, 8, 4096, 0.05), 4096, 1024, 1, seed=t)
 
 
 @pytest.mark.parametrize("t", [385, 3001])

@@ -60,11 +60,13 @@ ONE_CALL_CASES = 16
 
 @pytest.mark.parametrize("seed", range(ONE_CALL_CASES))
 def test_random_problem_through_the_one_call(seed):
-    """The same draws, with the batch cut to at most 3072 (token, k) pairs and
-    run through dispatch_layout_and_scatter: one kernel where it fits, the
-    layout and scatter kernels otherwise (many keys, few wavefronts)."""
+    """The same draws, with the batch cut to the one kernel's limit (3072
+    (token, k) pairs, 2048 when pad rows are zeroed) and run through
+    dispatch_layout_and_scatter: one kernel where it fits, the layout and
+    scatter kernels otherwise (many keys, few wavefronts)."""
     t, k, e, r, a, row_bytes, s, topk_bytes, mask, flags = _draw(500 + seed)
-    t = min(t, 3072 // k)
+    pads = a > 1 and flags & M.EXPERT_MAJOR and flags & M.ZERO_PAD
+    t = min(t, (2048 if pads else 3072) // k)
     print(f"\n[gpu-random] one call seed={seed} T={t} K={k} E={e} R={r} A={a} row={row_bytes} S={s} "
           f"idx={topk_bytes} mask={mask} flags={flags}", flush=True)
     w = W.Workload(f"rand1c{seed}", t, 64, "bf16", False, e, r, k, mask_frac=mask, seed=2000 + seed)
@@ -73,6 +75,7 @@ def test_random_problem_through_the_one_call(seed):
     sf = None if s == 0 else np.random.default_rng([seed, 8]).uniform(0.5, 2, (t, s)).astype(np.float32)
     ref = oracle.layout(topk, e, r, a)
     assert ref.status == 0
+    assert M.dispatch_kernel_count(M.make_problem(t, k, e, r, a, topk_bytes, row_bytes, s, flags=flags))[1] == 1
     run = H.run_gpu(topk, e, r, a, xb, sf, topk_bytes=topk_bytes, flags=flags, combined=True)
     H.assert_layout_equal(run, ref)
     H.assert_rows_full(run, ref, xb, sf)
