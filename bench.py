@@ -8,11 +8,14 @@ rank-contiguous and expert-major buffers, on inputs already resident in HBM.
 The default workload is 4096 tokens x 7168 bf16, top-8 of 256 experts in 8
 logical ranks with 5% of the routing entries masked.
 
-Prints one JSON line with the throughput in algorithmic GB/s (bytes the method
-must move per step / wall time per step), the scatter kernel's roofline
-(achieved bandwidth against the 8 TB/s HBM peak, timed with HIP events on the
-stream the kernel runs on) and the CPU oracle's throughput on the same input
-as a baseline.
+Each timed step is one dispatch_layout_and_scatter call, started with a cold
+Infinity Cache: before it, outside its HIP events, 512 MiB are written and
+read back. Prints one JSON line with the throughput in algorithmic GB/s (bytes
+the method must move per step / mean event time per step), the scatter
+kernel's roofline (achieved bandwidth against the 8 TB/s HBM peak, timed with
+HIP events on the stream the kernel runs on, under the same flush), the same
+step back to back without flushes as a side figure, and the CPU oracle's
+throughput on the same input as a baseline.
 """
 
 from __future__ import annotations
@@ -42,17 +45,15 @@ COMBINE_SOURCES = [os.path.join(ROOT, "moe_token_dispatch_amd", "csrc", "dispatc
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=500)
+    ap.add_argument("--steps", type=int, default=100, help="timed steps, each after a cache flush")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warm-steps", type=int, default=2000,
+                    help="steps of the side figure timed back to back without flushes")
     ap.add_argument("--workload", default=None, help="workload name (default: the metric workload)")
-    ap.add_argument("--event-every", type=int, default=8,
-                    help="bracket the scatter with HIP events on every n-th timed step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph-steps", type=int, default=1000,
                     help="steps replayed from a captured HIP graph, reported beside the eager steps (0 = skip)")
-    ap.add_argument("--cold-steps", type=int, default=100,
-                    help="steps timed one by one, back to back and after a 512 MiB cache-evicting read (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for counter calibration)")
     ap.add_argument("--expand", action="store_true",
@@ -489,23 +490,28 @@ def latency_bench(args):
           flush=True)
 
 
-def graph_step(args, dev, stream, prob, topk_d, lay, ws, x_d, sf_d, rows, total_b):
-    """The same step captured once into a HIP graph and replayed: the kernels
-    and buffers are the eager step's; only the launch path differs."""
+def graph_step(args, dev, stream, prob, topk_d, lay, ws, x_d, sf_d, rows, total_b, evict):
+    """The same step (the combined call) captured once into a HIP graph and
+    replayed, back to back and after the same flush as the timed steps: the
+    kernels and buffers are the eager step's; only the launch path differs."""
+    import statistics
+
     import torch
 
     import moe_token_dispatch_amd as M
 
+    def call():
+        M.dispatch_layout_and_scatter(prob, topk_d, lay, ws, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x,
+                                      rows.recv_sf)
+
     side = torch.cuda.Stream(device=dev)
     side.wait_stream(stream)
     with torch.cuda.stream(side):
-        M.dispatch_layout(prob, topk_d, lay, ws)
-        M.dispatch_scatter(prob, lay, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x, rows.recv_sf)
+        call()
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=side):
-        M.dispatch_layout(prob, topk_d, lay, ws)
-        M.dispatch_scatter(prob, lay, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x, rows.recv_sf)
+        call()
     for _ in range(max(1, args.graph_steps // 10)):
         graph.replay()
     torch.cuda.synchronize()
@@ -514,11 +520,23 @@ def graph_step(args, dev, stream, prob, topk_d, lay, ws, x_d, sf_d, rows, total_
         graph.replay()
     torch.cuda.synchronize()
     g_s = (time.perf_counter() - g0) / args.graph_steps
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(max(16, args.steps))]
+    for i, (e0, e1) in enumerate(marks):
+        evict(i)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    flushed_us = statistics.mean(a.elapsed_time(b) * 1e3 for a, b in marks)
     if int(lay.status.item()) != 0:
         raise RuntimeError("graph replay left a non-zero layout status")
     return {"value": round(total_b / g_s / 1e9, 1), "unit": "GB/s", "steps": args.graph_steps,
             "us_per_step": round(g_s * 1e6, 2),
-            "what": "the same layout + scatter step captured into a HIP graph and replayed"}
+            "flushed_us_per_step": round(flushed_us, 2),
+            "flushed_value": round(total_b / (flushed_us * 1e-6) / 1e9, 1),
+            "what": "the combined call captured into a HIP graph and replayed (back to back; and flushed as "
+                    "the timed steps)"}
 
 
 def main():
@@ -570,46 +588,65 @@ def main():
     _, step_kernels = M.dispatch_kernel_count(prob)
     one_kernel = step_kernels == 1
 
-    def step(ev=None):
-        if one_kernel:
-            if ev is not None:
-                ev[0].record(stream)
-            plan()
-            if ev is not None:
-                ev[1].record(stream)
-            return
-        plan.layout()
-        if ev is not None:
-            ev[0].record(stream)
-        plan.scatter()
-        if ev is not None:
-            ev[1].record(stream)
+    # 512 MiB written, then read back, before every flushed step (outside its
+    # events): the write evicts the step's data from the 256 MB Infinity Cache
+    # and the read turns the lines the write left dirty into clean ones, so
+    # that the timed step is not charged the sweep's own write-back.
+    scratch = torch.empty(64 << 20, dtype=torch.int64, device=dev)
+    sink = torch.empty((), dtype=torch.int64, device=dev)
+
+    def evict(i):
+        scratch.fill_(i)
+        torch.sum(scratch, dim=0, out=sink)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
 
     for _ in range(args.warmup):
-        step()
+        plan()
     torch.cuda.synchronize()
     if int(lay.status.item()) != 0:
         raise RuntimeError(f"dispatch status {int(lay.status.item())}")
 
-    # On every n-th timed step two events bracket the scatter kernel on the
-    # stream it runs on (sampling keeps the event records' own cost out of most
-    # steps); on the step before a sampled one, an event after its scatter
-    # gives the layout-plus-launch-gap span up to the sampled scatter's start.
-    every = max(1, args.event_every)
-    sampled = [i for i in range(args.steps) if i % every == every - 1]
-    events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for i in sampled}
-    before = {i - 1: torch.cuda.Event(enable_timing=True) for i in sampled if i > 0}
+    # The timed steps: one dispatch_layout_and_scatter call each (the layout
+    # kernels read the token rows ahead, then the scatter), after a flush,
+    # HIP events on the launch stream around the call.
+    marks = [(ev(), ev()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events.get(i))
-        if i in before:
-            before[i].record(stream)
+    for i, (e0, e1) in enumerate(marks):
+        evict(i)
+        e0.record(stream)
+        plan()
+        e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_us = [a.elapsed_time(b) * 1e3 for a, b in marks]
 
-    scatter_ms = [events[i][0].elapsed_time(events[i][1]) for i in sampled]
-    layout_ms = [before[i - 1].elapsed_time(events[i][0]) for i in sampled if i - 1 in before] or [0.0]
+    # The dominant kernel on its own, under the same flush: the same two
+    # parts the combined call enqueues (the read-ahead layout, then the
+    # scatter), with an event between them, on at least 16 steps.
+    n_roof = max(16, args.steps)
+    roof = [(ev(), ev(), ev()) for _ in range(n_roof)]
+    torch.cuda.synchronize()
+    for i, (e0, e1, e2) in enumerate(roof):
+        evict(i)
+        e0.record(stream)
+        if one_kernel:
+            plan()
+        else:
+            plan.layout_read_ahead()
+            e1.record(stream)
+            plan.scatter()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    if one_kernel:
+        kernel_us = [a.elapsed_time(c) * 1e3 for a, _, c in roof]
+        layout_us = [0.0]
+    else:
+        kernel_us = [b.elapsed_time(c) * 1e3 for _, b, c in roof]
+        layout_us = [a.elapsed_time(b) * 1e3 for a, b, _ in roof]
+
     p_rows = int(lay.expert_psum[-1].item())
     n_rank = int(lay.rank_psum[-1].item())
     t_live = int((inp.topk_idx >= 0).any(axis=1).sum())
@@ -620,16 +657,37 @@ def main():
     roof_kernel, roof_b = "scatter_kernel", sc_b
     if one_kernel:  # the one kernel moves the whole step's bytes
         roof_kernel, roof_b = "assign_kernel (one-kernel layout + scatter)", total_b
-    ms_per_step = wall / args.steps * 1e3
-    value = total_b / (wall / args.steps) / 1e9
-    sc_mean_ms = statistics.mean(scatter_ms)
-    achieved = roof_b / (sc_mean_ms * 1e-3) / 1e9
+    step_mean_us = statistics.mean(step_us)
+    ms_per_step = step_mean_us / 1e3
+    value = total_b / (step_mean_us * 1e-6) / 1e9
+    kernel_mean_us = statistics.mean(kernel_us)
+    achieved = roof_b / (kernel_mean_us * 1e-6) / 1e9
     traffic = None if one_kernel else load_traffic(workload=w.name)
 
+    def quant(us):
+        v = sorted(us)
+        q = lambda f: v[min(len(v) - 1, int(f * (len(v) - 1) + 0.5))]  # noqa: E731
+        return {"mean_us": round(statistics.mean(v), 2), "p10_us": round(q(0.1), 2),
+                "median_us": round(q(0.5), 2), "p90_us": round(q(0.9), 2)}
+
+    # Back to back, no flush between steps (the rows and the layout's inputs
+    # stay in the Infinity Cache from one step to the next): wall clock over
+    # warm_steps combined calls.
+    warm_steps = max(args.steps, args.warm_steps)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(warm_steps):
+        plan()
+    torch.cuda.synchronize()
+    warm_s = (time.perf_counter() - w0) / warm_steps
+    warm = {"steps": warm_steps, "us_per_step": round(warm_s * 1e6, 2),
+            "value": round(total_b / warm_s / 1e9, 1), "unit": "GB/s",
+            "hbm_frac": round(total_b / warm_s / 1e9 / HBM_PEAK_GBPS, 4),
+            "what": "the same combined call back to back with no flush (wall clock)"}
+
     # Cached dispatch: the same layout replayed, scatter only (the routing is
-    # unchanged, so the layout is not recomputed). Timed after, and outside,
-    # the main timed region.
-    replay_steps = max(1, args.steps // 4)
+    # unchanged, so the layout is not recomputed), back to back.
+    replay_steps = max(1, warm_steps // 4)
     torch.cuda.synchronize()
     r0 = time.perf_counter()
     for _ in range(replay_steps):
@@ -638,19 +696,19 @@ def main():
     replay_s = (time.perf_counter() - r0) / replay_steps
     replay = {"value": round(sc_b / replay_s / 1e9, 1), "unit": "GB/s", "steps": replay_steps,
               "us_per_step": round(replay_s * 1e6, 2),
-              "what": "dispatch_scatter alone on a saved layout (cached dispatch)"}
+              "what": "dispatch_scatter alone on a saved layout (cached dispatch), back to back"}
 
     graph_res = None
     if args.graph_steps > 0:
         try:
-            graph_res = graph_step(args, dev, stream, prob, topk_d, lay, ws, x_d, sf_d, rows, total_b)
+            graph_res = graph_step(args, dev, stream, prob, topk_d, lay, ws, x_d, sf_d, rows, total_b, evict)
         except Exception as exc:  # an optional figure: report it, keep the contract line
             torch.cuda.synchronize()
             graph_res = {"error": f"{type(exc).__name__}: {exc}"}
 
     # Layout alone, back to back (HIP events on the launch stream).
-    lay_steps = max(1, args.steps // 4)
-    ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    lay_steps = max(1, warm_steps // 4)
+    ev_a, ev_b = ev(), ev()
     torch.cuda.synchronize()
     ev_a.record(stream)
     for _ in range(lay_steps):
@@ -658,37 +716,8 @@ def main():
     ev_b.record(stream)
     torch.cuda.synchronize()
     layout_only_us = ev_a.elapsed_time(ev_b) * 1e3 / lay_steps
-
-    # One step at a time, HIP events around each: back to back, and with a
-    # 512 MiB read sweep before every step (outside its events) that pushes
-    # the previous step's data out of the 256 MB Infinity Cache. A read
-    # leaves clean lines behind; a write would leave dirty ones for the
-    # timed step to write back.
-    cold = None
-    if args.cold_steps > 0:
-        scratch = torch.ones(64 << 20, dtype=torch.int64, device=dev)
-        sink = torch.empty((), dtype=torch.int64, device=dev)
-
-        def per_step(evict):
-            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                     for _ in range(args.cold_steps)]
-            torch.cuda.synchronize()
-            for e0, e1 in pairs:
-                if evict:
-                    torch.sum(scratch, dim=0, out=sink)
-                e0.record(stream)
-                plan()
-                e1.record(stream)
-            torch.cuda.synchronize()
-            us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
-            q = lambda f: us[min(len(us) - 1, int(f * (len(us) - 1) + 0.5))]  # noqa: E731
-            return {"median_us": round(q(0.5), 2), "p10_us": round(q(0.1), 2), "p90_us": round(q(0.9), 2),
-                    "GBps_at_median": round(total_b / (q(0.5) * 1e-6) / 1e9, 1)}
-
-        cold = {"steps": args.cold_steps, "back_to_back": per_step(False), "after_512MiB_read": per_step(True),
-                "what": "layout + scatter, HIP events around each step"}
-        del scratch, sink
-        torch.cuda.empty_cache()
+    del scratch, sink
+    torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -725,16 +754,20 @@ def main():
             "outputs": "rank-contiguous + expert-major (zero pads)", "parallelism": "single GPU",
             "kernels_per_step": step_kernels, "seed": w.seed,
         },
+        "timing": ("mean of HIP-event step times over the timed steps; before each step, outside its "
+                   "events, 512 MiB are written and read back, so the step starts with none of its data "
+                   "in the Infinity Cache and no dirty lines to write back"),
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": total_b,
-        "tokens_per_s": round(t / (wall / args.steps), 1),
-        "pairs_per_s": round(p_valid / (wall / args.steps), 1),
-        "layout_and_gaps_us_mean": round(statistics.mean(layout_ms) * 1e3, 2),
-        ("step_kernel_us_mean" if one_kernel else "scatter_us_mean"): round(sc_mean_ms * 1e3, 2),
-        "layout_only_us": round(layout_only_us, 2),
-        "payload_GBps": round((n_rank + p_valid) * (w.row_bytes + 4 * s) / (wall / args.steps) / 1e9, 1),
-        "per_step_events": cold,
-        "scatter_event_samples": len(scatter_ms),
+        "step_events": quant(step_us),
+        "wall_s_timed_loop_incl_flushes": round(wall, 4),
+        "tokens_per_s": round(t / (ms_per_step * 1e-3), 1),
+        "pairs_per_s": round(p_valid / (ms_per_step * 1e-3), 1),
+        "payload_GBps": round((n_rank + p_valid) * (w.row_bytes + 4 * s) / (ms_per_step * 1e-3) / 1e9, 1),
+        ("step_kernel_events" if one_kernel else "scatter_events"): quant(kernel_us),
+        "layout_read_ahead_events": None if one_kernel else quant(layout_us),
+        "layout_only_us_back_to_back": round(layout_only_us, 2),
+        "warm_back_to_back": warm,
         "rows": {"expert_major": p_rows, "rank_contig": n_rank, "live_tokens": t_live, "pairs": p_valid},
         "roofline": {
             "kernel": roof_kernel,
@@ -744,7 +777,11 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
+            "traffic_counts": ("L2-to-fabric bytes (TCC_EA FETCH_SIZE + WRITE_SIZE, scaled by a plain copy); "
+                               "Infinity Cache hits count in them, gfx950 exposes no DRAM-side byte counter"),
             "algorithmic_bytes_per_launch": roof_b,
+            "event_samples": len(kernel_us),
+            "launch_us_mean": round(kernel_mean_us, 2),
         },
         "replay_scatter_only": replay,
         "graph_step": graph_res,

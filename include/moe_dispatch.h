@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define DISPATCH_ABI_VERSION 2
+#define DISPATCH_ABI_VERSION 3
 
 /* Limits. K <= 32 follows the page's bound on the top-k width (section 4.2);
  * R <= 1024 follows its kNumMaxRanks (section 6.2). */
@@ -143,6 +143,22 @@ int dispatch_layout(const dispatch_problem_t* problem, const void* topk_idx,
                     const dispatch_layout_t* out, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
+/* dispatch_layout, and while its kernels run, a read of the token rows x
+ * [T, row_bytes] (16-byte aligned) and of x_sf [T, S] (may be NULL) that
+ * leaves them in the GPU's Infinity Cache for a dispatch_scatter of the same
+ * rows that follows. The layout kernels are latency-bound and leave HBM
+ * idle; the scatter reads every live row once while it writes about
+ * fourteen times as many bytes, and rows it finds in the cache no longer
+ * interleave HBM reads into that write stream. Rows and scale factors of
+ * more than 160 MB together are not read (they would push their own first
+ * rows out of the 256 MB cache). Outputs, checks and errors are those of
+ * dispatch_layout, plus DISPATCH_ERR_ALIGN for a misaligned x or x_sf;
+ * nothing beyond the layout outputs is written. (Not a step of the page's
+ * method: a measure for MI355X's memory hierarchy.) */
+int dispatch_layout_read_ahead(const dispatch_problem_t* problem, const void* topk_idx,
+                               const dispatch_layout_t* out, void* workspace, size_t workspace_bytes,
+                               const void* x, const float* x_sf, hipStream_t stream);
+
 /* Row scatter of a layout made by dispatch_layout with the same problem
  * (sections 6.3, 7.3 and 8.2). Reads layout->expert_count, expert_psum,
  * expert_slot, rank_slot and status. x: device [T, row_bytes] (opaque bytes,
@@ -163,7 +179,7 @@ int dispatch_scatter(const dispatch_problem_t* problem, const dispatch_layout_t*
 
 /* dispatch_layout followed by dispatch_scatter in one call, with the same
  * arguments, checks, outputs and status semantics as those two calls made in
- * turn. A small batch (T * K up to 3072 pairs, or 2048 when pad rows are
+ * turn (the layout reads the rows ahead, as dispatch_layout_read_ahead). A small batch (T * K up to 3072 pairs, or 2048 when pad rows are
  * zeroed; fewer when E + R is large) is laid out and copied by a single
  * kernel: every workgroup ranks the whole batch itself, so none waits for
  * another, and each copies its share of the rows' 1 KB segments. That saves

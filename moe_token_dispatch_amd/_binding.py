@@ -17,7 +17,7 @@ import torch  # load torch's HIP runtime first so the library binds to the same 
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_dispatch.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 MAX_TOPK = 32
 MAX_EXPERTS = 4096
 MAX_RANKS = 1024
@@ -109,7 +109,8 @@ _LIB = None
 
 # Exported symbols of include/moe_dispatch.h.
 SYMBOLS = ("dispatch_abi_version", "dispatch_strerror", "dispatch_workspace_size",
-           "dispatch_max_rows", "dispatch_layout", "dispatch_scatter", "dispatch_layout_and_scatter",
+           "dispatch_max_rows", "dispatch_layout", "dispatch_layout_read_ahead", "dispatch_scatter",
+           "dispatch_layout_and_scatter",
            "dispatch_kernel_count",
            "dispatch_expand_workspace_size", "dispatch_expand_max_rows", "dispatch_expand_layout",
            "dispatch_expand_scatter", "dispatch_expand_layout_and_scatter", "dispatch_combine")
@@ -135,6 +136,9 @@ def load_library(path: str = LIB_PATH):
     lib.dispatch_max_rows.restype = i
     lib.dispatch_layout.argtypes = [ctypes.POINTER(Problem), p, ctypes.POINTER(LayoutPtrs), p, sz, p]
     lib.dispatch_layout.restype = i
+    lib.dispatch_layout_read_ahead.argtypes = [ctypes.POINTER(Problem), p, ctypes.POINTER(LayoutPtrs), p, sz, p, p,
+                                               p]
+    lib.dispatch_layout_read_ahead.restype = i
     lib.dispatch_scatter.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(LayoutPtrs), p, p, p, p, p, p, p]
     lib.dispatch_scatter.restype = i
     lib.dispatch_layout_and_scatter.argtypes = [ctypes.POINTER(Problem), p, ctypes.POINTER(LayoutPtrs), p, sz,
@@ -302,6 +306,33 @@ def dispatch_layout(problem: Problem, topk_idx: torch.Tensor, out: LayoutTensors
         raise DispatchError(rc, "dispatch_layout")
 
 
+def dispatch_layout_read_ahead(problem: Problem, topk_idx: torch.Tensor, out: LayoutTensors,
+                               workspace: torch.Tensor, x: torch.Tensor, x_sf: Optional[torch.Tensor] = None,
+                               stream: Optional[torch.cuda.Stream] = None,
+                               expert_count_cumulative: Optional[torch.Tensor] = None) -> None:
+    """dispatch_layout, reading the token rows ``x`` (and ``x_sf``) into the
+    Infinity Cache while it runs, for a dispatch_scatter of them that follows."""
+    _check_device_tensor(topk_idx, "topk_idx")
+    if topk_idx.element_size() != problem.topk_idx_bytes:
+        raise ValueError("topk_idx element width does not match problem.topk_idx_bytes")
+    _check_device_tensor(workspace, "workspace")
+    _check_device_tensor(x, "x")
+    if x_sf is not None:
+        _check_device_tensor(x_sf, "x_sf")
+    for f in dataclasses.fields(out):
+        _check_device_tensor(getattr(out, f.name), f.name, torch.int32)
+    _check_cumulative(expert_count_cumulative, problem.num_experts)
+    _check_dispatch_sizes(problem, topk_idx, out)
+    _need(x, "x", problem.num_tokens * problem.row_bytes)
+    _need(x_sf, "x_sf", 4 * problem.num_tokens * problem.sf_per_token)
+    lay = out.ptrs(expert_count_cumulative)
+    rc = load_library().dispatch_layout_read_ahead(ctypes.byref(problem), _ptr(topk_idx), ctypes.byref(lay),
+                                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                   _ptr(x), _ptr(x_sf), _stream_handle(stream, topk_idx.device))
+    if rc:
+        raise DispatchError(rc, "dispatch_layout_read_ahead")
+
+
 def dispatch_scatter(problem: Problem, layout: LayoutTensors, x: torch.Tensor,
                      x_sf: Optional[torch.Tensor], rank_x: Optional[torch.Tensor],
                      rank_sf: Optional[torch.Tensor], recv_x: Optional[torch.Tensor],
@@ -446,13 +477,18 @@ class Plan:
             _check_device_tensor(getattr(layout, f.name), f.name, torch.int32)
         _check_cumulative(expert_count_cumulative, problem.num_experts)
         _check_dispatch_sizes(problem, topk_idx, layout)
+        # The plan keeps its own copy of the problem: the tensor sizes were
+        # checked against these values, and a later change to the caller's
+        # struct must not reach the C calls.
+        problem = Problem.from_buffer_copy(problem)
+        self._problem = problem
         self._lib = load_library()
         self._keep = (problem, topk_idx, layout, workspace, x, x_sf, rows, expert_count_cumulative)
         self._lay = layout.ptrs(expert_count_cumulative)
         handle = _stream_handle(stream, topk_idx.device)
         self._layout_args = (ctypes.byref(problem), _ptr(topk_idx), ctypes.byref(self._lay), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), handle)
-        self._scatter_args = self._both_args = None
+        self._scatter_args = self._both_args = self._layout_ra_args = None
         if x is not None:
             _check_device_tensor(x, "x")
             rows = rows if rows is not None else RowBuffers(None, None, None, None)
@@ -467,11 +503,21 @@ class Plan:
                         _ptr(rows.recv_sf))
             self._scatter_args = (ctypes.byref(problem), ctypes.byref(self._lay), *row_ptrs, handle)
             self._both_args = (*self._layout_args[:-1], *row_ptrs, handle)
+            self._layout_ra_args = (*self._layout_args[:-1], _ptr(x), _ptr(x_sf), handle)
 
     def layout(self) -> None:
         rc = self._lib.dispatch_layout(*self._layout_args)
         if rc:
             raise DispatchError(rc, "dispatch_layout")
+
+    def layout_read_ahead(self) -> None:
+        """dispatch_layout_read_ahead: the layout, reading the plan's token rows
+        into the Infinity Cache for the scatter that follows."""
+        if self._layout_ra_args is None:
+            raise ValueError("this plan has no token batch to read ahead")
+        rc = self._lib.dispatch_layout_read_ahead(*self._layout_ra_args)
+        if rc:
+            raise DispatchError(rc, "dispatch_layout_read_ahead")
 
     def scatter(self) -> None:
         if self._scatter_args is None:
@@ -643,6 +689,9 @@ class ExpandPlan:
             if t is not None:
                 _check_device_tensor(t, name)
         _check_expand_sizes(problem, recv_topk_idx, recv_count, layout, recv_buf, recv_sf_buf, recv_x, recv_sf)
+        # Its own copy of the problem, as in Plan.
+        problem = ExpandProblem.from_buffer_copy(problem)
+        self._problem = problem
         self._lib = load_library()
         self._keep = (problem, recv_topk_idx, recv_count, layout, workspace, recv_buf, recv_sf_buf, recv_x, recv_sf,
                       expert_count_cumulative)

@@ -216,6 +216,25 @@ int dispatch_layout(const dispatch_problem_t* problem, const void* topk_idx, con
     return DISPATCH_OK;
 }
 
+int dispatch_layout_read_ahead(const dispatch_problem_t* problem, const void* topk_idx, const dispatch_layout_t* out,
+                               void* workspace, size_t workspace_bytes, const void* x, const float* x_sf,
+                               hipStream_t stream) {
+    TileGeometry g;
+    const int rc = check_layout_args(problem, topk_idx, out, workspace, workspace_bytes, &g);
+    if (rc != DISPATCH_OK) return rc;
+    const dispatch_problem_t& p = *problem;
+    if (p.num_tokens > 0 && p.row_bytes > 0 && x == nullptr) return DISPATCH_ERR_NULL;
+    if (p.num_tokens > 0 && p.sf_per_token > 0 && x_sf == nullptr) return DISPATCH_ERR_NULL;
+    if (p.row_bytes < 0 || p.row_bytes % 16 != 0 || (x && !aligned_to(x, 16)) || (x_sf && !aligned_to(x_sf, 4)))
+        return DISPATCH_ERR_ALIGN;
+    moe_dispatch::ReadAhead ra{x, p.num_tokens * p.row_bytes, x_sf, p.num_tokens * p.sf_per_token};
+    const bool read_ahead = moe_dispatch::read_ahead_fits(ra.x_bytes, ra.sf_words);
+    if (moe_dispatch::launch_layout(p, g, topk_idx, *out, workspace, stream, nullptr, read_ahead ? &ra : nullptr) !=
+        hipSuccess)
+        return DISPATCH_ERR_HIP;
+    return DISPATCH_OK;
+}
+
 int dispatch_kernel_count(const dispatch_problem_t* problem, int* layout_kernels, int* layout_and_scatter_kernels) {
     const int rc = check_problem(problem);
     if (rc != DISPATCH_OK) return rc;
@@ -244,7 +263,12 @@ int dispatch_layout_and_scatter(const dispatch_problem_t* problem, const void* t
             return DISPATCH_ERR_HIP;
         return DISPATCH_OK;
     }
-    if (moe_dispatch::launch_layout(p, g, topk_idx, *out, workspace, stream) != hipSuccess ||
+    // The layout kernels read the token rows ahead for the scatter when the
+    // batch fits the Infinity Cache.
+    moe_dispatch::ReadAhead ra{x, p.num_tokens * p.row_bytes, x_sf, p.num_tokens * p.sf_per_token};
+    const bool read_ahead = moe_dispatch::read_ahead_fits(ra.x_bytes, ra.sf_words);
+    if (moe_dispatch::launch_layout(p, g, topk_idx, *out, workspace, stream, nullptr,
+                                    read_ahead ? &ra : nullptr) != hipSuccess ||
         moe_dispatch::launch_scatter(p, *out, x, x_sf, rank_x, rank_sf, recv_x, recv_sf, stream,
                                      has_few_destinations(p)) != hipSuccess)
         return DISPATCH_ERR_HIP;

@@ -138,10 +138,29 @@ struct ExpandView {
     int32_t global_experts;     // E of the sending side
 };
 
+// Token rows that the layout kernels of a combined layout-and-scatter call
+// read ahead, into the Infinity Cache, for the scatter that follows: extra
+// workgroups of the count kernel read the first share, those of the assign
+// kernel the rest. Up to kReadAheadMaxBytes (rows and scale factors
+// together; larger batches are not read ahead: they would push their own
+// first rows out of the 256 MB cache before the scatter reads them).
+struct ReadAhead {
+    const void* x;
+    int64_t x_bytes;     // a multiple of 16
+    const float* x_sf;
+    int64_t sf_words;
+};
+constexpr int64_t kReadAheadMaxBytes = int64_t(160) << 20;
+constexpr int kReadAheadGroups = 256;     // read-ahead workgroups per layout kernel
+constexpr int kReadAheadCountPct = 35;    // percent of the rows the count kernel reads
+inline bool read_ahead_fits(int64_t x_bytes, int64_t sf_words) {
+    return x_bytes + 4 * sf_words <= kReadAheadMaxBytes;
+}
+
 // Launchers (defined in the .hip files). They return the HIP error of the launch.
 hipError_t launch_layout(const dispatch_problem_t& p, const TileGeometry& g, const void* topk_idx,
                          const dispatch_layout_t& out, void* workspace, hipStream_t stream,
-                         const ExpandView* expand = nullptr);
+                         const ExpandView* expand = nullptr, const ReadAhead* read_ahead = nullptr);
 // few_destinations: rows go to about one destination each (sets the segment width).
 hipError_t launch_scatter(const dispatch_problem_t& p, const dispatch_layout_t& lay, const void* x,
                           const float* x_sf, void* rank_x, float* rank_sf, void* recv_x,

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_binding_constants_match_header():
     d = _defines()
-    assert d["DISPATCH_ABI_VERSION"] == M.dispatch_abi_version() == 2
+    assert d["DISPATCH_ABI_VERSION"] == M.dispatch_abi_version() == 3
     assert (d["DISPATCH_ERR_NULL"], d["DISPATCH_ERR_ARG"], d["DISPATCH_ERR_ALIGN"],
             d["DISPATCH_ERR_WORKSPACE"], d["DISPATCH_ERR_HIP"]) == (
         M.ERR_NULL, M.ERR_ARG, M.ERR_ALIGN, M.ERR_WORKSPACE, M.ERR_HIP)
@@ -197,6 +197,32 @@ def test_layout_and_scatter_host_errors_before_launch():
     assert call(bad, 4096, good, 4096, ws_need, *rows) == M.ERR_ARG
 
 
+def test_layout_read_ahead_host_errors_before_launch():
+    """The read-ahead layout makes the layout's checks and those of the rows
+    it reads before enqueuing anything."""
+    lib = M.load_library()
+    p = M.Problem(100, 8, 256, 8, 1, 8, 4, 64, 1000, 1000, M.ALL_OUTPUTS, 0)
+    good = M.LayoutPtrs(*([4096] * 9))
+    ws_need = M.dispatch_workspace_size(p)
+
+    def call(prob, topk, lay, ws, n, x, sf):
+        return lib.dispatch_layout_read_ahead(ctypes.byref(prob) if prob is not None else None, topk,
+                                              ctypes.byref(lay) if lay is not None else None, ws, n, x, sf, None)
+
+    assert call(None, 4096, good, 4096, ws_need, 4096, 4096) == M.ERR_NULL
+    assert call(p, None, good, 4096, ws_need, 4096, 4096) == M.ERR_NULL
+    assert call(p, 4096, None, 4096, ws_need, 4096, 4096) == M.ERR_NULL
+    assert call(p, 4096, good, None, ws_need, 4096, 4096) == M.ERR_WORKSPACE
+    assert call(p, 4096, good, 4096, ws_need - 1, 4096, 4096) == M.ERR_WORKSPACE
+    assert call(p, 4100, good, 4096, ws_need, 4096, 4096) == M.ERR_ALIGN
+    assert call(p, 4096, good, 4096, ws_need, None, 4096) == M.ERR_NULL   # no rows
+    assert call(p, 4096, good, 4096, ws_need, 4096, None) == M.ERR_NULL   # S > 0 needs scale factors
+    assert call(p, 4096, good, 4096, ws_need, 4104, 4096) == M.ERR_ALIGN  # rows 16-byte aligned
+    assert call(p, 4096, good, 4096, ws_need, 4096, 4098) == M.ERR_ALIGN  # scale factors 4-byte aligned
+    bad = M.Problem(100, 8, 256, 8, 1, 8, 4, 72, 1000, 1000, M.ALL_OUTPUTS, 0)  # row_bytes % 16
+    assert call(bad, 4096, good, 4096, ws_need, 4096, 4096) == M.ERR_ALIGN
+
+
 def test_binding_refuses_host_tensors():
     import torch
 
@@ -265,3 +291,51 @@ def test_combine_host_errors():
     assert lib.dispatch_combine(None, 4096, 4096, 4096, 4096, None) == M.ERR_NULL
     empty = M.CombineProblem(**dict(good, num_tokens=0))
     assert call(empty, None, None, None, None) == M.OK  # nothing to do, nothing launched
+
+
+def test_plans_keep_their_own_problem(monkeypatch):
+    """A plan checks its tensors against the problem once; a later change to
+    the caller's struct must not reach its C calls (host tensors stand in for
+    device ones here: nothing is launched)."""
+    import torch
+
+    from moe_token_dispatch_amd import _binding as B
+
+    monkeypatch.setattr(B, "_check_device_tensor", lambda t, name, dtype=None: None)
+    monkeypatch.setattr(B, "_stream_handle", lambda stream, device: ctypes.c_void_p(0))
+    p = M.make_problem(64, 8, 256, 8, 1, row_bytes=256)
+    i32 = lambda n: torch.zeros(max(n, 1), dtype=torch.int32)  # noqa: E731
+    lay = M.LayoutTensors(i32(256), i32(8), i32(257), i32(9), i32(512), i32(512),
+                          i32(p.recv_capacity_rows), i32(p.rank_capacity_rows), i32(1))
+    topk = torch.zeros((64, 8), dtype=torch.int64)
+    ws = torch.zeros(M.dispatch_workspace_size(p), dtype=torch.uint8)
+    x = torch.zeros((64, 256), dtype=torch.uint8)
+    rows = M.RowBuffers(rank_x=torch.zeros((p.rank_capacity_rows, 256), dtype=torch.uint8), rank_sf=None,
+                        recv_x=torch.zeros((p.recv_capacity_rows, 256), dtype=torch.uint8), recv_sf=None)
+    plan = M.Plan(p, topk, lay, ws, x, None, rows)
+    p.num_tokens = 1 << 20
+    p.recv_capacity_rows = 1 << 30
+    for args in (plan._layout_args, plan._scatter_args, plan._both_args):
+        q = args[0]._obj
+        assert q is plan._problem and q is not p
+        assert q.num_tokens == 64 and q.recv_capacity_rows == 64 * 8
+
+
+def test_expand_plan_keeps_its_own_problem(monkeypatch):
+    import torch
+
+    from moe_token_dispatch_amd import _binding as B
+
+    monkeypatch.setattr(B, "_check_device_tensor", lambda t, name, dtype=None: None)
+    monkeypatch.setattr(B, "_stream_handle", lambda stream, device: ctypes.c_void_p(0))
+    q = M.make_expand_problem(4, 16, 8, 256, 8, 0, row_bytes=256)
+    cap = q.recv_capacity_rows
+    i32 = lambda n: torch.zeros(max(n, 1), dtype=torch.int32)  # noqa: E731
+    lay = M.ExpandLayoutTensors(i32(32), i32(33), i32(64 * 8), i32(cap), i32(1))
+    plan = M.ExpandPlan(q, torch.zeros((64, 8), dtype=torch.int64), i32(4), lay,
+                        torch.zeros(M.dispatch_expand_workspace_size(q), dtype=torch.uint8),
+                        torch.zeros((64, 256), dtype=torch.uint8), None,
+                        torch.zeros((cap, 256), dtype=torch.uint8), None)
+    q.rows_per_source = 1 << 20
+    for args in (plan._layout_args, plan._scatter_args, plan._both_args):
+        assert args[0]._obj is plan._problem and plan._problem.rows_per_source == 16

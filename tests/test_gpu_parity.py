@@ -50,14 +50,18 @@ def test_reduced_workload_full_parity(name, t):
 # The five workloads at full size, in the launch configuration the benchmark
 # times: the whole layout bit-exact, rows checked against the oracle on
 # samples (full rows for the smaller ones) and on every row by a device gather.
+# The benchmark times the combined call (the layout kernels read the token
+# rows ahead for the scatter when they fit the Infinity Cache); the two
+# separate calls are checked as well.
+@pytest.mark.parametrize("combined", [True, False], ids=["one_call", "two_calls"])
 @pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
-def test_workload_full_size(name):
+def test_workload_full_size(name, combined):
     w = W.get(name)
-    _banner(w.describe())
+    _banner(f"{w.describe()} combined={combined}")
     inp = W.make_inputs(w)
     xb = inp.x_bytes()
     ref = oracle.layout(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment)
-    run = H.run_gpu(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment, xb, inp.x_sf)
+    run = H.run_gpu(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment, xb, inp.x_sf, combined=combined)
     H.assert_layout_equal(run, ref)
     if w.num_tokens * w.row_bytes <= 64 << 20:
         H.assert_rows_full(run, ref, xb, inp.x_sf)
@@ -115,6 +119,9 @@ def test_token_counts_around_tiles(t):
 def test_layout_geometry_paths(t, k, e, r):
     _banner(f"geometry T={t} K={k} E={e} R={r}")
     _edge(_uniform(11, t, k, e, 0.05), e, r, 2, row_bytes=16)
+    # The combined call on the same shape: its layout kernels carry the
+    # read-ahead workgroups (and on the column-scan path, three kernels).
+    _edge(_uniform(11, t, k, e, 0.05), e, r, 2, row_bytes=16, s=3, combined=True)
 
 
 @pytest.mark.parametrize("k,e,r", [(1, 8, 2), (2, 16, 16), (3, 12, 4), (6, 64, 8), (7, 128, 128),
@@ -128,6 +135,9 @@ def test_topk_and_expert_shapes(k, e, r):
 def test_alignments(a):
     _banner(f"A={a}")
     _edge(_uniform(6, 900, 8, 64, 0.02), 64, 8, a, row_bytes=80, s=5)
+    # Combined call: pad entries of the inverse map are dealt over the layout
+    # workgroups only, not over the read-ahead workgroups of the same launch.
+    _edge(_uniform(6, 900, 8, 64, 0.02), 64, 8, a, row_bytes=80, s=5, combined=True)
 
 
 # Pad rows of small batches. While the routed rows can reach fewer blocks of
