@@ -190,6 +190,23 @@ int dispatch_layout_and_scatter(const dispatch_problem_t* problem, const void* t
                                 const void* x, const float* x_sf, void* rank_x, float* rank_sf,
                                 void* recv_x, float* recv_sf, hipStream_t stream);
 
+/* dispatch_layout_and_scatter without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. The layout's workspace is a
+ * device array of DISPATCH_NOALLOC_WORKSPACE_BYTES inside the library (one
+ * per GPU, held until the process ends); the call allocates nothing. A
+ * problem whose dispatch_workspace_size() exceeds that size returns
+ * DISPATCH_ERR_WORKSPACE before anything is enqueued; every other argument,
+ * check and output is that of dispatch_layout_and_scatter. The array needs
+ * no clearing, but calls that overlap in time on one GPU (concurrent
+ * streams) share it and race: serialize them, or use
+ * dispatch_layout_and_scatter with a workspace per stream. */
+#define DISPATCH_NOALLOC_WORKSPACE_BYTES 4194304 /* 4 MiB */
+int dispatch_layout_and_scatter_noalloc(const dispatch_problem_t* problem, const void* topk_idx,
+                                        const dispatch_layout_t* out, const void* x, const float* x_sf,
+                                        void* rank_x, float* rank_sf, void* recv_x, float* recv_sf,
+                                        hipStream_t stream);
+
 /* Kernels the calls above launch for this problem (its T, K, E, R and
  * row_bytes are read): *layout_kernels for dispatch_layout (1 when one tile
  * holds the batch, 2 with the tile histograms reduced in the assign kernel, 3

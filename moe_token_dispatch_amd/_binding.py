@@ -110,7 +110,7 @@ _LIB = None
 # Exported symbols of include/moe_dispatch.h.
 SYMBOLS = ("dispatch_abi_version", "dispatch_strerror", "dispatch_workspace_size",
            "dispatch_max_rows", "dispatch_layout", "dispatch_layout_read_ahead", "dispatch_scatter",
-           "dispatch_layout_and_scatter",
+           "dispatch_layout_and_scatter", "dispatch_layout_and_scatter_noalloc",
            "dispatch_kernel_count",
            "dispatch_expand_workspace_size", "dispatch_expand_max_rows", "dispatch_expand_layout",
            "dispatch_expand_scatter", "dispatch_expand_layout_and_scatter", "dispatch_combine")
@@ -144,6 +144,9 @@ def load_library(path: str = LIB_PATH):
     lib.dispatch_layout_and_scatter.argtypes = [ctypes.POINTER(Problem), p, ctypes.POINTER(LayoutPtrs), p, sz,
                                                 p, p, p, p, p, p, p]
     lib.dispatch_layout_and_scatter.restype = i
+    lib.dispatch_layout_and_scatter_noalloc.argtypes = [ctypes.POINTER(Problem), p, ctypes.POINTER(LayoutPtrs),
+                                                        p, p, p, p, p, p, p]
+    lib.dispatch_layout_and_scatter_noalloc.restype = i
     lib.dispatch_kernel_count.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(i), ctypes.POINTER(i)]
     lib.dispatch_kernel_count.restype = i
     ep = ctypes.POINTER(ExpandProblem)
@@ -393,6 +396,35 @@ def dispatch_layout_and_scatter(problem: Problem, topk_idx: torch.Tensor, out: L
         _ptr(recv_x), _ptr(recv_sf), _stream_handle(stream, topk_idx.device))
     if rc:
         raise DispatchError(rc, "dispatch_layout_and_scatter")
+
+
+def dispatch_layout_and_scatter_noalloc(problem: Problem, topk_idx: torch.Tensor, out: LayoutTensors,
+                                        x: torch.Tensor, x_sf: Optional[torch.Tensor],
+                                        rank_x: Optional[torch.Tensor], rank_sf: Optional[torch.Tensor],
+                                        recv_x: Optional[torch.Tensor], recv_sf: Optional[torch.Tensor],
+                                        stream: Optional[torch.cuda.Stream] = None,
+                                        expert_count_cumulative: Optional[torch.Tensor] = None) -> None:
+    """dispatch_layout_and_scatter with the library's own fixed workspace (no
+    workspace argument, nothing allocated). Calls that overlap on one GPU race."""
+    _check_device_tensor(topk_idx, "topk_idx")
+    if topk_idx.element_size() != problem.topk_idx_bytes:
+        raise ValueError("topk_idx element width does not match problem.topk_idx_bytes")
+    for f in dataclasses.fields(out):
+        _check_device_tensor(getattr(out, f.name), f.name, torch.int32)
+    _check_cumulative(expert_count_cumulative, problem.num_experts)
+    _check_device_tensor(x, "x")
+    for name, t in (("x_sf", x_sf), ("rank_x", rank_x), ("rank_sf", rank_sf), ("recv_x", recv_x),
+                    ("recv_sf", recv_sf)):
+        if t is not None:
+            _check_device_tensor(t, name)
+    _check_dispatch_sizes(problem, topk_idx, out)
+    _check_dispatch_rows(problem, x, x_sf, rank_x, rank_sf, recv_x, recv_sf)
+    lay = out.ptrs(expert_count_cumulative)
+    rc = load_library().dispatch_layout_and_scatter_noalloc(
+        ctypes.byref(problem), _ptr(topk_idx), ctypes.byref(lay), _ptr(x), _ptr(x_sf), _ptr(rank_x),
+        _ptr(rank_sf), _ptr(recv_x), _ptr(recv_sf), _stream_handle(stream, topk_idx.device))
+    if rc:
+        raise DispatchError(rc, "dispatch_layout_and_scatter_noalloc")
 
 
 # ------------------------------------------------- allocation helpers (plumbing)

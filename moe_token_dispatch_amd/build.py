@@ -20,7 +20,8 @@ LIB_NAME = "libmoe_dispatch.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["dispatch_api.cpp", "dispatch_layout.hip", "dispatch_scatter.hip", "dispatch_combine.hip"]
+SOURCES = ["dispatch_api.cpp", "dispatch_layout.hip", "dispatch_scatter.hip", "dispatch_combine.hip",
+           "dispatch_noalloc.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -339,3 +339,20 @@ def test_expand_plan_keeps_its_own_problem(monkeypatch):
     q.rows_per_source = 1 << 20
     for args in (plan._layout_args, plan._scatter_args, plan._both_args):
         assert args[0]._obj is plan._problem and plan._problem.rows_per_source == 16
+
+
+def test_noalloc_host_errors_before_launch():
+    """The allocation-free call refuses a problem whose workspace exceeds its
+    fixed device array, and a NULL problem, before anything is enqueued."""
+    lib = M.load_library()
+    good = M.LayoutPtrs(*([4096] * 9))
+    call = lambda prob: lib.dispatch_layout_and_scatter_noalloc(  # noqa: E731
+        ctypes.byref(prob) if prob is not None else None, 4096, ctypes.byref(good), 4096, 4096, 4096, 4096,
+        4096, 4096, None)
+    big = M.make_problem(200000, 8, 4096, 1024, 1, row_bytes=16)
+    assert M.dispatch_workspace_size(big) > 4194304
+    assert call(big) == M.ERR_WORKSPACE
+    assert call(None) == M.ERR_NULL
+    bad = M.make_problem(100, 8, 256, 8, 1, row_bytes=16)
+    bad.num_topk = 0
+    assert call(bad) == M.ERR_ARG
