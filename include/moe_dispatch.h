@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define DISPATCH_ABI_VERSION 3
+#define DISPATCH_ABI_VERSION 4
 
 /* Limits. K <= 32 follows the page's bound on the top-k width (section 4.2);
  * R <= 1024 follows its kNumMaxRanks (section 6.2). */
@@ -113,6 +113,24 @@ typedef struct dispatch_layout {
      * it wraps modulo 2^32, so a caller that keeps it over more than 2^31 rows
      * per expert reads and clears it from time to time. */
     int32_t* expert_count_cumulative;
+    /* Optional (NULL = off), 8-byte aligned, dispatch_row_order_size() ints:
+     * the order in which dispatch_scatter writes the rows. Entry 0 is the
+     * number n of routed rows (valid pairs plus rank rows), entry 1 is 0,
+     * then n (dest, token) pairs: dest >= 0 is a recv_x row, dest < 0 the
+     * rank_x row -1 - dest. The rows of each layout tile (a run of
+     * consecutive tokens) come together, after those of the earlier tiles,
+     * grouped by expert then by rank, each group in slot order. With it,
+     * dispatch_scatter walks the destinations in this order: consecutive
+     * workgroups fill consecutive rows of a bucket, each reading its slice
+     * of the source row (an MI355X choice, not a step of the page's method).
+     * It is kept only where that measured faster than walking the sources:
+     * rows of 4 to 8 KB with several destinations each (K expert rows, or
+     * expert and rank rows), E + R <= 2048, and T * (row_bytes + 4 * S) <=
+     * 160 MB (rows the layout reads ahead into the Infinity Cache, see
+     * dispatch_layout_read_ahead). Otherwise entry 0 is set to -1 and the
+     * scatter walks the source rows. Written by dispatch_layout when the
+     * status is 0. */
+    int32_t* row_order;
 } dispatch_layout_t;
 
 /* Version of this ABI (DISPATCH_ABI_VERSION). */
@@ -133,6 +151,10 @@ int dispatch_workspace_size(const dispatch_problem_t* problem, size_t* bytes);
  * output pointer may be NULL. */
 int dispatch_max_rows(const dispatch_problem_t* problem, int64_t* max_recv_rows,
                       int64_t* max_rank_rows);
+
+/* Length in int32 of a layout's optional row_order array:
+ * 2 + 2 * (T*K + T*min(K, R)). */
+int dispatch_row_order_size(const dispatch_problem_t* problem, int64_t* ints);
 
 /* Count -> Prefix Sum -> slot assignment (sections 4, 5, 6.2, 6.4 and 7).
  * topk_idx: device [T, K] row-major of problem->topk_idx_bytes wide signed

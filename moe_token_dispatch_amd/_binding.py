@@ -17,7 +17,7 @@ import torch  # load torch's HIP runtime first so the library binds to the same 
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_dispatch.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 MAX_TOPK = 32
 MAX_EXPERTS = 4096
 MAX_RANKS = 1024
@@ -71,7 +71,7 @@ class LayoutPtrs(ctypes.Structure):
 
     _fields_ = [(name, ctypes.c_void_p) for name in (
         "expert_count", "rank_count", "expert_psum", "rank_psum", "expert_slot", "rank_slot",
-        "recv_src_token_idx", "rank_src_token_idx", "status", "expert_count_cumulative")]
+        "recv_src_token_idx", "rank_src_token_idx", "status", "expert_count_cumulative", "row_order")]
 
 
 class ExpandProblem(ctypes.Structure):
@@ -109,8 +109,8 @@ _LIB = None
 
 # Exported symbols of include/moe_dispatch.h.
 SYMBOLS = ("dispatch_abi_version", "dispatch_strerror", "dispatch_workspace_size",
-           "dispatch_max_rows", "dispatch_layout", "dispatch_layout_read_ahead", "dispatch_scatter",
-           "dispatch_layout_and_scatter", "dispatch_layout_and_scatter_noalloc",
+           "dispatch_max_rows", "dispatch_row_order_size", "dispatch_layout", "dispatch_layout_read_ahead",
+           "dispatch_scatter", "dispatch_layout_and_scatter", "dispatch_layout_and_scatter_noalloc",
            "dispatch_kernel_count",
            "dispatch_expand_workspace_size", "dispatch_expand_max_rows", "dispatch_expand_layout",
            "dispatch_expand_scatter", "dispatch_expand_layout_and_scatter", "dispatch_combine")
@@ -134,6 +134,8 @@ def load_library(path: str = LIB_PATH):
     lib.dispatch_max_rows.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_int64),
                                       ctypes.POINTER(ctypes.c_int64)]
     lib.dispatch_max_rows.restype = i
+    lib.dispatch_row_order_size.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_int64)]
+    lib.dispatch_row_order_size.restype = i
     lib.dispatch_layout.argtypes = [ctypes.POINTER(Problem), p, ctypes.POINTER(LayoutPtrs), p, sz, p]
     lib.dispatch_layout.restype = i
     lib.dispatch_layout_read_ahead.argtypes = [ctypes.POINTER(Problem), p, ctypes.POINTER(LayoutPtrs), p, sz, p, p,
@@ -187,6 +189,15 @@ def dispatch_workspace_size(problem: Problem) -> int:
     return int(out.value)
 
 
+def dispatch_row_order_size(problem: Problem) -> int:
+    """int32 entries of a layout's row_order: 2 + 2 * (T*K + T*min(K, R))."""
+    n = ctypes.c_int64(0)
+    rc = load_library().dispatch_row_order_size(ctypes.byref(problem), ctypes.byref(n))
+    if rc:
+        raise DispatchError(rc, "dispatch_row_order_size")
+    return int(n.value)
+
+
 def dispatch_max_rows(problem: Problem) -> Tuple[int, int]:
     recv, rank = ctypes.c_int64(0), ctypes.c_int64(0)
     rc = load_library().dispatch_max_rows(ctypes.byref(problem), ctypes.byref(recv), ctypes.byref(rank))
@@ -217,12 +228,24 @@ class LayoutTensors:
     recv_src_token_idx: torch.Tensor
     rank_src_token_idx: torch.Tensor
     status: torch.Tensor
+    # Optional [dispatch_row_order_size] int32: the order the scatter writes
+    # the rows in (rows of 4 KB or more); None = the source-major scatter.
+    row_order: Optional[torch.Tensor] = None
 
     def ptrs(self, expert_count_cumulative: Optional[torch.Tensor] = None) -> LayoutPtrs:
         return LayoutPtrs(*[t.data_ptr() for t in (
             self.expert_count, self.rank_count, self.expert_psum, self.rank_psum, self.expert_slot,
             self.rank_slot, self.recv_src_token_idx, self.rank_src_token_idx, self.status)],
-            _ptr(expert_count_cumulative))
+            _ptr(expert_count_cumulative), _ptr(self.row_order))
+
+    def tensors(self):
+        """(name, tensor) of every output present."""
+        return [(f.name, getattr(self, f.name)) for f in dataclasses.fields(self) if getattr(self, f.name) is not None]
+
+
+def _fields_of(layout):
+    """(name, tensor) of every layout output present (optional ones may be None)."""
+    return [(f.name, getattr(layout, f.name)) for f in dataclasses.fields(layout) if getattr(layout, f.name) is not None]
 
 
 def _check_device_tensor(t: torch.Tensor, name: str, dtype=None):
@@ -256,6 +279,8 @@ def _check_dispatch_sizes(problem: Problem, topk_idx: Optional[torch.Tensor], la
                     ("recv_src_token_idx", problem.recv_capacity_rows),
                     ("rank_src_token_idx", problem.rank_capacity_rows), ("status", 1)):
         _need(getattr(layout, name), name, 4 * n)
+    if getattr(layout, "row_order", None) is not None:
+        _need(layout.row_order, "row_order", 4 * dispatch_row_order_size(problem))
 
 
 def _check_dispatch_rows(problem: Problem, x, x_sf, rank_x, rank_sf, recv_x, recv_sf) -> None:
@@ -297,8 +322,8 @@ def dispatch_layout(problem: Problem, topk_idx: torch.Tensor, out: LayoutTensors
     if topk_idx.element_size() != problem.topk_idx_bytes:
         raise ValueError("topk_idx element width does not match problem.topk_idx_bytes")
     _check_device_tensor(workspace, "workspace")
-    for f in dataclasses.fields(out):
-        _check_device_tensor(getattr(out, f.name), f.name, torch.int32)
+    for name, t in _fields_of(out):
+        _check_device_tensor(t, name, torch.int32)
     _check_cumulative(expert_count_cumulative, problem.num_experts)
     _check_dispatch_sizes(problem, topk_idx, out)
     lay = out.ptrs(expert_count_cumulative)
@@ -322,8 +347,8 @@ def dispatch_layout_read_ahead(problem: Problem, topk_idx: torch.Tensor, out: La
     _check_device_tensor(x, "x")
     if x_sf is not None:
         _check_device_tensor(x_sf, "x_sf")
-    for f in dataclasses.fields(out):
-        _check_device_tensor(getattr(out, f.name), f.name, torch.int32)
+    for name, t in _fields_of(out):
+        _check_device_tensor(t, name, torch.int32)
     _check_cumulative(expert_count_cumulative, problem.num_experts)
     _check_dispatch_sizes(problem, topk_idx, out)
     _need(x, "x", problem.num_tokens * problem.row_bytes)
@@ -346,8 +371,8 @@ def dispatch_scatter(problem: Problem, layout: LayoutTensors, x: torch.Tensor,
                     ("recv_sf", recv_sf)):
         if t is not None:
             _check_device_tensor(t, name)
-    for f in dataclasses.fields(layout):
-        _check_device_tensor(getattr(layout, f.name), f.name, torch.int32)
+    for name, t in _fields_of(layout):
+        _check_device_tensor(t, name, torch.int32)
     _check_dispatch_sizes(problem, None, layout)
     _check_dispatch_rows(problem, x, x_sf, rank_x, rank_sf, recv_x, recv_sf)
     lay = layout.ptrs()
@@ -379,8 +404,8 @@ def dispatch_layout_and_scatter(problem: Problem, topk_idx: torch.Tensor, out: L
     if topk_idx.element_size() != problem.topk_idx_bytes:
         raise ValueError("topk_idx element width does not match problem.topk_idx_bytes")
     _check_device_tensor(workspace, "workspace")
-    for f in dataclasses.fields(out):
-        _check_device_tensor(getattr(out, f.name), f.name, torch.int32)
+    for name, t in _fields_of(out):
+        _check_device_tensor(t, name, torch.int32)
     _check_cumulative(expert_count_cumulative, problem.num_experts)
     _check_device_tensor(x, "x")
     for name, t in (("x_sf", x_sf), ("rank_x", rank_x), ("rank_sf", rank_sf), ("recv_x", recv_x),
@@ -409,8 +434,8 @@ def dispatch_layout_and_scatter_noalloc(problem: Problem, topk_idx: torch.Tensor
     _check_device_tensor(topk_idx, "topk_idx")
     if topk_idx.element_size() != problem.topk_idx_bytes:
         raise ValueError("topk_idx element width does not match problem.topk_idx_bytes")
-    for f in dataclasses.fields(out):
-        _check_device_tensor(getattr(out, f.name), f.name, torch.int32)
+    for name, t in _fields_of(out):
+        _check_device_tensor(t, name, torch.int32)
     _check_cumulative(expert_count_cumulative, problem.num_experts)
     _check_device_tensor(x, "x")
     for name, t in (("x_sf", x_sf), ("rank_x", rank_x), ("rank_sf", rank_sf), ("recv_x", recv_x),
@@ -443,10 +468,12 @@ def make_problem(num_tokens: int, num_topk: int, num_experts: int, num_ranks: in
     return p
 
 
-def alloc_layout(problem: Problem, device) -> LayoutTensors:
+def alloc_layout(problem: Problem, device, row_order: bool = True) -> LayoutTensors:
+    """Layout outputs, with the row order unless ``row_order`` is False."""
     i32 = dict(dtype=torch.int32, device=device)
     t, k = problem.num_tokens, problem.num_topk
     return LayoutTensors(
+        row_order=torch.empty(dispatch_row_order_size(problem), **i32) if row_order else None,
         expert_count=torch.empty(problem.num_experts, **i32),
         rank_count=torch.empty(problem.num_ranks, **i32),
         expert_psum=torch.empty(problem.num_experts + 1, **i32),
@@ -505,8 +532,8 @@ class Plan:
         if topk_idx.element_size() != problem.topk_idx_bytes:
             raise ValueError("topk_idx element width does not match problem.topk_idx_bytes")
         _check_device_tensor(workspace, "workspace")
-        for f in dataclasses.fields(layout):
-            _check_device_tensor(getattr(layout, f.name), f.name, torch.int32)
+        for name, t in _fields_of(layout):
+            _check_device_tensor(t, name, torch.int32)
         _check_cumulative(expert_count_cumulative, problem.num_experts)
         _check_dispatch_sizes(problem, topk_idx, layout)
         # The plan keeps its own copy of the problem: the tensor sizes were
@@ -605,7 +632,7 @@ class ExpandLayoutTensors:
     def ptrs(self, expert_count_cumulative: Optional[torch.Tensor] = None) -> LayoutPtrs:
         return LayoutPtrs(self.expert_count.data_ptr(), None, self.expert_psum.data_ptr(), None,
                           self.expert_slot.data_ptr(), None, self.recv_src_row_idx.data_ptr(), None,
-                          self.status.data_ptr(), _ptr(expert_count_cumulative))
+                          self.status.data_ptr(), _ptr(expert_count_cumulative), None)
 
 
 def alloc_expand_layout(problem: ExpandProblem, device) -> ExpandLayoutTensors:
@@ -636,8 +663,8 @@ def dispatch_expand_layout(problem: ExpandProblem, recv_topk_idx: torch.Tensor, 
         raise ValueError("recv_topk_idx element width does not match problem.topk_idx_bytes")
     _check_device_tensor(recv_count, "recv_count", torch.int32)
     _check_device_tensor(workspace, "workspace")
-    for f in dataclasses.fields(out):
-        _check_device_tensor(getattr(out, f.name), f.name, torch.int32)
+    for name, t in _fields_of(out):
+        _check_device_tensor(t, name, torch.int32)
     _check_cumulative(expert_count_cumulative, problem.num_experts // problem.num_ranks)
     _check_expand_sizes(problem, recv_topk_idx, recv_count, out, None, None, None, None)
     lay = out.ptrs(expert_count_cumulative)
@@ -661,8 +688,8 @@ def dispatch_expand_layout_and_scatter(problem: ExpandProblem, recv_topk_idx: to
         raise ValueError("recv_topk_idx element width does not match problem.topk_idx_bytes")
     _check_device_tensor(recv_count, "recv_count", torch.int32)
     _check_device_tensor(workspace, "workspace")
-    for f in dataclasses.fields(out):
-        _check_device_tensor(getattr(out, f.name), f.name, torch.int32)
+    for name, t in _fields_of(out):
+        _check_device_tensor(t, name, torch.int32)
     _check_cumulative(expert_count_cumulative, problem.num_experts // problem.num_ranks)
     _check_device_tensor(recv_buf, "recv_buf")
     for name, t in (("recv_sf_buf", recv_sf_buf), ("recv_x", recv_x), ("recv_sf", recv_sf)):
@@ -686,8 +713,8 @@ def dispatch_expand_scatter(problem: ExpandProblem, layout: ExpandLayoutTensors,
     for name, t in (("recv_sf_buf", recv_sf_buf), ("recv_x", recv_x), ("recv_sf", recv_sf)):
         if t is not None:
             _check_device_tensor(t, name)
-    for f in dataclasses.fields(layout):
-        _check_device_tensor(getattr(layout, f.name), f.name, torch.int32)
+    for name, t in _fields_of(layout):
+        _check_device_tensor(t, name, torch.int32)
     _check_expand_sizes(problem, None, None, layout, recv_buf, recv_sf_buf, recv_x, recv_sf)
     lay = layout.ptrs()
     rc = load_library().dispatch_expand_scatter(ctypes.byref(problem), ctypes.byref(lay), _ptr(recv_buf),
@@ -713,8 +740,8 @@ class ExpandPlan:
             raise ValueError("recv_topk_idx element width does not match problem.topk_idx_bytes")
         _check_device_tensor(recv_count, "recv_count", torch.int32)
         _check_device_tensor(workspace, "workspace")
-        for f in dataclasses.fields(layout):
-            _check_device_tensor(getattr(layout, f.name), f.name, torch.int32)
+        for name, t in _fields_of(layout):
+            _check_device_tensor(t, name, torch.int32)
         _check_cumulative(expert_count_cumulative, problem.num_experts // problem.num_ranks)
         _check_device_tensor(recv_buf, "recv_buf")
         for name, t in (("recv_sf_buf", recv_sf_buf), ("recv_x", recv_x), ("recv_sf", recv_sf)):

@@ -63,7 +63,8 @@ int check_expand(const dispatch_expand_problem_t* q, dispatch_problem_t* p) {
 
 // Host checks of a row scatter's arguments (the problem already checked).
 int check_scatter_args(const dispatch_problem_t& p, const dispatch_layout_t* layout, const void* x,
-                       const float* x_sf, void* rank_x, float* rank_sf, void* recv_x, float* recv_sf) {
+                       const float* x_sf, void* rank_x, float* rank_sf, void* recv_x, float* recv_sf,
+                       bool few_destinations) {
     if (p.row_bytes <= 0 || p.row_bytes > INT32_MAX) return DISPATCH_ERR_ARG;
     if (p.row_bytes % 16 != 0) return DISPATCH_ERR_ALIGN;
     if (layout == nullptr || !layout->status || !layout->expert_count || !layout->expert_psum)
@@ -84,6 +85,9 @@ int check_scatter_args(const dispatch_problem_t& p, const dispatch_layout_t* lay
                            layout->expert_count, layout->expert_psum, layout->status};
     for (const void* q : words)
         if (q && !aligned_to(q, 4)) return DISPATCH_ERR_ALIGN;
+    if (layout->row_order && !aligned_to(layout->row_order, 8)) return DISPATCH_ERR_ALIGN;
+    // A grid beyond one launch is refused here, before any kernel of the call.
+    if (!moe_dispatch::scatter_grid_fits(p, *layout, few_destinations)) return DISPATCH_ERR_ARG;
     return DISPATCH_OK;
 }
 
@@ -94,7 +98,7 @@ int scatter_checked(const dispatch_problem_t* problem, const dispatch_layout_t* 
                     hipStream_t stream, bool few_destinations) {
     int rc = check_problem(problem);
     if (rc != DISPATCH_OK) return rc;
-    rc = check_scatter_args(*problem, layout, x, x_sf, rank_x, rank_sf, recv_x, recv_sf);
+    rc = check_scatter_args(*problem, layout, x, x_sf, rank_x, rank_sf, recv_x, recv_sf, few_destinations);
     if (rc != DISPATCH_OK) return rc;
     if (moe_dispatch::launch_scatter(*problem, *layout, x, x_sf, rank_x, rank_sf, recv_x, recv_sf, stream,
                                      few_destinations) != hipSuccess)
@@ -130,6 +134,7 @@ int check_layout_args(const dispatch_problem_t* problem, const void* topk_idx, c
                           out->rank_src_token_idx, out->status, out->expert_count_cumulative};
     for (const void* q : ints)
         if (q && !aligned_to(q, 4)) return DISPATCH_ERR_ALIGN;
+    if (out->row_order && !aligned_to(out->row_order, 8)) return DISPATCH_ERR_ALIGN;
     if (!aligned_to(workspace, 256)) return DISPATCH_ERR_WORKSPACE;
 
     *g = moe_dispatch::make_geometry(p.num_tokens, p.num_topk, p.num_experts, p.num_ranks);
@@ -147,7 +152,8 @@ int check_expand_layout_args(const dispatch_expand_problem_t* problem, const voi
     int rc = check_expand(problem, p);
     if (rc != DISPATCH_OK) return rc;
     if (out == nullptr || !out->expert_count || !out->expert_psum || !out->status) return DISPATCH_ERR_NULL;
-    if (out->rank_count || out->rank_psum || out->rank_slot || out->rank_src_token_idx) return DISPATCH_ERR_ARG;
+    if (out->rank_count || out->rank_psum || out->rank_slot || out->rank_src_token_idx || out->row_order)
+        return DISPATCH_ERR_ARG;
     if (p->num_tokens > 0 && (!recv_topk_idx || !out->expert_slot)) return DISPATCH_ERR_NULL;
     if (!recv_count) return DISPATCH_ERR_NULL;
     if (p->recv_capacity_rows > 0 && !out->recv_src_token_idx) return DISPATCH_ERR_NULL;
@@ -206,6 +212,14 @@ int dispatch_max_rows(const dispatch_problem_t* problem, int64_t* max_recv_rows,
     return DISPATCH_OK;
 }
 
+int dispatch_row_order_size(const dispatch_problem_t* problem, int64_t* ints) {
+    const int rc = check_problem(problem);
+    if (rc != DISPATCH_OK) return rc;
+    if (ints == nullptr) return DISPATCH_ERR_NULL;
+    *ints = moe_dispatch::row_order_ints(*problem);
+    return DISPATCH_OK;
+}
+
 int dispatch_layout(const dispatch_problem_t* problem, const void* topk_idx, const dispatch_layout_t* out,
                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
     TileGeometry g;
@@ -254,7 +268,8 @@ int dispatch_layout_and_scatter(const dispatch_problem_t* problem, const void* t
     TileGeometry g;
     int rc = check_layout_args(problem, topk_idx, out, workspace, workspace_bytes, &g);
     if (rc != DISPATCH_OK) return rc;
-    rc = check_scatter_args(*problem, out, x, x_sf, rank_x, rank_sf, recv_x, recv_sf);
+    rc = check_scatter_args(*problem, out, x, x_sf, rank_x, rank_sf, recv_x, recv_sf,
+                            has_few_destinations(*problem));
     if (rc != DISPATCH_OK) return rc;
     const dispatch_problem_t& p = *problem;
     if (moe_dispatch::fused_shape(p, g).fits) {
@@ -325,7 +340,7 @@ int dispatch_expand_layout_and_scatter(const dispatch_expand_problem_t* problem,
     int rc = check_expand_layout_args(problem, recv_topk_idx, recv_count, out, workspace, workspace_bytes, &p, &g,
                                       &view);
     if (rc != DISPATCH_OK) return rc;
-    rc = check_scatter_args(p, out, recv_buf, recv_sf_buf, nullptr, nullptr, recv_x, recv_sf);
+    rc = check_scatter_args(p, out, recv_buf, recv_sf_buf, nullptr, nullptr, recv_x, recv_sf, true);
     if (rc != DISPATCH_OK) return rc;
     if (moe_dispatch::fused_shape(p, g, true).fits) {
         if (moe_dispatch::launch_fused_dispatch(p, g, recv_topk_idx, *out, workspace, recv_buf, recv_sf_buf, nullptr,

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_binding_constants_match_header():
     d = _defines()
-    assert d["DISPATCH_ABI_VERSION"] == M.dispatch_abi_version() == 3
+    assert d["DISPATCH_ABI_VERSION"] == M.dispatch_abi_version() == 4
     assert (d["DISPATCH_ERR_NULL"], d["DISPATCH_ERR_ARG"], d["DISPATCH_ERR_ALIGN"],
             d["DISPATCH_ERR_WORKSPACE"], d["DISPATCH_ERR_HIP"]) == (
         M.ERR_NULL, M.ERR_ARG, M.ERR_ALIGN, M.ERR_WORKSPACE, M.ERR_HIP)
@@ -47,7 +47,7 @@ def test_binding_constants_match_header():
         M.RANK_CONTIG, M.EXPERT_MAJOR, M.ZERO_PAD)
     assert d["DISPATCH_MAX_TOPK"] == M.MAX_TOPK and d["DISPATCH_MAX_EXPERTS"] == M.MAX_EXPERTS
     assert d["DISPATCH_MAX_RANKS"] == M.MAX_RANKS
-    assert ctypes.sizeof(M.Problem) == 64 and ctypes.sizeof(M.LayoutPtrs) == 10 * 8
+    assert ctypes.sizeof(M.Problem) == 64 and ctypes.sizeof(M.LayoutPtrs) == 11 * 8
 
 
 def test_strerror_covers_codes():
@@ -356,3 +356,22 @@ def test_noalloc_host_errors_before_launch():
     bad = M.make_problem(100, 8, 256, 8, 1, row_bytes=16)
     bad.num_topk = 0
     assert call(bad) == M.ERR_ARG
+
+
+def test_row_order_size_and_checks():
+    """The row order's length, its 8-byte alignment, and its refusal by the
+    receiver-side expand layout (host checks only, nothing launched)."""
+    lib = M.load_library()
+    p = M.make_problem(100, 8, 256, 8, 1, row_bytes=64)
+    assert M.dispatch_row_order_size(p) == 2 + 2 * (100 * 8 + 100 * 8)
+    p3 = M.make_problem(100, 8, 256, 4, 1, row_bytes=64)
+    assert M.dispatch_row_order_size(p3) == 2 + 2 * (100 * 8 + 100 * 4)
+    ws_need = M.dispatch_workspace_size(p)
+    lay = M.LayoutPtrs(*([4096] * 9), None, 4100)  # row order 4-byte but not 8-byte aligned
+    assert lib.dispatch_layout(ctypes.byref(p), 4096, ctypes.byref(lay), 4096, ws_need, None) == M.ERR_ALIGN
+    assert lib.dispatch_scatter(ctypes.byref(p), ctypes.byref(lay), 4096, None, 4096, None, 4096, None,
+                                None) == M.ERR_ALIGN
+    q = M.make_expand_problem(2, 16, 8, 256, 8, 0, row_bytes=64)
+    eq = M.LayoutPtrs(4096, None, 4096, None, 4096, None, 4096, None, 4096, None, 4096)
+    assert lib.dispatch_expand_layout(ctypes.byref(q), 4096, 4096, ctypes.byref(eq), 4096,
+                                      M.dispatch_expand_workspace_size(q), None) == M.ERR_ARG

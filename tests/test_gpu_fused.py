@@ -163,6 +163,8 @@ def test_plan_call_and_running_counts():
     xb = H.random_rows(9, t, 256)
     prob = M.make_problem(t, k, e, r, a, 8, 256, 0)
     lay, ws, rows = M.alloc_layout(prob, H.DEVICE), M.alloc_workspace(prob, H.DEVICE), M.alloc_rows(prob, H.DEVICE)
+    for _, t_ in lay.tensors():  # canary bands past the totals, as assert_layout_equal expects
+        t_.fill_(H.CANARY)
     cum = torch.zeros(e, dtype=torch.int32, device=H.DEVICE)
     plan = M.Plan(prob, torch.from_numpy(topk).to(H.DEVICE), lay, ws, torch.from_numpy(xb).to(H.DEVICE), None,
                   rows, expert_count_cumulative=cum)

@@ -53,15 +53,18 @@ def test_reduced_workload_full_parity(name, t):
 # The benchmark times the combined call (the layout kernels read the token
 # rows ahead for the scatter when they fit the Infinity Cache); the two
 # separate calls are checked as well.
-@pytest.mark.parametrize("combined", [True, False], ids=["one_call", "two_calls"])
+# The source-major scatter (a layout without a row order) as well.
+@pytest.mark.parametrize("combined,row_order", [(True, True), (False, True), (False, False)],
+                         ids=["one_call", "two_calls", "two_calls_source_major"])
 @pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
-def test_workload_full_size(name, combined):
+def test_workload_full_size(name, combined, row_order):
     w = W.get(name)
-    _banner(f"{w.describe()} combined={combined}")
+    _banner(f"{w.describe()} combined={combined} row_order={row_order}")
     inp = W.make_inputs(w)
     xb = inp.x_bytes()
     ref = oracle.layout(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment)
-    run = H.run_gpu(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment, xb, inp.x_sf, combined=combined)
+    run = H.run_gpu(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment, xb, inp.x_sf, combined=combined,
+                    row_order=row_order)
     H.assert_layout_equal(run, ref)
     if w.num_tokens * w.row_bytes <= 64 << 20:
         H.assert_rows_full(run, ref, xb, inp.x_sf)
