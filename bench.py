@@ -34,12 +34,17 @@ if ROOT not in sys.path:
 
 METRIC = "dispatch GB/s & % HBM peak, 4096 tok×7168 bf16, top-8 of 256 experts"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scatter_traffic.json")
 SCATTER_SOURCES = [os.path.join(ROOT, "moe_token_dispatch_amd", "csrc", f)
                    for f in ("dispatch_scatter.hip", "dispatch_device.hpp")]
 COMBINE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_traffic.json")
 EXPAND_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expand_scatter_traffic.json")
-COMBINE_SOURCES = [os.path.join(ROOT, "moe_token_dispatch_amd", "csrc", "dispatch_combine.hip")]
+COMBINE_SOURCES = [os.path.join(ROOT, "moe_token_dispatch_amd", "csrc", f)
+                   for f in ("dispatch_combine.hip", "dispatch_device.hpp")]
+
+
+def traffic_file(workload):
+    """Committed counter summary of the dispatch scatter on one workload."""
+    return os.path.join(ROOT, "profiles", f"scatter_traffic_{workload}.json")
 
 
 def parse_args():
@@ -96,8 +101,9 @@ def source_digest(paths):
     return h.hexdigest()
 
 
-def load_traffic(path=TRAFFIC_FILE, sources=SCATTER_SOURCES, workload=None):
-    """HBM bytes per launch of a kernel from committed rocprofv3 counters, or
+def load_traffic(path, sources=SCATTER_SOURCES, workload=None):
+    """Bytes per launch of a kernel from committed rocprofv3 counters
+    (L2-to-fabric bytes: FETCH_SIZE + WRITE_SIZE scaled by a plain copy), or
     None when they are missing, were taken on another workload or on another
     version of the kernel's source."""
     try:
@@ -654,7 +660,10 @@ def main():
     total_b, layout_b, _ = algorithmic_bytes(t, k, w.num_experts, w.num_ranks, 8, w.row_bytes, s,
                                              t_live, p_rows, n_rank)
     sc_b = scatter_launch_bytes(t, k, w.num_experts, w.row_bytes, s, t_live, p_rows, n_rank)
-    roof_kernel, roof_b = "scatter_kernel", sc_b
+    # The layout keeps a row order where the scatter walks destinations
+    # (order_scatter_kernel); elsewhere its count is -1 (scatter_kernel).
+    ordered = lay.row_order is not None and int(lay.row_order[0].item()) >= 0
+    roof_kernel, roof_b = ("order_scatter_kernel" if ordered else "scatter_kernel"), sc_b
     if one_kernel:  # the one kernel moves the whole step's bytes
         roof_kernel, roof_b = "assign_kernel (one-kernel layout + scatter)", total_b
     step_mean_us = statistics.mean(step_us)
@@ -662,7 +671,7 @@ def main():
     value = total_b / (step_mean_us * 1e-6) / 1e9
     kernel_mean_us = statistics.mean(kernel_us)
     achieved = roof_b / (kernel_mean_us * 1e-6) / 1e9
-    traffic = None if one_kernel else load_traffic(workload=w.name)
+    traffic = None if one_kernel else load_traffic(traffic_file(w.name), workload=w.name)
 
     def quant(us):
         v = sorted(us)

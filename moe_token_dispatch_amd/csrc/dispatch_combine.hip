@@ -17,16 +17,13 @@
 // nontemporal; the output goes out with the sc1 policy (measured best for
 // this kernel among the store policies).
 #include "dispatch_common.hpp"
+#include "dispatch_device.hpp"
 
 namespace moe_dispatch {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kCombineWaves = 2;         // wavefronts per workgroup
 constexpr int kCombineBatch = 8;         // expert rows loaded before the multiply-adds
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
-constexpr int kOutPolicy = 16;            // sc1
 constexpr int64_t kMaxCombineBlocks = int64_t(1) << 16;  // larger grids loop
 
 struct CombineParams {
@@ -97,14 +94,13 @@ combine_kernel(const u32x4* __restrict__ y, const float* __restrict__ weights,
         }
         // One row per token; a vector past the row end falls outside the
         // row's buffer range and is dropped by the hardware.
-        const __amdgpu_buffer_rsrc_t dst =
-            __builtin_amdgcn_make_buffer_rsrc(out + t * nv, 0, (int)(nv * 16), kBufferWord3);
+        const RowStore<kSc1Policy> dst(out + t * nv, (int)(nv * 16));
         u32x4 o;
         o.x = to_bf16(acc[0]) | (to_bf16(acc[1]) << 16);
         o.y = to_bf16(acc[2]) | (to_bf16(acc[3]) << 16);
         o.z = to_bf16(acc[4]) | (to_bf16(acc[5]) << 16);
         o.w = to_bf16(acc[6]) | (to_bf16(acc[7]) << 16);
-        __builtin_amdgcn_raw_buffer_store_b128(o, dst, live ? (int)(i * 16) : (int)(nv * 16), 0, kOutPolicy);
+        dst.store(live ? i : nv, o);
     }
 }
 

@@ -375,3 +375,24 @@ def test_row_order_size_and_checks():
     eq = M.LayoutPtrs(4096, None, 4096, None, 4096, None, 4096, None, 4096, None, 4096)
     assert lib.dispatch_expand_layout(ctypes.byref(q), 4096, 4096, ctypes.byref(eq), 4096,
                                       M.dispatch_expand_workspace_size(q), None) == M.ERR_ARG
+
+
+def test_scatter_grid_beyond_one_launch_is_refused_before_any_launch():
+    """A scatter whose grid would exceed one launch (2^32 work-items: here 64
+    tokens of 2 GiB rows, 2^21 one-KB segments each) is refused with
+    DISPATCH_ERR_ARG by the scatter and by the combined call, which makes the
+    check before it enqueues the layout kernels."""
+    lib = M.load_library()
+    row = (1 << 31) - 16
+    p = M.make_problem(64, 1, 8, 2, 1, 8, row, 0, 64, 64, M.ALL_OUTPUTS)
+    good = M.LayoutPtrs(*([4096] * 9))
+    assert lib.dispatch_scatter(ctypes.byref(p), ctypes.byref(good), 4096, None, 4096, None, 4096, None,
+                                None) == M.ERR_ARG
+    assert lib.dispatch_layout_and_scatter(ctypes.byref(p), 4096, ctypes.byref(good), 4096,
+                                           M.dispatch_workspace_size(p), 4096, None, 4096, None, 4096, None,
+                                           None) == M.ERR_ARG
+    # Half the tokens fit one launch: the checks pass (nothing is launched
+    # here, the NULL status pointer stops the call first).
+    p.num_tokens = 16
+    assert lib.dispatch_scatter(ctypes.byref(p), ctypes.byref(M.LayoutPtrs(*([4096] * 8), None)), 4096, None,
+                                4096, None, 4096, None, None) == M.ERR_NULL
