@@ -269,21 +269,37 @@ def expand_bench(args):
     recv_x = torch.empty((max(q.recv_capacity_rows, 1), rb), dtype=torch.uint8, device=dev)
     out_sf = torch.empty((max(q.recv_capacity_rows, 1), s_f), dtype=torch.float32, device=dev) if s_f else None
     stream = torch.cuda.current_stream(dev)
+    # A prepared plan: one C call per step (the layout and scatter kernels, or
+    # one kernel for a small receive buffer).
+    plan = M.ExpandPlan(q, recv_topk, counts, elay, ews, recv_buf, recv_sf, recv_x, out_sf, stream)
+    scratch = torch.empty(64 << 20, dtype=torch.int64, device=dev)
+    sink = torch.empty((), dtype=torch.int64, device=dev)
 
-    def step():
-        M.dispatch_expand_layout(q, recv_topk, counts, elay, ews, stream)
-        M.dispatch_expand_scatter(q, elay, recv_buf, recv_sf, recv_x, out_sf, stream)
+    def evict(i):  # as in the dispatch bench: 512 MiB written, then read back
+        scratch.fill_(i)
+        torch.sum(scratch, dim=0, out=sink)
 
     for _ in range(args.warmup):
-        step()
+        plan()
     torch.cuda.synchronize()
     if int(elay.status.item()) != 0:
         raise RuntimeError(f"expand status {int(elay.status.item())}")
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / args.steps
+    for i, (e0, e1) in enumerate(marks):
+        evict(i)
+        e0.record(stream)
+        plan()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    dt = statistics.mean(a.elapsed_time(b) for a, b in marks) / 1e3
+    warm_steps = max(args.steps, args.warm_steps)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(warm_steps):
+        plan()
+    torch.cuda.synchronize()
+    warm_s = (time.perf_counter() - w0) / warm_steps
     received = int(counts.sum().item())
     p_rows = int(elay.expert_psum[-1].item())
     local = e // r
@@ -294,15 +310,21 @@ def expand_bench(args):
     # stream: every received row read once, every expert-major row written
     # (pads as zeros), the slot map read.
     scatter_b = received * row + p_rows * row + 4 * s_count * m * k + 4 * (2 * local + 1)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n_sc = max(1, args.steps // 2)
+    # The row copy under the same flush: the layout call, then an event, then
+    # the scatter call, on at least 16 steps.
+    roof = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(max(16, args.steps))]
     torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(n_sc):
-        M.dispatch_expand_scatter(q, elay, recv_buf, recv_sf, recv_x, out_sf, stream)
-    ev1.record(stream)
+    for i, (e0, e1, e2) in enumerate(roof):
+        evict(i)
+        e0.record(stream)
+        plan.layout()
+        e1.record(stream)
+        plan.scatter()
+        e2.record(stream)
     torch.cuda.synchronize()
-    sc_s = ev0.elapsed_time(ev1) / 1e3 / n_sc
+    sc_s = statistics.mean(b.elapsed_time(c) for _, b, c in roof) / 1e3
+    lay_s = statistics.mean(a.elapsed_time(b) for a, b, _ in roof) / 1e3
+    del scratch, sink
     out = {
         "metric": "receiver-side expand GB/s & % HBM peak",
         "value": round(total_b / dt / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -311,14 +333,21 @@ def expand_bench(args):
         "config": {"workload": f"expand of {s_count} x {base.name} into rank {rank}", "sources": s_count,
                    "rows_per_source": m, "received_rows": received, "expert_major_rows": p_rows,
                    "local_experts": local, "expert_alignment": base.alignment},
+        "timing": ("mean of HIP-event step times (one prepared call each); before each step, outside its "
+                   "events, 512 MiB are written and read back"),
         "hbm_frac": round(total_b / dt / 1e9 / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": total_b,
+        "layout_events_us_mean": round(lay_s * 1e6, 2),
+        "warm_back_to_back": {"steps": warm_steps, "us_per_step": round(warm_s * 1e6, 2),
+                              "value": round(total_b / warm_s / 1e9, 1),
+                              "hbm_frac": round(total_b / warm_s / 1e9 / HBM_PEAK_GBPS, 4)},
         "roofline": {
             "kernel": "scatter_kernel (expand)", "bound": "hbm",
             "achieved": round(scatter_b / sc_s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(scatter_b / sc_s / 1e9 / HBM_PEAK_GBPS, 4),
             "traffic": load_traffic(EXPAND_TRAFFIC_FILE, SCATTER_SOURCES, base.name),
             "algorithmic_bytes_per_launch": scatter_b, "launch_us_mean": round(sc_s * 1e6, 2),
+            "event_samples": len(roof),
         },
     }
     print(json.dumps(out), flush=True)
