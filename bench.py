@@ -660,7 +660,8 @@ def main():
 
     # The dominant kernel on its own, under the same flush: the same two
     # parts the combined call enqueues (the read-ahead layout, then the
-    # scatter), with an event between them, on at least 16 steps.
+    # scatter with the read-ahead hint, which the library ignores for rows it
+    # does not read ahead), with an event between them, on at least 16 steps.
     n_roof = max(16, args.steps)
     roof = [(ev(), ev(), ev()) for _ in range(n_roof)]
     torch.cuda.synchronize()
@@ -672,7 +673,7 @@ def main():
         else:
             plan.layout_read_ahead()
             e1.record(stream)
-            plan.scatter()
+            plan.scatter(read_ahead=True)
         e2.record(stream)
     torch.cuda.synchronize()
     if one_kernel:
@@ -689,10 +690,7 @@ def main():
     total_b, layout_b, _ = algorithmic_bytes(t, k, w.num_experts, w.num_ranks, 8, w.row_bytes, s,
                                              t_live, p_rows, n_rank)
     sc_b = scatter_launch_bytes(t, k, w.num_experts, w.row_bytes, s, t_live, p_rows, n_rank)
-    # The layout keeps a row order where the scatter walks destinations
-    # (order_scatter_kernel); elsewhere its count is -1 (scatter_kernel).
-    ordered = lay.row_order is not None and int(lay.row_order[0].item()) >= 0
-    roof_kernel, roof_b = ("order_scatter_kernel" if ordered else "scatter_kernel"), sc_b
+    roof_kernel, roof_b = "split_scatter_kernel", sc_b
     if one_kernel:  # the one kernel moves the whole step's bytes
         roof_kernel, roof_b = "assign_kernel (one-kernel layout + scatter)", total_b
     step_mean_us = statistics.mean(step_us)

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define DISPATCH_ABI_VERSION 4
+#define DISPATCH_ABI_VERSION 5
 
 /* Limits. K <= 32 follows the page's bound on the top-k width (section 4.2);
  * R <= 1024 follows its kNumMaxRanks (section 6.2). */
@@ -78,6 +78,14 @@ extern "C" {
 #define DISPATCH_EXPERT_MAJOR 2u /* write recv_x (and recv_sf) */
 #define DISPATCH_ZERO_PAD 4u     /* zero the alignment pad rows of recv_x / recv_sf */
 #define DISPATCH_ALL_OUTPUTS (DISPATCH_RANK_CONTIG | DISPATCH_EXPERT_MAJOR | DISPATCH_ZERO_PAD)
+/* A hint for dispatch_scatter, changing no result: the token rows were just
+ * read into the Infinity Cache (by dispatch_layout_read_ahead, on the same
+ * stream). The scatter then keeps fewer row stores in flight per CU, which on
+ * MI355X moves rows from the cache faster (and rows from HBM slower). It is
+ * ignored where dispatch_layout_read_ahead reads nothing (rows and scale
+ * factors above 160 MB) and by the layout calls; dispatch_layout_and_scatter
+ * sets it itself when it reads the rows ahead. */
+#define DISPATCH_ROWS_READ_AHEAD 8u
 
 typedef struct dispatch_problem {
     int64_t num_tokens;         /* T >= 0 */
@@ -90,7 +98,7 @@ typedef struct dispatch_problem {
     int64_t row_bytes;          /* bytes per token row (H * element size), multiple of 16, 16..2^31-16 */
     int64_t recv_capacity_rows; /* rows of recv_x / recv_sf / recv_src_token_idx */
     int64_t rank_capacity_rows; /* rows of rank_x / rank_sf / rank_src_token_idx */
-    uint32_t flags;             /* DISPATCH_* output selection, used by dispatch_scatter */
+    uint32_t flags;             /* DISPATCH_* output selection and DISPATCH_ROWS_READ_AHEAD, used by dispatch_scatter */
     uint32_t reserved;          /* must be 0 */
 } dispatch_problem_t;
 
@@ -113,24 +121,6 @@ typedef struct dispatch_layout {
      * it wraps modulo 2^32, so a caller that keeps it over more than 2^31 rows
      * per expert reads and clears it from time to time. */
     int32_t* expert_count_cumulative;
-    /* Optional (NULL = off), 8-byte aligned, dispatch_row_order_size() ints:
-     * the order in which dispatch_scatter writes the rows. Entry 0 is the
-     * number n of routed rows (valid pairs plus rank rows), entry 1 is 0,
-     * then n (dest, token) pairs: dest >= 0 is a recv_x row, dest < 0 the
-     * rank_x row -1 - dest. The rows of each layout tile (a run of
-     * consecutive tokens) come together, after those of the earlier tiles,
-     * grouped by expert then by rank, each group in slot order. With it,
-     * dispatch_scatter walks the destinations in this order: consecutive
-     * workgroups fill consecutive rows of a bucket, each reading its slice
-     * of the source row (an MI355X choice, not a step of the page's method).
-     * It is kept only where that measured faster than walking the sources:
-     * rows of 4 to 8 KB with several destinations each (K expert rows, or
-     * expert and rank rows), E + R <= 2048, and T * (row_bytes + 4 * S) <=
-     * 160 MB (rows the layout reads ahead into the Infinity Cache, see
-     * dispatch_layout_read_ahead). Otherwise entry 0 is set to -1 and the
-     * scatter walks the source rows. Written by dispatch_layout when the
-     * status is 0. */
-    int32_t* row_order;
 } dispatch_layout_t;
 
 /* Version of this ABI (DISPATCH_ABI_VERSION). */
@@ -152,10 +142,6 @@ int dispatch_workspace_size(const dispatch_problem_t* problem, size_t* bytes);
 int dispatch_max_rows(const dispatch_problem_t* problem, int64_t* max_recv_rows,
                       int64_t* max_rank_rows);
 
-/* Length in int32 of a layout's optional row_order array:
- * 2 + 2 * (T*K + T*min(K, R)). */
-int dispatch_row_order_size(const dispatch_problem_t* problem, int64_t* ints);
-
 /* Count -> Prefix Sum -> slot assignment (sections 4, 5, 6.2, 6.4 and 7).
  * topk_idx: device [T, K] row-major of problem->topk_idx_bytes wide signed
  * integers; a negative entry is masked. Writes every field of `out` (counts
@@ -173,7 +159,9 @@ int dispatch_layout(const dispatch_problem_t* problem, const void* topk_idx,
  * fourteen times as many bytes, and rows it finds in the cache no longer
  * interleave HBM reads into that write stream. Rows and scale factors of
  * more than 160 MB together are not read (they would push their own first
- * rows out of the 256 MB cache). Outputs, checks and errors are those of
+ * rows out of the 256 MB cache). The scatter that follows is told so by
+ * DISPATCH_ROWS_READ_AHEAD in its problem's flags. Outputs, checks and
+ * errors are those of
  * dispatch_layout, plus DISPATCH_ERR_ALIGN for a misaligned x or x_sf;
  * nothing beyond the layout outputs is written. (Not a step of the page's
  * method: a measure for MI355X's memory hierarchy.) */

@@ -13,7 +13,7 @@ from ._binding import (  # noqa: F401
     STATUS_RECV_OVERFLOW, SYMBOLS, ZERO_PAD, DispatchError, LayoutPtrs, LayoutTensors, Problem,
     RowBuffers, alloc_layout, alloc_rows, alloc_workspace, dispatch_abi_version, dispatch_layout,
     dispatch_max_rows, dispatch_scatter, dispatch_layout_and_scatter, dispatch_kernel_count,
-    dispatch_layout_read_ahead, dispatch_layout_and_scatter_noalloc, dispatch_row_order_size,
+    dispatch_layout_read_ahead, dispatch_layout_and_scatter_noalloc, ROWS_READ_AHEAD,
     dispatch_strerror, dispatch_workspace_size, load_library, make_problem, STATUS_BAD_COUNT, ExpandProblem, ExpandLayoutTensors, make_expand_problem,
     dispatch_expand_workspace_size, alloc_expand_layout, alloc_expand_workspace, dispatch_expand_layout,
     dispatch_expand_scatter, dispatch_expand_layout_and_scatter, ExpandPlan, CombineProblem, dispatch_combine,

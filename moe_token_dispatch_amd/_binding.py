@@ -17,7 +17,7 @@ import torch  # load torch's HIP runtime first so the library binds to the same 
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_dispatch.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 MAX_TOPK = 32
 MAX_EXPERTS = 4096
 MAX_RANKS = 1024
@@ -39,6 +39,7 @@ RANK_CONTIG = 1
 EXPERT_MAJOR = 2
 ZERO_PAD = 4
 ALL_OUTPUTS = RANK_CONTIG | EXPERT_MAJOR | ZERO_PAD
+ROWS_READ_AHEAD = 8  # scatter hint: the rows were just read ahead (changes no result)
 
 
 class DispatchError(RuntimeError):
@@ -71,7 +72,7 @@ class LayoutPtrs(ctypes.Structure):
 
     _fields_ = [(name, ctypes.c_void_p) for name in (
         "expert_count", "rank_count", "expert_psum", "rank_psum", "expert_slot", "rank_slot",
-        "recv_src_token_idx", "rank_src_token_idx", "status", "expert_count_cumulative", "row_order")]
+        "recv_src_token_idx", "rank_src_token_idx", "status", "expert_count_cumulative")]
 
 
 class ExpandProblem(ctypes.Structure):
@@ -109,7 +110,7 @@ _LIB = None
 
 # Exported symbols of include/moe_dispatch.h.
 SYMBOLS = ("dispatch_abi_version", "dispatch_strerror", "dispatch_workspace_size",
-           "dispatch_max_rows", "dispatch_row_order_size", "dispatch_layout", "dispatch_layout_read_ahead",
+           "dispatch_max_rows", "dispatch_layout", "dispatch_layout_read_ahead",
            "dispatch_scatter", "dispatch_layout_and_scatter", "dispatch_layout_and_scatter_noalloc",
            "dispatch_kernel_count",
            "dispatch_expand_workspace_size", "dispatch_expand_max_rows", "dispatch_expand_layout",
@@ -134,8 +135,6 @@ def load_library(path: str = LIB_PATH):
     lib.dispatch_max_rows.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_int64),
                                       ctypes.POINTER(ctypes.c_int64)]
     lib.dispatch_max_rows.restype = i
-    lib.dispatch_row_order_size.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_int64)]
-    lib.dispatch_row_order_size.restype = i
     lib.dispatch_layout.argtypes = [ctypes.POINTER(Problem), p, ctypes.POINTER(LayoutPtrs), p, sz, p]
     lib.dispatch_layout.restype = i
     lib.dispatch_layout_read_ahead.argtypes = [ctypes.POINTER(Problem), p, ctypes.POINTER(LayoutPtrs), p, sz, p, p,
@@ -189,15 +188,6 @@ def dispatch_workspace_size(problem: Problem) -> int:
     return int(out.value)
 
 
-def dispatch_row_order_size(problem: Problem) -> int:
-    """int32 entries of a layout's row_order: 2 + 2 * (T*K + T*min(K, R))."""
-    n = ctypes.c_int64(0)
-    rc = load_library().dispatch_row_order_size(ctypes.byref(problem), ctypes.byref(n))
-    if rc:
-        raise DispatchError(rc, "dispatch_row_order_size")
-    return int(n.value)
-
-
 def dispatch_max_rows(problem: Problem) -> Tuple[int, int]:
     recv, rank = ctypes.c_int64(0), ctypes.c_int64(0)
     rc = load_library().dispatch_max_rows(ctypes.byref(problem), ctypes.byref(recv), ctypes.byref(rank))
@@ -228,15 +218,12 @@ class LayoutTensors:
     recv_src_token_idx: torch.Tensor
     rank_src_token_idx: torch.Tensor
     status: torch.Tensor
-    # Optional [dispatch_row_order_size] int32: the order the scatter writes
-    # the rows in (rows of 4 KB or more); None = the source-major scatter.
-    row_order: Optional[torch.Tensor] = None
 
     def ptrs(self, expert_count_cumulative: Optional[torch.Tensor] = None) -> LayoutPtrs:
         return LayoutPtrs(*[t.data_ptr() for t in (
             self.expert_count, self.rank_count, self.expert_psum, self.rank_psum, self.expert_slot,
             self.rank_slot, self.recv_src_token_idx, self.rank_src_token_idx, self.status)],
-            _ptr(expert_count_cumulative), _ptr(self.row_order))
+            _ptr(expert_count_cumulative))
 
     def tensors(self):
         """(name, tensor) of every output present."""
@@ -279,8 +266,6 @@ def _check_dispatch_sizes(problem: Problem, topk_idx: Optional[torch.Tensor], la
                     ("recv_src_token_idx", problem.recv_capacity_rows),
                     ("rank_src_token_idx", problem.rank_capacity_rows), ("status", 1)):
         _need(getattr(layout, name), name, 4 * n)
-    if getattr(layout, "row_order", None) is not None:
-        _need(layout.row_order, "row_order", 4 * dispatch_row_order_size(problem))
 
 
 def _check_dispatch_rows(problem: Problem, x, x_sf, rank_x, rank_sf, recv_x, recv_sf) -> None:
@@ -468,12 +453,10 @@ def make_problem(num_tokens: int, num_topk: int, num_experts: int, num_ranks: in
     return p
 
 
-def alloc_layout(problem: Problem, device, row_order: bool = True) -> LayoutTensors:
-    """Layout outputs, with the row order unless ``row_order`` is False."""
+def alloc_layout(problem: Problem, device) -> LayoutTensors:
     i32 = dict(dtype=torch.int32, device=device)
     t, k = problem.num_tokens, problem.num_topk
     return LayoutTensors(
-        row_order=torch.empty(dispatch_row_order_size(problem), **i32) if row_order else None,
         expert_count=torch.empty(problem.num_experts, **i32),
         rank_count=torch.empty(problem.num_ranks, **i32),
         expert_psum=torch.empty(problem.num_experts + 1, **i32),
@@ -519,7 +502,8 @@ class Plan:
 
     ``layout()`` enqueues dispatch_layout, ``scatter()`` enqueues
     dispatch_scatter, ``__call__`` enqueues both as one
-    dispatch_layout_and_scatter call. The tensors must stay alive and keep
+    dispatch_layout_and_scatter call; ``layout_read_ahead()`` followed by
+    ``scatter(read_ahead=True)`` is that call's two halves. The tensors must stay alive and keep
     their storage while the plan is used.
     """
 
@@ -547,7 +531,7 @@ class Plan:
         handle = _stream_handle(stream, topk_idx.device)
         self._layout_args = (ctypes.byref(problem), _ptr(topk_idx), ctypes.byref(self._lay), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), handle)
-        self._scatter_args = self._both_args = self._layout_ra_args = None
+        self._scatter_args = self._scatter_ra_args = self._both_args = self._layout_ra_args = None
         if x is not None:
             _check_device_tensor(x, "x")
             rows = rows if rows is not None else RowBuffers(None, None, None, None)
@@ -561,6 +545,12 @@ class Plan:
             row_ptrs = (_ptr(x), _ptr(x_sf), _ptr(rows.rank_x), _ptr(rows.rank_sf), _ptr(rows.recv_x),
                         _ptr(rows.recv_sf))
             self._scatter_args = (ctypes.byref(problem), ctypes.byref(self._lay), *row_ptrs, handle)
+            # The same problem with the read-ahead hint, for the scatter that
+            # follows layout_read_ahead().
+            ra_problem = Problem.from_buffer_copy(problem)
+            ra_problem.flags |= ROWS_READ_AHEAD
+            self._keep += (ra_problem,)
+            self._scatter_ra_args = (ctypes.byref(ra_problem), *self._scatter_args[1:])
             self._both_args = (*self._layout_args[:-1], *row_ptrs, handle)
             self._layout_ra_args = (*self._layout_args[:-1], _ptr(x), _ptr(x_sf), handle)
 
@@ -578,10 +568,12 @@ class Plan:
         if rc:
             raise DispatchError(rc, "dispatch_layout_read_ahead")
 
-    def scatter(self) -> None:
+    def scatter(self, read_ahead: bool = False) -> None:
+        """dispatch_scatter; ``read_ahead``: right after layout_read_ahead()
+        (sets DISPATCH_ROWS_READ_AHEAD)."""
         if self._scatter_args is None:
             raise ValueError("this plan has no token batch to scatter")
-        rc = self._lib.dispatch_scatter(*self._scatter_args)
+        rc = self._lib.dispatch_scatter(*(self._scatter_ra_args if read_ahead else self._scatter_args))
         if rc:
             raise DispatchError(rc, "dispatch_scatter")
 
@@ -632,7 +624,7 @@ class ExpandLayoutTensors:
     def ptrs(self, expert_count_cumulative: Optional[torch.Tensor] = None) -> LayoutPtrs:
         return LayoutPtrs(self.expert_count.data_ptr(), None, self.expert_psum.data_ptr(), None,
                           self.expert_slot.data_ptr(), None, self.recv_src_row_idx.data_ptr(), None,
-                          self.status.data_ptr(), _ptr(expert_count_cumulative), None)
+                          self.status.data_ptr(), _ptr(expert_count_cumulative))
 
 
 def alloc_expand_layout(problem: ExpandProblem, device) -> ExpandLayoutTensors:

@@ -27,7 +27,8 @@ int check_problem(const dispatch_problem_t* p) {
     if (p->topk_idx_bytes != 4 && p->topk_idx_bytes != 8) return DISPATCH_ERR_ARG;
     if (p->sf_per_token < 0) return DISPATCH_ERR_ARG;
     if (p->recv_capacity_rows < 0 || p->rank_capacity_rows < 0) return DISPATCH_ERR_ARG;
-    if ((p->flags & ~uint32_t(DISPATCH_ALL_OUTPUTS)) != 0 || p->reserved != 0) return DISPATCH_ERR_ARG;
+    if ((p->flags & ~uint32_t(DISPATCH_ALL_OUTPUTS | DISPATCH_ROWS_READ_AHEAD)) != 0 || p->reserved != 0)
+        return DISPATCH_ERR_ARG;
     // Slots and row counts are int32: the worst case must fit (T is bounded
     // first, so the product below cannot overflow).
     if (p->num_tokens > INT32_MAX) return DISPATCH_ERR_ARG;
@@ -85,9 +86,8 @@ int check_scatter_args(const dispatch_problem_t& p, const dispatch_layout_t* lay
                            layout->expert_count, layout->expert_psum, layout->status};
     for (const void* q : words)
         if (q && !aligned_to(q, 4)) return DISPATCH_ERR_ALIGN;
-    if (layout->row_order && !aligned_to(layout->row_order, 8)) return DISPATCH_ERR_ALIGN;
     // A grid beyond one launch is refused here, before any kernel of the call.
-    if (!moe_dispatch::scatter_grid_fits(p, *layout, few_destinations)) return DISPATCH_ERR_ARG;
+    if (!moe_dispatch::scatter_grid_fits(p, few_destinations)) return DISPATCH_ERR_ARG;
     return DISPATCH_OK;
 }
 
@@ -134,7 +134,6 @@ int check_layout_args(const dispatch_problem_t* problem, const void* topk_idx, c
                           out->rank_src_token_idx, out->status, out->expert_count_cumulative};
     for (const void* q : ints)
         if (q && !aligned_to(q, 4)) return DISPATCH_ERR_ALIGN;
-    if (out->row_order && !aligned_to(out->row_order, 8)) return DISPATCH_ERR_ALIGN;
     if (!aligned_to(workspace, 256)) return DISPATCH_ERR_WORKSPACE;
 
     *g = moe_dispatch::make_geometry(p.num_tokens, p.num_topk, p.num_experts, p.num_ranks);
@@ -152,8 +151,7 @@ int check_expand_layout_args(const dispatch_expand_problem_t* problem, const voi
     int rc = check_expand(problem, p);
     if (rc != DISPATCH_OK) return rc;
     if (out == nullptr || !out->expert_count || !out->expert_psum || !out->status) return DISPATCH_ERR_NULL;
-    if (out->rank_count || out->rank_psum || out->rank_slot || out->rank_src_token_idx || out->row_order)
-        return DISPATCH_ERR_ARG;
+    if (out->rank_count || out->rank_psum || out->rank_slot || out->rank_src_token_idx) return DISPATCH_ERR_ARG;
     if (p->num_tokens > 0 && (!recv_topk_idx || !out->expert_slot)) return DISPATCH_ERR_NULL;
     if (!recv_count) return DISPATCH_ERR_NULL;
     if (p->recv_capacity_rows > 0 && !out->recv_src_token_idx) return DISPATCH_ERR_NULL;
@@ -209,14 +207,6 @@ int dispatch_max_rows(const dispatch_problem_t* problem, int64_t* max_recv_rows,
         *max_recv_rows = problem->num_tokens * problem->num_topk +
                          int64_t(problem->num_experts) * (problem->expert_alignment - 1);
     if (max_rank_rows) *max_rank_rows = problem->num_tokens * k_or_r;
-    return DISPATCH_OK;
-}
-
-int dispatch_row_order_size(const dispatch_problem_t* problem, int64_t* ints) {
-    const int rc = check_problem(problem);
-    if (rc != DISPATCH_OK) return rc;
-    if (ints == nullptr) return DISPATCH_ERR_NULL;
-    *ints = moe_dispatch::row_order_ints(*problem);
     return DISPATCH_OK;
 }
 
@@ -279,12 +269,15 @@ int dispatch_layout_and_scatter(const dispatch_problem_t* problem, const void* t
         return DISPATCH_OK;
     }
     // The layout kernels read the token rows ahead for the scatter when the
-    // batch fits the Infinity Cache.
+    // batch fits the Infinity Cache, and the scatter then runs as after
+    // dispatch_layout_read_ahead.
     moe_dispatch::ReadAhead ra{x, p.num_tokens * p.row_bytes, x_sf, p.num_tokens * p.sf_per_token};
     const bool read_ahead = moe_dispatch::read_ahead_fits(ra.x_bytes, ra.sf_words);
+    dispatch_problem_t sp = p;
+    if (read_ahead) sp.flags |= DISPATCH_ROWS_READ_AHEAD;
     if (moe_dispatch::launch_layout(p, g, topk_idx, *out, workspace, stream, nullptr,
                                     read_ahead ? &ra : nullptr) != hipSuccess ||
-        moe_dispatch::launch_scatter(p, *out, x, x_sf, rank_x, rank_sf, recv_x, recv_sf, stream,
+        moe_dispatch::launch_scatter(sp, *out, x, x_sf, rank_x, rank_sf, recv_x, recv_sf, stream,
                                      has_few_destinations(p)) != hipSuccess)
         return DISPATCH_ERR_HIP;
     return DISPATCH_OK;

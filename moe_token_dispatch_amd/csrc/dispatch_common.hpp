@@ -27,10 +27,15 @@ constexpr int kFewTileWaves = 16;     // wavefronts per tile on the two-launch p
 constexpr int kMidTileWaves = 8;      // wavefronts per tile on the two-launch path when the histograms fit
 constexpr int kManyTileWaves = 4;     // wavefronts per tile on the column-scan path
 constexpr int kLdsBudgetInts = 40000; // LDS ints per workgroup for key arrays (gfx950: 160 KiB per CU)
-// Key rows of the assign kernel besides its wavefront counters: totals and
-// first slots, and with a row order (up to kOrderMaxKeys keys) its offsets.
-constexpr int kOrderMaxKeys = 2048;
-inline int assign_key_rows(int num_keys) { return num_keys <= kOrderMaxKeys ? 3 : 2; }
+constexpr int kLdsPerCu = 160 * 1024;  // gfx950
+// Dynamic LDS per workgroup that lets at most n workgroups of a launch share
+// a CU (a kernel that needs no LDS reserves it only to bound its occupancy):
+// midway between the sizes at which n and n + 1 workgroups just fit, so that
+// the hardware's allocation granularity cannot change the count.
+inline int lds_for_workgroups_per_cu(int n) {
+    if (n < 1) n = 1;
+    return (kLdsPerCu / n + kLdsPerCu / (n + 1)) / 2;
+}
 
 struct TileGeometry {
     int64_t num_tokens;
@@ -61,9 +66,9 @@ inline TileGeometry make_geometry(int64_t num_tokens, int32_t num_topk, int32_t 
     g.num_topk = num_topk;
     g.tokens_per_chunk = kWave / num_topk;
     g.num_keys = num_experts + num_ranks;
-    // The assign kernel holds W wavefront counter rows plus
-    // assign_key_rows() more rows of num_keys ints in LDS.
-    const int w_lds = kLdsBudgetInts / g.num_keys - assign_key_rows(g.num_keys);
+    // The assign kernel holds W wavefront counter rows plus two more rows of
+    // num_keys ints in LDS.
+    const int w_lds = kLdsBudgetInts / g.num_keys - 2;
     auto clamp_w = [&](int cap) { return w_lds < 1 ? 1 : (w_lds > cap ? cap : w_lds); };
     // Histogram rows are padded to whole 16-byte vectors.
     g.hist_stride = (g.num_keys + 3) / 4 * 4;
@@ -133,14 +138,6 @@ inline TileGeometry make_geometry(int64_t num_tokens, int32_t num_topk, int32_t 
 // totals[num_keys] and tile_err[num_tiles], int32, each 256-byte aligned.
 inline size_t workspace_bytes(const TileGeometry& g) { return g.ws_bytes; }
 
-// Length in int32 of a layout's row_order array: a 2-int header, then one
-// (dest, token) pair per routed row, at most T*K expert rows and
-// T*min(K, R) rank rows.
-inline int64_t row_order_ints(const dispatch_problem_t& p) {
-    const int64_t k_or_r = p.num_topk < p.num_ranks ? p.num_topk : p.num_ranks;
-    return 2 + 2 * (p.num_tokens * p.num_topk + p.num_tokens * k_or_r);
-}
-
 // How the receiver-side expand sees its receive buffer through the layout
 // kernels (see dispatch_expand_layout).
 struct ExpandView {
@@ -169,25 +166,6 @@ inline bool read_ahead_fits(int64_t x_bytes, int64_t sf_words) {
     return x_bytes + 4 * sf_words <= kReadAheadMaxBytes;
 }
 
-// Whether a layout keeps its row order (when one is asked for) and the
-// scatter walks it: rows of 4 to 8 KB with several destinations each, at
-// most kOrderMaxKeys keys, and rows (with scale factors) that the layout
-// reads ahead into the Infinity Cache. Measured on MI355X against the
-// source-major scatter, flushed steps: 7 KB fp8 rows 115.3 against 120.4 us,
-// 8 KB bf16 rows (16384 tokens) 378.5 against 384.0 us; 14 KB bf16 rows tie
-// (161.0 against 160.6 us at best), and rows that do not fit the cache lose
-// (1477 against 1219 us at 65536 fp8 tokens), as every destination re-reads
-// its source row.
-constexpr int64_t kOrderMinRowBytes = 4096;
-constexpr int64_t kOrderMaxRowBytes = 8192;
-inline bool keeps_row_order(const dispatch_problem_t& p) {
-    const int destinations = ((p.flags & DISPATCH_EXPERT_MAJOR) ? p.num_topk : 0) +
-                             ((p.flags & DISPATCH_RANK_CONTIG) ? 1 : 0);
-    return destinations > 1 && p.row_bytes >= kOrderMinRowBytes && p.row_bytes <= kOrderMaxRowBytes &&
-           p.num_experts + p.num_ranks <= kOrderMaxKeys &&
-           p.num_tokens * (p.row_bytes + 4 * (int64_t)p.sf_per_token) <= kReadAheadMaxBytes;
-}
-
 // Launchers (defined in the .hip files). They return the HIP error of the launch.
 hipError_t launch_layout(const dispatch_problem_t& p, const TileGeometry& g, const void* topk_idx,
                          const dispatch_layout_t& out, void* workspace, hipStream_t stream,
@@ -195,7 +173,7 @@ hipError_t launch_layout(const dispatch_problem_t& p, const TileGeometry& g, con
 // few_destinations: rows go to about one destination each (sets the segment width).
 // Whether the scatter's grid fits one launch (at most 2^31 - 1 workgroups and
 // 2^32 - 1 work-items); checked before anything of a call is enqueued.
-bool scatter_grid_fits(const dispatch_problem_t& p, const dispatch_layout_t& lay, bool few_destinations);
+bool scatter_grid_fits(const dispatch_problem_t& p, bool few_destinations);
 hipError_t launch_scatter(const dispatch_problem_t& p, const dispatch_layout_t& lay, const void* x,
                           const float* x_sf, void* rank_x, float* rank_sf, void* recv_x,
                           float* recv_sf, hipStream_t stream, bool few_destinations);

@@ -77,7 +77,6 @@ struct LayoutParams {
     int64_t pf_rows_lo, pf_rows_hi;
     int64_t pf_sf_lo, pf_sf_hi;
     int32_t pf_groups;
-    int32_t keep_order;  // the layout's row_order is asked for and kept (keeps_row_order)
 };
 
 // Where one lane's pair lands inside its wavefront's chunks.
@@ -236,64 +235,6 @@ __device__ int2 block_exclusive_scan2(const int* __restrict__ in, int* __restric
         }
     }
     const int2 totals = make_int2(scratch[2 * nwaves], scratch[2 * nwaves + 1]);
-    __syncthreads();
-    return totals;
-}
-
-// Exclusive scan of io[0, n) in place by the whole workgroup, with the sums
-// of a[0, n) (a may be NULL: zeros) and b[0, n) taken on the side. Returns
-// (total of io, sum of a, sum of b). `scratch` holds 3 * (wavefronts + 1)
-// ints.
-__device__ int3 block_scan_sum(int* __restrict__ io, const int* __restrict__ a, const int* __restrict__ b, int n,
-                               int* __restrict__ scratch) {
-    const int tid = threadIdx.x, nthreads = blockDim.x;
-    const int lane = tid & (kWave - 1), wave = tid / kWave, nwaves = nthreads / kWave;
-    const int per = (n + nthreads - 1) / nthreads;
-    const int lo = min(n, tid * per), hi = min(n, lo + per);
-    int ls = 0, la = 0, lb = 0;
-    for (int i = lo; i < hi; ++i) {
-        ls += io[i];
-        la += a != nullptr ? a[i] : 0;
-        lb += b[i];
-    }
-    int is = ls;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int u = __shfl_up(is, off, kWave);
-        if (lane >= off) is += u;
-    }
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-        la += __shfl_xor(la, off, kWave);
-        lb += __shfl_xor(lb, off, kWave);
-    }
-    if (lane == kWave - 1) {
-        scratch[3 * wave] = is;
-        scratch[3 * wave + 1] = la;
-        scratch[3 * wave + 2] = lb;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int rs = 0, ra = 0, rb = 0;
-        for (int w = 0; w < nwaves; ++w) {
-            const int ts = scratch[3 * w];
-            scratch[3 * w] = rs;
-            rs += ts;
-            ra += scratch[3 * w + 1];
-            rb += scratch[3 * w + 2];
-        }
-        scratch[3 * nwaves] = rs;
-        scratch[3 * nwaves + 1] = ra;
-        scratch[3 * nwaves + 2] = rb;
-    }
-    __syncthreads();
-    int run = scratch[3 * wave] + is - ls;
-    for (int i = lo; i < hi; ++i) {
-        const int c = io[i];
-        io[i] = run;
-        run += c;
-    }
-    const int3 totals = make_int3(scratch[3 * nwaves], scratch[3 * nwaves + 1], scratch[3 * nwaves + 2]);
     __syncthreads();
     return totals;
 }
@@ -483,10 +424,9 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
         read_ahead(p, blockIdx.x - p.num_tiles);
         return;
     }
-    // LDS: [W][num_keys] wavefront counters, then totals[num_keys],
-    // first[num_keys] and off[num_keys].
+    // LDS: [W][num_keys] wavefront counters, then totals[num_keys] and first[num_keys].
     extern __shared__ int lds[];
-    __shared__ int scratch[3 * (kLayoutThreads / kWave + 1)];
+    __shared__ int scratch[2 * (kLayoutThreads / kWave + 1)];
     __shared__ uint32_t block_err;
     __shared__ int dest_expert[FUSED ? kFusedMaxPairs : 1], dest_rank[FUSED ? kFusedMaxPairs : 1];
 
@@ -512,10 +452,6 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
     int* counters = lds + wave * nkeys;
     int* totals = lds + nwaves * nkeys;  // per key, over all tiles
     int* first = totals + nkeys;         // per key, first slot (exclusive psum)
-    int* off = first + nkeys;            // per key, row-order position minus the key's running count
-    // The row order is kept where the scatter walks it (keeps_row_order: the
-    // launcher's keep_order); otherwise its entry count is set to -1.
-    const bool order = p.keep_order != 0;
     // The routing entries and the tiles' error words do not depend on the
     // histograms: their loads go out first, so the three latencies overlap.
     const int token_in_chunk = lane / K;
@@ -595,29 +531,15 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
     // tile has no earlier tiles, and its totals are its counters' sums.
     __syncthreads();
     for (int j = tid; j < nkeys; j += nthreads) {
-        const int start = MODE == kSingleTile ? 0 : first[j];
-        int run = start;
+        int run = MODE == kSingleTile ? 0 : first[j];
         for (int w = 0; w < nwaves; ++w) {
             const int c = lds[w * nkeys + j];
             lds[w * nkeys + j] = run;
             run += c;
         }
         if (MODE == kSingleTile) totals[j] = run;
-        if (order) off[j] = run - start;  // this tile's pairs of key j
     }
-    __syncthreads();
-    // The row order (when asked for): the tile's rows follow those of the
-    // earlier tiles, grouped by key in key order, each key's rows in slot
-    // order. A pair's position is its key's running count (the wavefront
-    // counter plus its rank in the chunk, as for its slot) plus off[key] =
-    // the tile's rows of lower keys + all rows of earlier tiles - the key's
-    // pairs in earlier tiles (which the running count includes).
-    int order_rows = 0;
-    if (order) {
-        const int3 sums = block_scan_sum(off, MODE == kSingleTile ? nullptr : first, totals, nkeys, scratch);
-        order_rows = sums.z;
-        for (int j = tid; j < nkeys; j += nthreads) off[j] += sums.y - (MODE == kSingleTile ? 0 : first[j]);
-    }
+    if (MODE == kSingleTile) __syncthreads();
     const int2 row_totals = block_exclusive_scan2(totals, first, E, nkeys, p.alignment, scratch);
     const int recv_rows = row_totals.x, rank_rows = row_totals.y;
     uint32_t status = block_err;
@@ -642,7 +564,6 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
             out.expert_psum[E] = recv_rows;
             if (out.rank_psum) out.rank_psum[R] = rank_rows;
             *out.status = (int32_t)status;
-            if (out.row_order) *reinterpret_cast<int2*>(out.row_order) = make_int2(order ? order_rows : -1, 0);
         }
     }
     if (status != 0) return;  // the layout is unspecified: write nothing more
@@ -674,12 +595,6 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
         if (out.rank_slot) {
             out.rank_slot[tok * K + k] = rs;
             if (rs >= 0 && rs < p.rank_capacity) out.rank_src_token_idx[rs] = (int32_t)tok;
-        }
-        if (order) {  // (destination, token); rank rows as -1 - row
-            int2* entries = reinterpret_cast<int2*>(out.row_order) + 1;
-            if (e >= 0) entries[counters[e] + pos[c].expert_pos + off[e]] = make_int2(es, (int32_t)tok);
-            if (r >= 0)
-                entries[counters[E + r] + pos[c].rank_pos + off[E + r]] = make_int2(-1 - rs, (int32_t)tok);
         }
     }
 
@@ -812,7 +727,7 @@ hipError_t launch_typed(const LayoutParams& p, const TileGeometry& g, const void
     Workspace wc = ws;
     dispatch_layout_t oc = out;
     RowArgs rc{};  // no rows: the layout alone
-    const size_t assign_lds = (size_t)(g.waves_per_tile + assign_key_rows(g.num_keys)) * g.num_keys * sizeof(int);
+    const size_t assign_lds = (size_t)(g.waves_per_tile + 2) * g.num_keys * sizeof(int);
     void* assign_args[] = {&idx, &pc, &wc, &oc, &rc};
     if (g.num_tiles == 1 && !g.column_scan)
         return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, kSingleTile, EXPAND, IdxT>), grid,
@@ -877,7 +792,7 @@ hipError_t launch_fused_typed(const LayoutParams& p, const TileGeometry& g, cons
     RowArgs rc = rows;
     // f.waves may exceed the tile's wavefronts: the extra ones rank empty
     // chunks (no change to any count) and add their threads to the copies.
-    const size_t lds = (size_t)(f.waves + assign_key_rows(g.num_keys)) * g.num_keys * sizeof(int);
+    const size_t lds = (size_t)(f.waves + 2) * g.num_keys * sizeof(int);
     void* args[] = {&idx, &pc, &wc, &oc, &rc};
     return hipLaunchKernel(reinterpret_cast<const void*>(&assign_kernel<CH, kSingleTile, EXPAND, IdxT, true>),
                            dim3((unsigned)f.groups), dim3(f.waves * kWave), args, lds, stream);
@@ -904,13 +819,6 @@ LayoutParams make_params(const dispatch_problem_t& prob, const TileGeometry& g) 
     return p;
 }
 
-// The row order is kept when asked for (row_order non-NULL) and the scatter
-// walks it; its offsets need an LDS row, which geometries of more than
-// kOrderMaxKeys keys do not have.
-void set_keep_order(LayoutParams& p, const dispatch_problem_t& prob, const dispatch_layout_t& out) {
-    p.keep_order = out.row_order != nullptr && keeps_row_order(prob) && p.num_keys <= kOrderMaxKeys;
-}
-
 Workspace make_workspace(const TileGeometry& g, void* workspace) {
     char* base = static_cast<char*>(workspace);
     Workspace ws;
@@ -927,7 +835,6 @@ hipError_t launch_layout(const dispatch_problem_t& prob, const TileGeometry& g, 
                          const dispatch_layout_t& out, void* workspace, hipStream_t stream,
                          const ExpandView* expand, const ReadAhead* ra) {
     LayoutParams p = make_params(prob, g);
-    if (expand == nullptr) set_keep_order(p, prob, out);
     const Workspace ws = make_workspace(g, workspace);
     if (expand != nullptr) {
         p.recv_count = expand->recv_count;
@@ -982,7 +889,6 @@ hipError_t launch_fused_dispatch(const dispatch_problem_t& prob, const TileGeome
     tile.num_tiles = 1;
     tile.column_scan = false;
     LayoutParams p = make_params(prob, tile);
-    if (expand == nullptr) set_keep_order(p, prob, out);
     if (expand != nullptr) {
         p.recv_count = expand->recv_count;
         p.rows_per_source = expand->rows_per_source;

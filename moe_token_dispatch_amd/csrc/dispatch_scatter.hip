@@ -4,21 +4,30 @@
 // This is the data move of the method ("DeepEP Counting Sort / Bucketization"
 // page): the rank-level copy of sections 6.2-6.3, the expert-major copy of the
 // expand mode (sections 6.4 and 8.2) and the zero padding of section 7.3. It
-// moves nearly all of the bytes, so it is built for HBM bandwidth: a token
-// row is cut into segments of 64 x V 16-byte vectors, and one wavefront per
-// (token, segment) reads its segment once, 16 bytes per lane per instruction,
-// holds it in registers and writes it to every destination row of that token
-// (the read-once / write-to-many-destinations copy of the "Symmetric Memory"
-// page's sender warp, here to local rows). Destination slots come from the
-// layout's expert_slot / rank_slot, which are wavefront-uniform, so the
-// destination loop runs on scalar registers. Pad rows are cleared by extra
-// wavefronts after the token wavefronts, one row each.
+// moves nearly all of the bytes, so it is built for HBM bandwidth. Two
+// kernels, chosen per problem by the launcher:
+//  - split_scatter_kernel (a dispatch: many destinations per row): a token
+//    row is cut into 1 KB segments; one workgroup per (token, segment), whose
+//    wavefronts each read the segment, 16 bytes per lane per instruction, and
+//    write it to their share of the token's destination rows (the read-once /
+//    write-to-many-destinations copy of the "Symmetric Memory" page's sender
+//    warp, here to local rows, split over a few wavefronts);
+//  - scatter_kernel (about one destination per row: the receiver-side expand,
+//    a top-1 copy): one wavefront per (token, 4 KB segment) reads its segment
+//    once and writes it to every destination.
+// Destination slots are wavefront-uniform (readlane), so destination loops
+// run on scalar registers. Pad rows are cleared by extra wavefronts after the
+// token workgroups, one row each.
 //
 // Row stores go through a buffer resource that spans exactly one destination
 // row, so the hardware drops any offset outside that row, and carry the
 // streaming cache policy (nt with sc1): the output is far larger than the
 // caches and is not read back here, and of the store forms measured on MI355X
-// this one moved the rows fastest.
+// this one moved the rows fastest. Walking the destinations instead (each
+// destination row written by consecutive workgroups, its source row read
+// once per destination from the Infinity Cache) measured slower than the
+// split kernel with bounded occupancy on every batch tried (7 KB fp8 rows:
+// 97.7 against 94.6 us; 8 KB bf16 rows of 16384 tokens: 351 against 306 us).
 #include "dispatch_common.hpp"
 #include "dispatch_device.hpp"
 
@@ -29,13 +38,11 @@ static_assert(DISPATCH_MAX_EXPERTS <= kWave * kWave, "expert_of_row searches two
 // V, the 16-byte vectors per lane of one row segment, follows the stores per
 // loaded row (measured on MI355X): with many destinations per row (dispatch:
 // K expert rows and the rank rows) one vector per lane, i.e. many short
-// wavefronts, moves the rows fastest; with about one destination per row
-// (the receiver-side expand, a top-1 copy) four vectors per lane do.
+// wavefronts, moves the rows fastest (split_scatter_kernel below); with
+// about one destination per row (the receiver-side expand, a top-1 copy) four
+// vectors per lane do, with four wavefronts per workgroup (scatter_kernel).
 constexpr int kVecsManyDestinations = 1;
 constexpr int kVecsFewDestinations = 4;
-// Wavefronts per workgroup, measured the same way: 1 with many destinations
-// per row, 4 with about one.
-constexpr int kWavesManyDestinations = 1;
 constexpr int kWavesFewDestinations = 4;
 
 struct ScatterParams {
@@ -53,6 +60,7 @@ struct ScatterParams {
     int32_t alignment;
     int32_t write_rank;      // rank_x / rank_sf requested
     int32_t write_expert;    // recv_x / recv_sf requested
+    int64_t token_groups;    // split kernel: workgroups of token segments (num_tokens * segments)
 };
 
 template <int V>
@@ -194,158 +202,104 @@ scatter_kernel(const u32x4* __restrict__ x, const uint32_t* __restrict__ x_sf, S
     }
 }
 
-// Row scatter in destination order, for layouts that keep a row order
-// (keeps_row_order: rows of 4 to 8 KB with several destinations each, read
-// ahead into the Infinity Cache). The order lists every
-// routed row as (dest, token), tile by tile (a tile is a run of consecutive
-// tokens), inside a tile grouped by expert then rank, each group in slot
-// order. Workgroup b takes kOrderWaves * kOrderRows consecutive entries and
-// one slice (of about 3.5 KB) of their rows: b / slices picks the entries,
-// b % slices the slice. Workgroups run on XCD b % 8, so each XCD's L2 holds
-// only a slice of the current tile's source rows, and consecutive workgroups
-// fill consecutive destination rows. Each destination row is written once;
-// each source row is read once per destination, from the caches (the layout
-// kernels read the rows ahead into the Infinity Cache). On MI355X this moved
-// 7 KB fp8 rows with scale factors 5 % faster than one wavefront per source
-// row segment writing all of its destinations (98 against 104 us for 4096
-// tokens, top-8 of 256, alignment 128); 4 wavefronts of 2 rows and slices of
-// at most 4 KB measured best.
-constexpr int kOrderRows = 2;          // order entries (destination rows) per wavefront
-constexpr int kOrderWaves = 4;         // wavefronts per workgroup
-constexpr int kOrderSliceMaxVecs = 256;  // 16-byte vectors per row slice, at most (4 per lane)
+// Rows with many destinations (a dispatch: K expert rows and up to K rank
+// rows per token): one workgroup per (token, 1 KB row segment), whose
+// wavefronts split the token's destinations, kSplitDestinations each. Every
+// wavefront loads the segment itself (the workgroup's wavefronts share the
+// CU's L1), issued with the status and slot loads so that one memory latency
+// precedes the stores. The launch bounds how many workgroups share a CU
+// (kSplitStoresPerCu): on MI355X the write stream of this scatter ran faster
+// with fewer row stores in flight, down to a cliff. Measured on the
+// 4096 x 7168 bf16 batch (top-8 of 256 experts, 8 ranks), rows read ahead into
+// the Infinity Cache: 141 us at full occupancy, 131 us with about 48 1 KB
+// stores in flight per CU (3 workgroups of 4 wavefronts), 170 us with 32.
+// Pad rows follow as extra workgroups, one row per wavefront.
+constexpr int kSplitDestinations = 4;
+constexpr int kSplitStoresPerCu = 64;
+constexpr int kWaveSlotsPerCu = 32;
 
-struct OrderShape {
-    int64_t groups;       // workgroups per slice (entries / (kOrderWaves * kOrderRows), rounded up)
-    int64_t max_entries;  // entries the order can hold
-    int32_t slices;
-    int32_t slice_vecs;
-};
-
-inline OrderShape order_shape(const dispatch_problem_t& prob) {
-    OrderShape o{};
-    const int64_t row_vecs = prob.row_bytes / 16;
-    o.slices = (int32_t)((row_vecs + kOrderSliceMaxVecs - 1) / kOrderSliceMaxVecs);
-    o.slice_vecs = (int32_t)((row_vecs + o.slices - 1) / o.slices);
-    o.max_entries = (row_order_ints(prob) - 2) / 2;
-    o.groups = (o.max_entries + kOrderWaves * kOrderRows - 1) / (kOrderWaves * kOrderRows);
-    return o;
-}
-
-template <int SV>
-__global__ void __launch_bounds__(kOrderWaves * kWave)
-order_scatter_kernel(const u32x4* __restrict__ x, const uint32_t* __restrict__ x_sf, ScatterParams p, OrderShape o,
-                     const int2* __restrict__ order, const int32_t* __restrict__ expert_count,
-                     const int32_t* __restrict__ expert_psum, const int32_t* __restrict__ status,
-                     u32x4* __restrict__ rank_x, uint32_t* __restrict__ rank_sf, u32x4* __restrict__ recv_x,
-                     uint32_t* __restrict__ recv_sf) {
+__global__ void __launch_bounds__(1024)
+split_scatter_kernel(const u32x4* __restrict__ x, const uint32_t* __restrict__ x_sf, ScatterParams p,
+                     const int32_t* __restrict__ expert_slot, const int32_t* __restrict__ rank_slot,
+                     const int32_t* __restrict__ expert_count, const int32_t* __restrict__ expert_psum,
+                     const int32_t* __restrict__ status, u32x4* __restrict__ rank_x,
+                     uint32_t* __restrict__ rank_sf, u32x4* __restrict__ recv_x, uint32_t* __restrict__ recv_sf) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t order_blocks = o.groups * o.slices;
-    if ((int64_t)blockIdx.x >= order_blocks) {  // pad rows, one per wavefront
+    const int waves = blockDim.x / kWave;
+    if ((int64_t)blockIdx.x >= p.token_groups) {  // pad rows, one per wavefront
         if (*status != 0) return;  // the layout is unspecified: write nothing
-        zero_pads(p, ((int64_t)blockIdx.x - order_blocks) * kOrderWaves + wave, lane, expert_count, expert_psum,
-                  recv_x, recv_sf);
+        zero_pads(p, ((int64_t)blockIdx.x - p.token_groups) * waves + wave, lane, expert_count, expert_psum, recv_x,
+                  recv_sf);
         return;
     }
-    const int64_t group = blockIdx.x / o.slices;
-    const int j = (int)(blockIdx.x - group * o.slices);
-    const int64_t first = (group * kOrderWaves + wave) * kOrderRows;
-    // The status, the entry count and this wavefront's entries are loaded
-    // together (entries past the count lie inside the array and are dropped
-    // below), so that one memory latency, not three, precedes the row loads.
-    const int st = *status;
-    const int64_t count = order[0].x;
-    int2 ent = make_int2(0, -1);
-    if (lane < kOrderRows && first + lane < o.max_entries) ent = order[1 + first + lane];
-    asm volatile("" ::: "memory");  // the three loads go out before the checks below
-    if (st != 0) return;  // the layout is unspecified: write nothing
-    const int64_t n = min(count, o.max_entries);
-    if (first >= n) return;
-    if (first + lane >= n) ent.y = -1;
+    const int K = p.num_topk;
+    const int64_t t = blockIdx.x / p.segments;
+    const int seg = (int)(blockIdx.x - t * p.segments);
     const int64_t nv = p.row_vecs;
-    const int64_t v0 = (int64_t)j * o.slice_vecs;
-    const int64_t v1 = min(v0 + o.slice_vecs, nv);
-    // All loads of the wavefront's rows go out before the first store.
-    u32x4 v[kOrderRows][SV];
-    int src[kOrderRows];
-#pragma unroll
-    for (int r = 0; r < kOrderRows; ++r) {
-        const int t = __builtin_amdgcn_readlane(ent.y, r);
-        src[r] = t >= 0 && t < p.num_tokens ? t : -1;
-#pragma unroll
-        for (int q = 0; q < SV; ++q) {
-            const int64_t i = v0 + q * kWave + lane;
-            if (src[r] >= 0 && i < v1) v[r][q] = x[(int64_t)src[r] * nv + i];
+    const int64_t i = (int64_t)seg * kWave + lane;
+    const int S = seg == 0 ? p.sf_per_token : 0;  // the first segment's workgroup moves the scale factors
+    // The segment, the status (a vector load, so that no wait for it holds
+    // back the others) and the token's destinations: lanes [0, K) its expert
+    // rows, lanes [K, 2K) its rank rows (at the owning k, else -1).
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (i < nv) v = x[t * nv + i];
+    uint32_t sf = 0;
+    if (lane < S) sf = x_sf[t * S + lane];
+    const int st = (int)__builtin_amdgcn_raw_buffer_load_b32(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(status), 0, 4, kBufferWord3), 0, 0, 0);
+    // One load instruction for both lists (a per-lane address, not two
+    // branches, whose loads the compiler would serialize).
+    const bool expert_lane = lane < K;
+    const bool want = expert_lane ? p.write_expert != 0 : (lane < 2 * K && rank_slot != nullptr && p.write_rank != 0);
+    const int32_t* slot = expert_lane ? expert_slot + t * K + lane : rank_slot + t * K + (lane - K);
+    int d = -1;
+    if (want) d = *slot;
+    asm volatile("" ::: "memory");  // the loads go out before the check below
+    if (__builtin_amdgcn_readfirstlane(st) != 0) return;  // the layout is unspecified: write nothing
+    // Slots past the capacities never occur with status 0; they are dropped
+    // so that no store can leave the output buffers.
+    if (expert_lane ? d >= p.recv_capacity : d >= p.rank_capacity) d = -1;
+    uint64_t mine = __ballot(d >= 0);
+    // This wavefront's destinations: the valid ones numbered
+    // [wave * kSplitDestinations, (wave + 1) * kSplitDestinations).
+    for (int skip = wave * kSplitDestinations; skip > 0 && mine != 0; --skip) mine &= mine - 1;
+    for (int n = 0; n < kSplitDestinations && mine != 0; ++n, mine &= mine - 1) {
+        const int j = __builtin_ctzll(mine);
+        const int dest = __builtin_amdgcn_readlane(d, j);
+        // Vectors past the row end fall outside the row's buffer range and are dropped.
+        u32x4* row = (j < K ? recv_x : rank_x) + (int64_t)dest * nv;
+        RowWriter(row, (int)(nv * 16)).store(i, v);
+        if (S > 0) {
+            uint32_t* sf_row = (j < K ? recv_sf : rank_sf) + (int64_t)dest * S;
+            for (int q = lane; q < S; q += kWave) sf_row[q] = q < kWave ? sf : x_sf[t * S + q];
         }
-    }
-#pragma unroll
-    for (int r = 0; r < kOrderRows; ++r) {
-        if (src[r] < 0) continue;
-        const int d = __builtin_amdgcn_readlane(ent.x, r);
-        u32x4* row;
-        uint32_t* sf_row;
-        if (d >= 0) {
-            if (!p.write_expert || d >= p.recv_capacity) continue;
-            row = recv_x + (int64_t)d * nv;
-            sf_row = recv_sf + (int64_t)d * p.sf_per_token;
-        } else {
-            const int64_t rr = -1 - (int64_t)d;
-            if (!p.write_rank || rr >= p.rank_capacity) continue;
-            row = rank_x + rr * nv;
-            sf_row = rank_sf + rr * p.sf_per_token;
-        }
-        const RowWriter dst(row, (int)(nv * 16));
-#pragma unroll
-        for (int q = 0; q < SV; ++q) {
-            const int64_t i = v0 + q * kWave + lane;
-            if (i < v1) dst.store(i, v[r][q]);
-        }
-        if (j == 0)  // the first slice's wavefronts move the scale factors
-            for (int i = lane; i < p.sf_per_token; i += kWave)
-                sf_row[i] = x_sf[(int64_t)src[r] * p.sf_per_token + i];
     }
 }
 
 template <int V, int W>
-hipError_t launch_v(dim3 grid, hipStream_t stream, const u32x4* x, const uint32_t* x_sf, ScatterParams p,
+hipError_t launch_v(dim3 grid, size_t lds, hipStream_t stream, const u32x4* x, const uint32_t* x_sf, ScatterParams p,
                     const int32_t* expert_slot, const int32_t* rank_slot, const int32_t* expert_count,
                     const int32_t* expert_psum, const int32_t* status, u32x4* rank_x, uint32_t* rank_sf,
                     u32x4* recv_x, uint32_t* recv_sf) {
     void* args[] = {&x, &x_sf, &p, &expert_slot, &rank_slot, &expert_count, &expert_psum,
                     &status, &rank_x, &rank_sf, &recv_x, &recv_sf};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&scatter_kernel<V, W>), grid, dim3(W * kWave), args, 0,
+    return hipLaunchKernel(reinterpret_cast<const void*>(&scatter_kernel<V, W>), grid, dim3(W * kWave), args, lds,
                            stream);
 }
 
-template <int SV>
-hipError_t launch_order_sv(dim3 grid, hipStream_t stream, const u32x4* x, const uint32_t* x_sf, ScatterParams p,
-                           OrderShape o, const int2* order, const int32_t* expert_count, const int32_t* expert_psum,
-                           const int32_t* status, u32x4* rank_x, uint32_t* rank_sf, u32x4* recv_x,
-                           uint32_t* recv_sf) {
-    void* args[] = {&x, &x_sf, &p, &o, &order, &expert_count, &expert_psum, &status, &rank_x, &rank_sf, &recv_x,
-                    &recv_sf};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&order_scatter_kernel<SV>), grid, dim3(kOrderWaves * kWave),
-                           args, 0, stream);
-}
-
-// Whether a scatter of this problem takes the ordered kernel.
-inline bool takes_order(const dispatch_problem_t& prob, const dispatch_layout_t& lay, bool few_destinations) {
-    return lay.row_order != nullptr && !few_destinations && keeps_row_order(prob);
-}
-
 // The scatter's parameters and grid for a problem: workgroups and threads
-// per workgroup, token wavefronts first (or the ordered kernel's entry
-// groups), then the pad-row wavefronts.
+// per workgroup, the token workgroups first, then the pad-row wavefronts.
 struct ScatterLaunch {
     ScatterParams p;
-    bool order;
-    OrderShape o;
-    int v;             // 16-byte vectors per lane of the source-major kernel
+    bool split;        // split_scatter_kernel, else scatter_kernel
+    int v;             // 16-byte vectors per lane of scatter_kernel
     int64_t blocks;
     int threads;
+    int lds;           // dynamic LDS per workgroup, reserved only to bound the workgroups per CU
 };
 
-ScatterLaunch plan_scatter(const dispatch_problem_t& prob, const dispatch_layout_t& lay, bool few_destinations) {
+ScatterLaunch plan_scatter(const dispatch_problem_t& prob, bool few_destinations) {
     ScatterLaunch s{};
     ScatterParams& p = s.p;
     p.num_tokens = prob.num_tokens;
@@ -356,8 +310,14 @@ ScatterLaunch plan_scatter(const dispatch_problem_t& prob, const dispatch_layout
     if (p.segments < 1) p.segments = 1;
     const int64_t seg_vecs = (p.row_vecs + p.segments - 1) / p.segments;
     s.v = (int)((seg_vecs + kWave - 1) / kWave);
-    s.order = takes_order(prob, lay, few_destinations);
-    const int w = s.order ? kOrderWaves : (few_destinations ? kWavesFewDestinations : kWavesManyDestinations);
+    // A token's destinations at most: K expert rows and min(K, R) rank rows.
+    const int list = ((prob.flags & DISPATCH_EXPERT_MAJOR) ? prob.num_topk : 0) +
+                     ((prob.flags & DISPATCH_RANK_CONTIG) ? (prob.num_topk < prob.num_ranks ? prob.num_topk
+                                                                                              : prob.num_ranks)
+                                                          : 0);
+    s.split = !few_destinations;
+    const int split_waves = list < 1 ? 1 : (list + kSplitDestinations - 1) / kSplitDestinations;
+    const int w = s.split ? split_waves : kWavesFewDestinations;
     s.threads = w * kWave;
     const int64_t waves = prob.num_tokens * p.segments;
     p.token_waves = (waves + w - 1) / w * w;
@@ -379,9 +339,18 @@ ScatterLaunch plan_scatter(const dispatch_problem_t& prob, const dispatch_layout
     p.pad_by_block = blocks_reached < prob.num_experts;
     const int64_t pad_waves =
         pads ? (p.pad_by_block ? blocks_reached : (int64_t)prob.num_experts) * p.pad_waves_per_expert : 0;
-    if (s.order) {
-        s.o = order_shape(prob);
-        s.blocks = s.o.groups * s.o.slices + (pad_waves + w - 1) / w;
+    p.token_groups = prob.num_tokens * p.segments;
+    if (s.split) {
+        s.blocks = p.token_groups + (pad_waves + w - 1) / w;
+        // Rows read ahead into the Infinity Cache: about kSplitStoresPerCu
+        // row stores in flight per CU, each workgroup issuing up to `list`;
+        // no bound where a CU's wavefront slots allow no more workgroups
+        // anyway. Rows from HBM need every workgroup the CU can hold.
+        if ((prob.flags & DISPATCH_ROWS_READ_AHEAD) &&
+            read_ahead_fits(prob.num_tokens * prob.row_bytes, prob.num_tokens * prob.sf_per_token)) {
+            const int per_cu = (kSplitStoresPerCu + list - 1) / (list < 1 ? 1 : list);
+            s.lds = per_cu * w < kWaveSlotsPerCu ? lds_for_workgroups_per_cu(per_cu) : 0;
+        }
     } else {
         s.blocks = (p.token_waves + pad_waves + w - 1) / w;
     }
@@ -390,8 +359,8 @@ ScatterLaunch plan_scatter(const dispatch_problem_t& prob, const dispatch_layout
 
 }  // namespace
 
-bool scatter_grid_fits(const dispatch_problem_t& prob, const dispatch_layout_t& lay, bool few_destinations) {
-    const ScatterLaunch s = plan_scatter(prob, lay, few_destinations);
+bool scatter_grid_fits(const dispatch_problem_t& prob, bool few_destinations) {
+    const ScatterLaunch s = plan_scatter(prob, few_destinations);
     // One grid dimension: at most 2^31 - 1 workgroups and 2^32 - 1 work-items.
     return s.blocks <= INT32_MAX && s.blocks * s.threads <= (int64_t)UINT32_MAX;
 }
@@ -399,11 +368,12 @@ bool scatter_grid_fits(const dispatch_problem_t& prob, const dispatch_layout_t& 
 hipError_t launch_scatter(const dispatch_problem_t& prob, const dispatch_layout_t& lay, const void* x,
                           const float* x_sf, void* rank_x, float* rank_sf, void* recv_x, float* recv_sf,
                           hipStream_t stream, bool few_destinations) {
-    const ScatterLaunch s = plan_scatter(prob, lay, few_destinations);
+    const ScatterLaunch s = plan_scatter(prob, few_destinations);
     if (s.blocks == 0) return hipSuccess;
     if (s.blocks > INT32_MAX || s.blocks * s.threads > (int64_t)UINT32_MAX)
         return hipErrorInvalidConfiguration;  // beyond one grid: refused, never truncated
     const dim3 grid((unsigned)s.blocks);
+    const size_t lds = (size_t)s.lds;
     const ScatterParams& p = s.p;
     auto* xs = static_cast<const u32x4*>(x);
     auto* sfs = reinterpret_cast<const uint32_t*>(x_sf);
@@ -411,32 +381,27 @@ hipError_t launch_scatter(const dispatch_problem_t& prob, const dispatch_layout_
     auto* rsf = reinterpret_cast<uint32_t*>(rank_sf);
     auto* ex = static_cast<u32x4*>(recv_x);
     auto* esf = reinterpret_cast<uint32_t*>(recv_sf);
-    if (s.order) {
-        const auto* order = reinterpret_cast<const int2*>(lay.row_order);
-        switch ((s.o.slice_vecs + kWave - 1) / kWave) {
-            case 1: return launch_order_sv<1>(grid, stream, xs, sfs, p, s.o, order, lay.expert_count,
-                                              lay.expert_psum, lay.status, rx, rsf, ex, esf);
-            case 2: return launch_order_sv<2>(grid, stream, xs, sfs, p, s.o, order, lay.expert_count,
-                                              lay.expert_psum, lay.status, rx, rsf, ex, esf);
-            case 3: return launch_order_sv<3>(grid, stream, xs, sfs, p, s.o, order, lay.expert_count,
-                                              lay.expert_psum, lay.status, rx, rsf, ex, esf);
-            default: return launch_order_sv<4>(grid, stream, xs, sfs, p, s.o, order, lay.expert_count,
-                                               lay.expert_psum, lay.status, rx, rsf, ex, esf);
-        }
+    if (s.split) {
+        const int32_t* es = lay.expert_slot;
+        const int32_t* rs = lay.rank_slot;
+        const int32_t* ec = lay.expert_count;
+        const int32_t* ep = lay.expert_psum;
+        const int32_t* st = lay.status;
+        ScatterParams pc = p;
+        void* args[] = {&xs, &sfs, &pc, &es, &rs, &ec, &ep, &st, &rx, &rsf, &ex, &esf};
+        return hipLaunchKernel(reinterpret_cast<const void*>(&split_scatter_kernel), grid, dim3(s.threads), args, lds,
+                               stream);
     }
-    if (!few_destinations)  // one vector per lane: v == 1
-        return launch_v<1, kWavesManyDestinations>(grid, stream, xs, sfs, p, lay.expert_slot, lay.rank_slot,
-                                                   lay.expert_count, lay.expert_psum, lay.status, rx, rsf, ex, esf);
 #define MOE_DISPATCH_SCATTER_CASE(N)                                                                       \
     case N:                                                                                                \
-        return launch_v<N, kWavesFewDestinations>(grid, stream, xs, sfs, p, lay.expert_slot, lay.rank_slot, \
+        return launch_v<N, kWavesFewDestinations>(grid, lds, stream, xs, sfs, p, lay.expert_slot, lay.rank_slot, \
                                                   lay.expert_count, lay.expert_psum, lay.status, rx, rsf, ex, esf);
     switch (s.v) {
         MOE_DISPATCH_SCATTER_CASE(1)
         MOE_DISPATCH_SCATTER_CASE(2)
         MOE_DISPATCH_SCATTER_CASE(3)
         default:
-            return launch_v<4, kWavesFewDestinations>(grid, stream, xs, sfs, p, lay.expert_slot, lay.rank_slot,
+            return launch_v<4, kWavesFewDestinations>(grid, lds, stream, xs, sfs, p, lay.expert_slot, lay.rank_slot,
                                                       lay.expert_count, lay.expert_psum, lay.status, rx, rsf, ex, esf);
     }
 #undef MOE_DISPATCH_SCATTER_CASE

@@ -39,7 +39,6 @@ int main(void) {
     OFF(dispatch_layout_t, rank_src_token_idx);
     OFF(dispatch_layout_t, status);
     OFF(dispatch_layout_t, expert_count_cumulative);
-    OFF(dispatch_layout_t, row_order);
 
     SIZE(dispatch_expand_problem_t);
     OFF(dispatch_expand_problem_t, num_sources);

@@ -47,17 +47,18 @@ def run_gpu(topk: np.ndarray, num_experts: int, num_ranks: int, alignment: int,
             x_bytes: np.ndarray, x_sf: Optional[np.ndarray] = None, *, topk_bytes: int = 8,
             flags: int = M.ALL_OUTPUTS, recv_capacity: Optional[int] = None,
             rank_capacity: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
-            scatter: bool = True, combined: bool = False, row_order: bool = True) -> GpuRun:
+            scatter: bool = True, combined: bool = False, read_ahead: bool = False) -> GpuRun:
     """Layout and scatter of one batch on the GPU: two calls, or with
-    ``combined`` the single dispatch_layout_and_scatter call. ``row_order``
-    requests the layout's row order (the scatter then walks destinations for
-    rows of 4 KB or more); without it the scatter walks the source rows."""
+    ``combined`` the single dispatch_layout_and_scatter call. ``read_ahead``:
+    the two calls as dispatch_layout_read_ahead, then dispatch_scatter with
+    the DISPATCH_ROWS_READ_AHEAD hint (the scatter's bounded-occupancy
+    launch)."""
     t, k = topk.shape
     row_bytes = x_bytes.shape[1]
     s = 0 if x_sf is None else x_sf.shape[1]
     prob = M.make_problem(t, k, num_experts, num_ranks, alignment, topk_bytes, row_bytes, s,
                           recv_capacity, rank_capacity, flags)
-    lay = M.alloc_layout(prob, DEVICE, row_order=row_order)
+    lay = M.alloc_layout(prob, DEVICE)
     for _, t_ in lay.tensors():
         t_.fill_(CANARY)
     ws = workspace if workspace is not None else M.alloc_workspace(prob, DEVICE)
@@ -73,6 +74,12 @@ def run_gpu(topk: np.ndarray, num_experts: int, num_ranks: int, alignment: int,
     if combined:
         M.dispatch_layout_and_scatter(prob, topk_d, lay, ws, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x,
                                       rows.recv_sf)
+    elif read_ahead:
+        M.dispatch_layout_read_ahead(prob, topk_d, lay, ws, x_d, sf_d)
+        if scatter:
+            hinted = M.Problem.from_buffer_copy(prob)
+            hinted.flags |= M.ROWS_READ_AHEAD
+            M.dispatch_scatter(hinted, lay, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x, rows.recv_sf)
     else:
         M.dispatch_layout(prob, topk_d, lay, ws)
         if scatter:
@@ -96,54 +103,6 @@ def assert_layout_equal(run: GpuRun, ref: oracle.Layout):
     assert np.array_equal(got["rank_src_token_idx"][:n_rank], ref.rank_src_token_idx[:n_rank]), "rank_src"
     assert np.all(got["recv_src_token_idx"][p_total:] == CANARY), "recv_src written past the total"
     assert np.all(got["rank_src_token_idx"][n_rank:] == CANARY), "rank_src written past the total"
-    if "row_order" in got:
-        assert_row_order(got["row_order"], ref, run.problem)
-
-
-def keeps_row_order(problem) -> bool:
-    """The documented rule for when a layout keeps its row order."""
-    dests = (problem.num_topk if problem.flags & M.EXPERT_MAJOR else 0) + (1 if problem.flags & M.RANK_CONTIG else 0)
-    return (dests > 1 and 4096 <= problem.row_bytes <= 8192 and problem.num_experts + problem.num_ranks <= 2048
-            and problem.num_tokens * (problem.row_bytes + 4 * problem.sf_per_token) <= 160 << 20)
-
-
-def assert_row_order(row_order: np.ndarray, ref: oracle.Layout, problem=None):
-    """The layout's row order against the oracle's inverse maps. It must hold
-    every routed row once, as (dest, token), with rank rows as -1 - row; the
-    entries form runs of consecutive tokens (tiles, in token order), and
-    inside a run they are grouped by key (experts, then ranks), each group in
-    consecutive slots. The tile length is the library's choice, so a run may
-    span several tiles: the checks hold either way."""
-    n = int(row_order[0])
-    assert int(row_order[1]) == 0
-    if problem is not None and not keeps_row_order(problem):
-        assert n == -1, "row order kept where the scatter does not walk it"
-        return
-    p_total, n_rank = ref.num_recv_rows, ref.num_rank_rows
-    recv_src = ref.recv_src_token_idx[:p_total]
-    slots = np.nonzero(recv_src >= 0)[0]
-    want = np.concatenate([np.stack([slots, recv_src[slots]], axis=1),
-                           np.stack([-1 - np.arange(n_rank), ref.rank_src_token_idx[:n_rank]], axis=1)])
-    assert n == len(want), f"row order holds {n} rows, the oracle has {len(want)}"
-    ent = row_order[2:2 + 2 * n].reshape(n, 2).astype(np.int64)
-    order = lambda a: a[np.lexsort((a[:, 1], a[:, 0]))]  # noqa: E731
-    assert np.array_equal(order(ent), order(want.astype(np.int64))), "row order is not a permutation of the rows"
-    if n == 0:
-        return
-    num_e = len(ref.expert_count)
-    dest, tok = ent[:, 0], ent[:, 1]
-    key = np.where(dest >= 0, np.searchsorted(ref.expert_psum, dest, side="right") - 1,
-                   num_e + np.searchsorted(ref.rank_psum, -1 - dest, side="right") - 1)
-    # Runs: maximal stretches of non-decreasing key.
-    starts = np.concatenate([[0], np.nonzero(np.diff(key) < 0)[0] + 1, [n]])
-    prev_max = -1
-    for a, b in zip(starts[:-1], starts[1:]):
-        k_run, d_run, t_run = key[a:b], dest[a:b], tok[a:b]
-        same = k_run[1:] == k_run[:-1]
-        row = np.where(d_run >= 0, d_run, -1 - d_run)
-        assert np.all(row[1:][same] == row[:-1][same] + 1), "a key's rows are not consecutive slots"
-        assert t_run.min() > prev_max, "runs are not in token order"
-        prev_max = t_run.max()
 
 
 def assert_rows_full(run: GpuRun, ref: oracle.Layout, x_bytes: np.ndarray, x_sf: Optional[np.ndarray]):

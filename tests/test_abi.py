@@ -36,18 +36,18 @@ def test_library_exports_every_declared_symbol():
 
 def test_binding_constants_match_header():
     d = _defines()
-    assert d["DISPATCH_ABI_VERSION"] == M.dispatch_abi_version() == 4
+    assert d["DISPATCH_ABI_VERSION"] == M.dispatch_abi_version() == 5
     assert (d["DISPATCH_ERR_NULL"], d["DISPATCH_ERR_ARG"], d["DISPATCH_ERR_ALIGN"],
             d["DISPATCH_ERR_WORKSPACE"], d["DISPATCH_ERR_HIP"]) == (
         M.ERR_NULL, M.ERR_ARG, M.ERR_ALIGN, M.ERR_WORKSPACE, M.ERR_HIP)
     assert (d["DISPATCH_STATUS_BAD_EXPERT"], d["DISPATCH_STATUS_RECV_OVERFLOW"],
             d["DISPATCH_STATUS_RANK_OVERFLOW"], d["DISPATCH_STATUS_DUP_EXPERT"]) == (
         M.STATUS_BAD_EXPERT, M.STATUS_RECV_OVERFLOW, M.STATUS_RANK_OVERFLOW, M.STATUS_DUP_EXPERT)
-    assert (d["DISPATCH_RANK_CONTIG"], d["DISPATCH_EXPERT_MAJOR"], d["DISPATCH_ZERO_PAD"]) == (
-        M.RANK_CONTIG, M.EXPERT_MAJOR, M.ZERO_PAD)
+    assert (d["DISPATCH_RANK_CONTIG"], d["DISPATCH_EXPERT_MAJOR"], d["DISPATCH_ZERO_PAD"],
+            d["DISPATCH_ROWS_READ_AHEAD"]) == (M.RANK_CONTIG, M.EXPERT_MAJOR, M.ZERO_PAD, M.ROWS_READ_AHEAD)
     assert d["DISPATCH_MAX_TOPK"] == M.MAX_TOPK and d["DISPATCH_MAX_EXPERTS"] == M.MAX_EXPERTS
     assert d["DISPATCH_MAX_RANKS"] == M.MAX_RANKS
-    assert ctypes.sizeof(M.Problem) == 64 and ctypes.sizeof(M.LayoutPtrs) == 11 * 8
+    assert ctypes.sizeof(M.Problem) == 64 and ctypes.sizeof(M.LayoutPtrs) == 10 * 8
 
 
 def test_strerror_covers_codes():
@@ -73,7 +73,7 @@ BAD_PROBLEMS = [
     dict(num_tokens=-1), dict(num_topk=0), dict(num_topk=33), dict(num_experts=0),
     dict(num_experts=4097), dict(num_ranks=3), dict(num_ranks=0), dict(num_ranks=512),
     dict(num_experts=4096, num_ranks=2048),
-    dict(expert_alignment=0), dict(topk_idx_bytes=2), dict(sf_per_token=-1), dict(flags=8),
+    dict(expert_alignment=0), dict(topk_idx_bytes=2), dict(sf_per_token=-1), dict(flags=16),
     dict(recv_capacity_rows=-1), dict(reserved=1), dict(num_tokens=1 << 31),
     dict(num_tokens=1 << 28, expert_alignment=1 << 20),
     dict(num_tokens=(1 << 62) + 1),  # rejected before T * K is formed
@@ -358,23 +358,16 @@ def test_noalloc_host_errors_before_launch():
     assert call(bad) == M.ERR_ARG
 
 
-def test_row_order_size_and_checks():
-    """The row order's length, its 8-byte alignment, and its refusal by the
-    receiver-side expand layout (host checks only, nothing launched)."""
-    lib = M.load_library()
-    p = M.make_problem(100, 8, 256, 8, 1, row_bytes=64)
-    assert M.dispatch_row_order_size(p) == 2 + 2 * (100 * 8 + 100 * 8)
-    p3 = M.make_problem(100, 8, 256, 4, 1, row_bytes=64)
-    assert M.dispatch_row_order_size(p3) == 2 + 2 * (100 * 8 + 100 * 4)
-    ws_need = M.dispatch_workspace_size(p)
-    lay = M.LayoutPtrs(*([4096] * 9), None, 4100)  # row order 4-byte but not 8-byte aligned
-    assert lib.dispatch_layout(ctypes.byref(p), 4096, ctypes.byref(lay), 4096, ws_need, None) == M.ERR_ALIGN
-    assert lib.dispatch_scatter(ctypes.byref(p), ctypes.byref(lay), 4096, None, 4096, None, 4096, None,
-                                None) == M.ERR_ALIGN
-    q = M.make_expand_problem(2, 16, 8, 256, 8, 0, row_bytes=64)
-    eq = M.LayoutPtrs(4096, None, 4096, None, 4096, None, 4096, None, 4096, None, 4096)
-    assert lib.dispatch_expand_layout(ctypes.byref(q), 4096, 4096, ctypes.byref(eq), 4096,
-                                      M.dispatch_expand_workspace_size(q), None) == M.ERR_ARG
+def test_read_ahead_hint_flag_is_accepted_and_other_bits_refused():
+    """DISPATCH_ROWS_READ_AHEAD passes the problem check of every call (the
+    layout calls ignore it); an unknown flag bit is refused."""
+    p = M.make_problem(100, 8, 256, 8, 1, row_bytes=64, flags=M.ALL_OUTPUTS | M.ROWS_READ_AHEAD)
+    assert M.dispatch_workspace_size(p) == M.dispatch_workspace_size(M.make_problem(100, 8, 256, 8, 1, row_bytes=64))
+    assert M.dispatch_max_rows(p) == (800, 800)
+    p.flags = M.ALL_OUTPUTS | 16
+    with pytest.raises(M.DispatchError) as e:
+        M.dispatch_workspace_size(p)
+    assert e.value.code == M.ERR_ARG
 
 
 def test_scatter_grid_beyond_one_launch_is_refused_before_any_launch():

@@ -51,20 +51,20 @@ def test_reduced_workload_full_parity(name, t):
 # times: the whole layout bit-exact, rows checked against the oracle on
 # samples (full rows for the smaller ones) and on every row by a device gather.
 # The benchmark times the combined call (the layout kernels read the token
-# rows ahead for the scatter when they fit the Infinity Cache); the two
-# separate calls are checked as well.
-# The source-major scatter (a layout without a row order) as well.
-@pytest.mark.parametrize("combined,row_order", [(True, True), (False, True), (False, False)],
-                         ids=["one_call", "two_calls", "two_calls_source_major"])
+# rows ahead for the scatter when they fit the Infinity Cache, and the
+# scatter then bounds its workgroups per CU); the two separate calls are
+# checked as well, plain and as the read-ahead layout plus the hinted scatter.
+@pytest.mark.parametrize("combined,read_ahead", [(True, False), (False, False), (False, True)],
+                         ids=["one_call", "two_calls", "two_calls_read_ahead"])
 @pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
-def test_workload_full_size(name, combined, row_order):
+def test_workload_full_size(name, combined, read_ahead):
     w = W.get(name)
-    _banner(f"{w.describe()} combined={combined} row_order={row_order}")
+    _banner(f"{w.describe()} combined={combined} read_ahead={read_ahead}")
     inp = W.make_inputs(w)
     xb = inp.x_bytes()
     ref = oracle.layout(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment)
     run = H.run_gpu(inp.topk_idx, w.num_experts, w.num_ranks, w.alignment, xb, inp.x_sf, combined=combined,
-                    row_order=row_order)
+                    read_ahead=read_ahead)
     H.assert_layout_equal(run, ref)
     if w.num_tokens * w.row_bytes <= 64 << 20:
         H.assert_rows_full(run, ref, xb, inp.x_sf)
