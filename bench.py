@@ -35,8 +35,9 @@ if ROOT not in sys.path:
 METRIC = "dispatch GB/s & % HBM peak, 4096 tok×7168 bf16, top-8 of 256 experts"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 SCATTER_SOURCES = [os.path.join(ROOT, "moe_token_dispatch_amd", "csrc", f)
-                   for f in ("dispatch_scatter.hip", "dispatch_device.hpp")]
+                   for f in ("dispatch_scatter.hip", "dispatch_device.hpp", "dispatch_common.hpp")]
 COMBINE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_traffic.json")
+READ_AHEAD_MAX_BYTES = 160 << 20  # token rows + scale factors the layout reads ahead, at most
 EXPAND_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expand_scatter_traffic.json")
 COMBINE_SOURCES = [os.path.join(ROOT, "moe_token_dispatch_amd", "csrc", f)
                    for f in ("dispatch_combine.hip", "dispatch_device.hpp")]
@@ -690,7 +691,10 @@ def main():
     total_b, layout_b, _ = algorithmic_bytes(t, k, w.num_experts, w.num_ranks, 8, w.row_bytes, s,
                                              t_live, p_rows, n_rank)
     sc_b = scatter_launch_bytes(t, k, w.num_experts, w.row_bytes, s, t_live, p_rows, n_rank)
-    roof_kernel, roof_b = "split_scatter_kernel", sc_b
+    # Rows that the layout reads ahead (up to 160 MB with their scale
+    # factors) are copied by the split kernel, others by scatter_kernel.
+    read_ahead = t * (w.row_bytes + 4 * s) <= READ_AHEAD_MAX_BYTES
+    roof_kernel, roof_b = ("split_scatter_kernel" if read_ahead else "scatter_kernel"), sc_b
     if one_kernel:  # the one kernel moves the whole step's bytes
         roof_kernel, roof_b = "assign_kernel (one-kernel layout + scatter)", total_b
     step_mean_us = statistics.mean(step_us)

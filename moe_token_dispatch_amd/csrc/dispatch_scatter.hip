@@ -6,15 +6,17 @@
 // expand mode (sections 6.4 and 8.2) and the zero padding of section 7.3. It
 // moves nearly all of the bytes, so it is built for HBM bandwidth. Two
 // kernels, chosen per problem by the launcher:
-//  - split_scatter_kernel (a dispatch: many destinations per row): a token
-//    row is cut into 1 KB segments; one workgroup per (token, segment), whose
-//    wavefronts each read the segment, 16 bytes per lane per instruction, and
-//    write it to their share of the token's destination rows (the read-once /
-//    write-to-many-destinations copy of the "Symmetric Memory" page's sender
-//    warp, here to local rows, split over a few wavefronts);
-//  - scatter_kernel (about one destination per row: the receiver-side expand,
-//    a top-1 copy): one wavefront per (token, 4 KB segment) reads its segment
-//    once and writes it to every destination.
+//  - split_scatter_kernel (a dispatch whose rows were just read into the
+//    Infinity Cache): a token row is cut into 1 KB segments; one workgroup per
+//    (token, segment), whose wavefronts each read the segment, 16 bytes per
+//    lane per instruction, and write it to their share of the token's
+//    destination rows, with the workgroups per CU bounded;
+//  - scatter_kernel (rows from HBM, and rows with about one destination: the
+//    receiver-side expand, a top-1 copy): one wavefront per (token, segment of
+//    1 KB, or 4 KB with about one destination) reads its segment once and
+//    writes it to every destination.
+// Both are the read-once / write-to-many-destinations copy of the "Symmetric
+// Memory" page's sender warp, here to local rows.
 // Destination slots are wavefront-uniform (readlane), so destination loops
 // run on scalar registers. Pad rows are cleared by extra wavefronts after the
 // token workgroups, one row each.
@@ -38,9 +40,9 @@ static_assert(DISPATCH_MAX_EXPERTS <= kWave * kWave, "expert_of_row searches two
 // V, the 16-byte vectors per lane of one row segment, follows the stores per
 // loaded row (measured on MI355X): with many destinations per row (dispatch:
 // K expert rows and the rank rows) one vector per lane, i.e. many short
-// wavefronts, moves the rows fastest (split_scatter_kernel below); with
-// about one destination per row (the receiver-side expand, a top-1 copy) four
-// vectors per lane do, with four wavefronts per workgroup (scatter_kernel).
+// wavefronts, moves the rows fastest; with about one destination per row (the
+// receiver-side expand, a top-1 copy) four vectors per lane do. Four
+// wavefronts per workgroup either way.
 constexpr int kVecsManyDestinations = 1;
 constexpr int kVecsFewDestinations = 4;
 constexpr int kWavesFewDestinations = 4;
@@ -203,17 +205,21 @@ scatter_kernel(const u32x4* __restrict__ x, const uint32_t* __restrict__ x_sf, S
 }
 
 // Rows with many destinations (a dispatch: K expert rows and up to K rank
-// rows per token): one workgroup per (token, 1 KB row segment), whose
-// wavefronts split the token's destinations, kSplitDestinations each. Every
-// wavefront loads the segment itself (the workgroup's wavefronts share the
-// CU's L1), issued with the status and slot loads so that one memory latency
-// precedes the stores. The launch bounds how many workgroups share a CU
-// (kSplitStoresPerCu): on MI355X the write stream of this scatter ran faster
-// with fewer row stores in flight, down to a cliff. Measured on the
-// 4096 x 7168 bf16 batch (top-8 of 256 experts, 8 ranks), rows read ahead into
-// the Infinity Cache: 141 us at full occupancy, 131 us with about 48 1 KB
-// stores in flight per CU (3 workgroups of 4 wavefronts), 170 us with 32.
-// Pad rows follow as extra workgroups, one row per wavefront.
+// rows per token) that the layout has just read into the Infinity Cache: one
+// workgroup per (token, 1 KB row segment), whose wavefronts split the token's
+// destinations, kSplitDestinations each. Every wavefront loads the segment
+// itself (the workgroup's wavefronts share the CU's L1), issued with the
+// status and slot loads so that one memory latency precedes the stores. The
+// launch bounds how many workgroups share a CU (kSplitStoresPerCu): on MI355X
+// the write stream ran faster with fewer row stores in flight, down to a
+// cliff. Measured on the 4096 x 7168 bf16 batch (top-8 of 256 experts, 8
+// ranks; 4 wavefronts per workgroup): 144 us at full occupancy, 134 / 129 /
+// 153 / 213 us at 5 / 4 / 3 / 2 workgroups per CU; scatter_kernel, one
+// wavefront per segment writing all its destinations, 143 us. With rows from
+// HBM the bound slows it (163 against 216 us on the same batch) and the split
+// itself loses (65 536 fp8 tokens: 1334 against 1223 us for scatter_kernel),
+// so rows that were not read ahead take scatter_kernel. Pad rows follow as
+// extra workgroups, one row per wavefront.
 constexpr int kSplitDestinations = 4;
 constexpr int kSplitStoresPerCu = 64;
 constexpr int kWaveSlotsPerCu = 32;
@@ -315,7 +321,11 @@ ScatterLaunch plan_scatter(const dispatch_problem_t& prob, bool few_destinations
                      ((prob.flags & DISPATCH_RANK_CONTIG) ? (prob.num_topk < prob.num_ranks ? prob.num_topk
                                                                                               : prob.num_ranks)
                                                           : 0);
-    s.split = !few_destinations;
+    // Rows read ahead into the Infinity Cache (the hint, and rows that
+    // dispatch_layout_read_ahead does read) take the split kernel.
+    const bool cached = (prob.flags & DISPATCH_ROWS_READ_AHEAD) &&
+                        read_ahead_fits(prob.num_tokens * prob.row_bytes, prob.num_tokens * prob.sf_per_token);
+    s.split = !few_destinations && cached;
     const int split_waves = list < 1 ? 1 : (list + kSplitDestinations - 1) / kSplitDestinations;
     const int w = s.split ? split_waves : kWavesFewDestinations;
     s.threads = w * kWave;
@@ -342,15 +352,11 @@ ScatterLaunch plan_scatter(const dispatch_problem_t& prob, bool few_destinations
     p.token_groups = prob.num_tokens * p.segments;
     if (s.split) {
         s.blocks = p.token_groups + (pad_waves + w - 1) / w;
-        // Rows read ahead into the Infinity Cache: about kSplitStoresPerCu
-        // row stores in flight per CU, each workgroup issuing up to `list`;
-        // no bound where a CU's wavefront slots allow no more workgroups
-        // anyway. Rows from HBM need every workgroup the CU can hold.
-        if ((prob.flags & DISPATCH_ROWS_READ_AHEAD) &&
-            read_ahead_fits(prob.num_tokens * prob.row_bytes, prob.num_tokens * prob.sf_per_token)) {
-            const int per_cu = (kSplitStoresPerCu + list - 1) / (list < 1 ? 1 : list);
-            s.lds = per_cu * w < kWaveSlotsPerCu ? lds_for_workgroups_per_cu(per_cu) : 0;
-        }
+        // About kSplitStoresPerCu row stores in flight per CU, each
+        // workgroup issuing up to `list`; no bound where a CU's wavefront
+        // slots allow no more workgroups anyway.
+        const int per_cu = (kSplitStoresPerCu + list - 1) / (list < 1 ? 1 : list);
+        s.lds = per_cu * w < kWaveSlotsPerCu ? lds_for_workgroups_per_cu(per_cu) : 0;
     } else {
         s.blocks = (p.token_waves + pad_waves + w - 1) / w;
     }

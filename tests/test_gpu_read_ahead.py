@@ -1,10 +1,11 @@
 """The scatter after a read-ahead layout, bit for bit against the CPU oracle:
 dispatch_layout_read_ahead then dispatch_scatter with the
 DISPATCH_ROWS_READ_AHEAD hint, and the combined call, which reads the rows
-ahead and bounds the scatter's workgroups per CU itself when the rows fit the
-Infinity Cache. The hint changes only the launch (the reserved LDS that caps
-the workgroups per CU, from the destinations per token); every output must
-equal the oracle's, with canary bands past every total untouched."""
+ahead and sets the hint itself when the rows fit the read-ahead. The hint
+changes only the kernel (split_scatter_kernel instead of scatter_kernel) and
+its launch (the reserved LDS that caps the workgroups per CU, from the
+destinations per token); every output must equal the oracle's, with canary
+bands past every total untouched."""
 
 import numpy as np
 import pytest
