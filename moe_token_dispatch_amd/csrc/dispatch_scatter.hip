@@ -261,9 +261,9 @@ split_scatter_kernel(const u32x4* __restrict__ x, const uint32_t* __restrict__ x
     // branches, whose loads the compiler would serialize).
     const bool expert_lane = lane < K;
     const bool want = expert_lane ? p.write_expert != 0 : (lane < 2 * K && rank_slot != nullptr && p.write_rank != 0);
-    const int32_t* slot = expert_lane ? expert_slot + t * K + lane : rank_slot + t * K + (lane - K);
+    const int32_t* slots = expert_lane ? expert_slot : rank_slot;
     int d = -1;
-    if (want) d = *slot;
+    if (want) d = slots[t * K + (expert_lane ? lane : lane - K)];
     asm volatile("" ::: "memory");  // the loads go out before the check below
     if (__builtin_amdgcn_readfirstlane(st) != 0) return;  // the layout is unspecified: write nothing
     // Slots past the capacities never occur with status 0; they are dropped
