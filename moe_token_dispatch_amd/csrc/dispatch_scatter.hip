@@ -60,7 +60,9 @@ struct ScatterParams {
     int32_t segments;        // row segments per token
     int32_t sf_per_token;
     int32_t num_experts;
-    int32_t pad_waves_per_expert;  // alignment - 1 with pads, else 1
+    int32_t pad_waves_per_expert;  // pad rows per expert covered: alignment - 1 with pads, else 1
+    int32_t pad_parts;             // wavefronts per pad row, each zeroing pad_part_vecs vectors
+    int64_t pad_part_vecs;
     int32_t pad_by_block;          // pad wavefronts mapped per row block (else per expert)
     int32_t alignment;
     int32_t write_rank;      // rank_x / rank_sf requested
@@ -164,6 +166,11 @@ __device__ __forceinline__ void zero_pads(const ScatterParams& p, int64_t pad_wa
                                           const int32_t* __restrict__ expert_count,
                                           const int32_t* __restrict__ expert_psum,
                                           u32x4* __restrict__ recv_x, uint32_t* __restrict__ recv_sf) {
+    // A pad row is zeroed by pad_parts consecutive wavefronts, pad_part_vecs
+    // vectors each.
+    const int64_t row_wave = pad_wave / p.pad_parts;
+    const int part = (int)(pad_wave - row_wave * p.pad_parts);
+    pad_wave = row_wave;
     int64_t row;
     int e;
     if (p.pad_by_block) {
@@ -181,7 +188,10 @@ __device__ __forceinline__ void zero_pads(const ScatterParams& p, int64_t pad_wa
         return;
     const u32x4 zero = {0u, 0u, 0u, 0u};
     const RowWriter dst(recv_x + row * p.row_vecs, (int)(p.row_vecs * 16));
-    for (int64_t i = lane; i < p.row_vecs; i += kWave) dst.store(i, zero);
+    const int64_t v0 = (int64_t)part * p.pad_part_vecs;
+    const int64_t v1 = min(p.row_vecs, v0 + p.pad_part_vecs);
+    for (int64_t i = v0 + lane; i < v1; i += kWave) dst.store(i, zero);
+    if (part != 0) return;  // the first part's wavefront zeroes the scale factors
     const int S = p.sf_per_token;
     for (int i = lane; i < S; i += kWave) recv_sf[row * S + i] = 0u;
 }
@@ -225,6 +235,7 @@ scatter_kernel(const u32x4* __restrict__ x, const uint32_t* __restrict__ x_sf, S
 // extra workgroups, one row per wavefront.
 constexpr int kSplitDestinations = 4;
 constexpr int kSplitStoresPerCu = 64;
+constexpr int64_t kSplitPadVecs = 4 * kWave;  // a pad wavefront's vectors: 4 KB
 constexpr int kWaveSlotsPerCu = 32;
 
 __global__ void __launch_bounds__(1024)
@@ -350,8 +361,14 @@ ScatterLaunch plan_scatter(const dispatch_problem_t& prob, bool few_destinations
     const int64_t blocks_reached = (pairs < prob.num_experts ? pairs : prob.num_experts) +
                                    pairs / prob.expert_alignment;
     p.pad_by_block = blocks_reached < prob.num_experts;
+    // The split kernel's pad wavefronts zero at most kSplitPadVecs vectors
+    // each, about as many stores as its token wavefronts issue; the other
+    // kernel's zero whole rows.
+    p.pad_part_vecs = s.split ? kSplitPadVecs : (p.row_vecs > 0 ? p.row_vecs : 1);
+    p.pad_parts = p.row_vecs > p.pad_part_vecs ? (int32_t)((p.row_vecs + p.pad_part_vecs - 1) / p.pad_part_vecs) : 1;
     const int64_t pad_waves =
-        pads ? (p.pad_by_block ? blocks_reached : (int64_t)prob.num_experts) * p.pad_waves_per_expert : 0;
+        pads ? (p.pad_by_block ? blocks_reached : (int64_t)prob.num_experts) * p.pad_waves_per_expert * p.pad_parts
+             : 0;
     p.token_groups = prob.num_tokens * p.segments;
     if (s.split) {
         s.blocks = p.token_groups + (pad_waves + w - 1) / w;
