@@ -24,7 +24,7 @@ LAYOUT_FIELDS = ("expert_count", "rank_count", "expert_psum", "rank_psum", "expe
 
 
 @dataclasses.dataclass
-class GpuRun:
+class DeviceRun:
     problem: M.Problem
     layout: M.LayoutTensors
     rows: M.RowBuffers
@@ -47,7 +47,7 @@ def run_gpu(topk: np.ndarray, num_experts: int, num_ranks: int, alignment: int,
             x_bytes: np.ndarray, x_sf: Optional[np.ndarray] = None, *, topk_bytes: int = 8,
             flags: int = M.ALL_OUTPUTS, recv_capacity: Optional[int] = None,
             rank_capacity: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
-            scatter: bool = True, combined: bool = False, read_ahead: bool = False) -> GpuRun:
+            scatter: bool = True, combined: bool = False, read_ahead: bool = False) -> DeviceRun:
     """Layout and scatter of one batch on the GPU: two calls, or with
     ``combined`` the single dispatch_layout_and_scatter call. ``read_ahead``:
     the two calls as dispatch_layout_read_ahead, then dispatch_scatter with
@@ -85,10 +85,10 @@ def run_gpu(topk: np.ndarray, num_experts: int, num_ranks: int, alignment: int,
         if scatter:
             M.dispatch_scatter(prob, lay, x_d, sf_d, rows.rank_x, rows.rank_sf, rows.recv_x, rows.recv_sf)
     torch.cuda.synchronize()
-    return GpuRun(prob, lay, rows, x_d, sf_d, ws)
+    return DeviceRun(prob, lay, rows, x_d, sf_d, ws)
 
 
-def assert_layout_equal(run: GpuRun, ref: oracle.Layout):
+def assert_layout_equal(run: DeviceRun, ref: oracle.Layout):
     """Bit-exact comparison of every layout output, plus untouched canary bands."""
     got = run.host_layout()
     assert int(got["status"][0]) == ref.status, f"status {int(got['status'][0])} != oracle {ref.status}"
@@ -105,7 +105,7 @@ def assert_layout_equal(run: GpuRun, ref: oracle.Layout):
     assert np.all(got["rank_src_token_idx"][n_rank:] == CANARY), "rank_src written past the total"
 
 
-def assert_rows_full(run: GpuRun, ref: oracle.Layout, x_bytes: np.ndarray, x_sf: Optional[np.ndarray]):
+def assert_rows_full(run: DeviceRun, ref: oracle.Layout, x_bytes: np.ndarray, x_sf: Optional[np.ndarray]):
     """Every row byte against the oracle's scatter, and untouched rows past the totals."""
     p = run.problem
     want = oracle.scatter(ref, x_bytes, x_sf, rank_contig=bool(p.flags & M.RANK_CONTIG),
@@ -124,7 +124,7 @@ def assert_rows_full(run: GpuRun, ref: oracle.Layout, x_bytes: np.ndarray, x_sf:
         assert np.all(g[n:] == ROW_FILL), f"{name} written past the total"
 
 
-def assert_rows_sampled(run: GpuRun, ref: oracle.Layout, x_bytes: np.ndarray, x_sf: Optional[np.ndarray],
+def assert_rows_sampled(run: DeviceRun, ref: oracle.Layout, x_bytes: np.ndarray, x_sf: Optional[np.ndarray],
                         n_samples: int = 2048, seed: int = 0):
     """Sampled rows against the oracle's row definition, computed one row at a time."""
     rng = np.random.default_rng(seed)
@@ -150,7 +150,7 @@ def assert_rows_sampled(run: GpuRun, ref: oracle.Layout, x_bytes: np.ndarray, x_
             assert np.array_equal(got, want), f"sampled {kind}_sf rows differ from the oracle"
 
 
-def assert_rows_gather_property(run: GpuRun, ref: oracle.Layout, chunk: int = 8192):
+def assert_rows_gather_property(run: DeviceRun, ref: oracle.Layout, chunk: int = 8192):
     """All rows, on the device: row s equals x[token of s] (a torch gather), pads are zero."""
     p_total, n_rank = ref.num_recv_rows, ref.num_rank_rows
     recv_src = torch.from_numpy(ref.recv_src_token_idx[:p_total].astype(np.int64)).to(DEVICE)

@@ -67,7 +67,7 @@ def test_overlapping_calls_on_streams_share_only_the_running_counts():
     for j in jobs:
         ref = oracle.layout(j["topk"], e, r, j["a"])
         assert ref.status == 0
-        run = H.GpuRun(j["prob"], j["lay"], j["rows"], j["x_d"], j["sf_d"], j["ws"])
+        run = H.DeviceRun(j["prob"], j["lay"], j["rows"], j["x_d"], j["sf_d"], j["ws"])
         H.assert_layout_equal(run, ref)
         H.assert_rows_full(run, ref, j["xb"], j["sf"])
         want += rounds * ref.expert_count.astype(np.int64)

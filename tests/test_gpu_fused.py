@@ -172,7 +172,7 @@ def test_plan_call_and_running_counts():
     plan()
     torch.cuda.synchronize()
     ref = oracle.layout(topk, e, r, a)
-    run = H.GpuRun(prob, lay, rows, torch.from_numpy(xb).to(H.DEVICE), None, ws)
+    run = H.DeviceRun(prob, lay, rows, torch.from_numpy(xb).to(H.DEVICE), None, ws)
     H.assert_layout_equal(run, ref)
     want = oracle.scatter(ref, xb)
     assert np.array_equal(rows.recv_x[:ref.num_recv_rows].cpu().numpy(), want.recv_x[:ref.num_recv_rows])

@@ -97,7 +97,7 @@ def test_captured_dispatch_replays_match_oracle(dtype, with_sf, alignment, t, co
         graph.replay()
         torch.cuda.synchronize()
         ref = oracle.layout(inp.topk_idx, e, r, alignment)
-        run = H.GpuRun(prob, lay, rows, x_d, sf_d, ws)
+        run = H.DeviceRun(prob, lay, rows, x_d, sf_d, ws)
         H.assert_layout_equal(run, ref)
         H.assert_rows_full(run, ref, inp.x_bytes(), inp.x_sf)
         if combine:
