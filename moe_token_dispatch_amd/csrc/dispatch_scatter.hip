@@ -19,7 +19,8 @@
 // Memory" page's sender warp, here to local rows.
 // Destination slots are wavefront-uniform (readlane), so destination loops
 // run on scalar registers. Pad rows are cleared by extra wavefronts after the
-// token workgroups, one row each.
+// token workgroups: one row each in scatter_kernel, 4 KB of a row each in
+// split_scatter_kernel.
 //
 // Row stores go through a buffer resource that spans exactly one destination
 // row, so the hardware drops any offset outside that row, and carry the
@@ -230,9 +231,11 @@ scatter_kernel(const u32x4* __restrict__ x, const uint32_t* __restrict__ x_sf, S
 // 153 / 213 us at 5 / 4 / 3 / 2 workgroups per CU; scatter_kernel, one
 // wavefront per segment writing all its destinations, 143 us. With rows from
 // HBM the bound slows it (163 against 216 us on the same batch) and the split
-// itself loses (65 536 fp8 tokens: 1334 against 1223 us for scatter_kernel),
+// itself loses (65 536 fp8 tokens: 1334 against 1198 us for scatter_kernel),
 // so rows that were not read ahead take scatter_kernel. Pad rows follow as
-// extra workgroups, one row per wavefront.
+// extra workgroups, 4 KB of a row per wavefront, about as many stores as a
+// token wavefront issues (a whole 7 KB row per wavefront: 1 % slower on the
+// 7 KB fp8 batch at alignment 128; 1 or 2 KB: 36 % and 14 % slower).
 constexpr int kSplitDestinations = 4;
 constexpr int kSplitStoresPerCu = 64;
 constexpr int64_t kSplitPadVecs = 4 * kWave;  // a pad wavefront's vectors: 4 KB
@@ -247,7 +250,7 @@ split_scatter_kernel(const u32x4* __restrict__ x, const uint32_t* __restrict__ x
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int waves = blockDim.x / kWave;
-    if ((int64_t)blockIdx.x >= p.token_groups) {  // pad rows, one per wavefront
+    if ((int64_t)blockIdx.x >= p.token_groups) {  // pad rows, 4 KB per wavefront
         if (*status != 0) return;  // the layout is unspecified: write nothing
         zero_pads(p, ((int64_t)blockIdx.x - p.token_groups) * waves + wave, lane, expert_count, expert_psum, recv_x,
                   recv_sf);
