@@ -179,8 +179,10 @@ int dispatch_layout_read_ahead(const dispatch_problem_t* problem, const void* to
  *   pad rows zeroed under DISPATCH_ZERO_PAD.
  * Copies are bitwise. Writes nothing when the layout's status is non-zero.
  * One wavefront copies each 1 KB of a row (4 KB when rows have about one
- * destination), so T * ceil(row_bytes / 1024) must stay below 2^31; larger
- * problems return DISPATCH_ERR_HIP without launching.
+ * destination; after a read-ahead, one workgroup of ceil((K + min(K, R)) / 4)
+ * wavefronts per 1 KB), and the launch must fit one grid: at most 2^31 - 1
+ * workgroups and 2^32 - 1 work-items. A larger problem returns
+ * DISPATCH_ERR_ARG before anything is enqueued.
  * A layout may be kept and scattered again, for new rows of the same routing,
  * without recomputing it (the page's cached dispatch, section 6.2). */
 int dispatch_scatter(const dispatch_problem_t* problem, const dispatch_layout_t* layout,
