@@ -191,7 +191,9 @@ int dispatch_scatter(const dispatch_problem_t* problem, const dispatch_layout_t*
 
 /* dispatch_layout followed by dispatch_scatter in one call, with the same
  * arguments, checks, outputs and status semantics as those two calls made in
- * turn (the layout reads the rows ahead, as dispatch_layout_read_ahead). A small batch (T * K up to 3072 pairs, or 2048 when pad rows are
+ * turn (the layout reads the rows ahead, as dispatch_layout_read_ahead, and
+ * the scatter then runs as with DISPATCH_ROWS_READ_AHEAD). A small batch
+ * (T * K up to 3072 pairs, or 2048 when pad rows are
  * zeroed; fewer when E + R is large) is laid out and copied by a single
  * kernel: every workgroup ranks the whole batch itself, so none waits for
  * another, and each copies its share of the rows' 1 KB segments. That saves
