@@ -31,7 +31,8 @@ constexpr int kLdsPerCu = 160 * 1024;  // gfx950
 // Dynamic LDS per workgroup that lets at most n workgroups of a launch share
 // a CU (a kernel that needs no LDS reserves it only to bound its occupancy):
 // midway between the sizes at which n and n + 1 workgroups just fit, so that
-// the hardware's allocation granularity cannot change the count.
+// an allocation granularity of up to 2 KiB cannot change the count for
+// n <= 8 (above that it may admit one workgroup fewer).
 inline int lds_for_workgroups_per_cu(int n) {
     if (n < 1) n = 1;
     return (kLdsPerCu / n + kLdsPerCu / (n + 1)) / 2;

@@ -240,6 +240,7 @@ constexpr int kSplitDestinations = 4;
 constexpr int kSplitStoresPerCu = 64;
 constexpr int64_t kSplitPadVecs = 4 * kWave;  // a pad wavefront's vectors: 4 KB
 constexpr int kWaveSlotsPerCu = 32;
+constexpr int kMaxBoundedWorkgroupsPerCu = 8;
 
 __global__ void __launch_bounds__(1024)
 split_scatter_kernel(const u32x4* __restrict__ x, const uint32_t* __restrict__ x_sf, ScatterParams p,
@@ -376,10 +377,14 @@ ScatterLaunch plan_scatter(const dispatch_problem_t& prob, bool few_destinations
     if (s.split) {
         s.blocks = p.token_groups + (pad_waves + w - 1) / w;
         // About kSplitStoresPerCu row stores in flight per CU, each
-        // workgroup issuing up to `list`; no bound where a CU's wavefront
-        // slots allow no more workgroups anyway.
+        // workgroup issuing up to `list`. The bound was measured with 1 to 8
+        // workgroups per CU (8 to 64 destinations per token); fewer
+        // destinations per token, and bounds a CU's wavefront slots impose
+        // anyway, run unbounded.
         const int per_cu = (kSplitStoresPerCu + list - 1) / (list < 1 ? 1 : list);
-        s.lds = per_cu * w < kWaveSlotsPerCu ? lds_for_workgroups_per_cu(per_cu) : 0;
+        s.lds = per_cu <= kMaxBoundedWorkgroupsPerCu && per_cu * w < kWaveSlotsPerCu
+                    ? lds_for_workgroups_per_cu(per_cu)
+                    : 0;
     } else {
         s.blocks = (p.token_waves + pad_waves + w - 1) / w;
     }
