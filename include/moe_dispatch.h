@@ -32,8 +32,10 @@
  *     dispatch_scatter writes no row.
  *   - Rows and inverse-map entries beyond the totals (expert_psum[E],
  *     rank_psum[R]) up to the capacities are never written.
- *   - Reentrancy: the library is stateless; concurrent calls need their own
- *     workspaces and outputs.
+ *   - Reentrancy: concurrent calls need their own workspaces and outputs. A
+ *     dispatch workspace is zero-filled once by its owner and then kept by
+ *     the calls (see dispatch_workspace_size); the only process-wide setting
+ *     is the guard on in-kernel waits (dispatch_set_wait_limit).
  *   - Language: the header is plain C (C99) as well as C++. A compiler other
  *     than hipcc must define __HIP_PLATFORM_AMD__, as HIP's own runtime header
  *     included below requires.
@@ -50,7 +52,7 @@
 extern "C" {
 #endif
 
-#define DISPATCH_ABI_VERSION 5
+#define DISPATCH_ABI_VERSION 6
 
 /* Limits. K <= 32 follows the page's bound on the top-k width (section 4.2);
  * R <= 1024 follows its kNumMaxRanks (section 6.2). */
@@ -72,6 +74,9 @@ extern "C" {
 #define DISPATCH_STATUS_RANK_OVERFLOW 4u  /* rank_psum[R] > rank_capacity_rows */
 #define DISPATCH_STATUS_DUP_EXPERT 8u     /* an expert repeated within one token */
 #define DISPATCH_STATUS_BAD_COUNT 16u     /* expand: a recv_count outside [0, rows_per_source] */
+#define DISPATCH_STATUS_TIMEOUT 32u       /* one-launch layout: a tile's bounded wait for the other
+                                             tiles ran out (a guard, see dispatch_set_wait_limit);
+                                             slot maps, inverse maps and rows are unspecified */
 
 /* Output selection for dispatch_scatter. */
 #define DISPATCH_RANK_CONTIG 1u  /* write rank_x (and rank_sf) */
@@ -129,11 +134,14 @@ int dispatch_abi_version(void);
 /* Static, human-readable text for a host error code. Never NULL. */
 const char* dispatch_strerror(int code);
 
-/* Bytes of device workspace dispatch_layout needs for this problem (T, K, E,
- * R are read). The workspace must be 256-byte aligned. It holds per-tile
- * histograms that each call rewrites before reading, so it needs no clearing,
- * before the first call or between calls; it carries nothing from one call to
- * the next. */
+/* Bytes of device workspace the dispatch layout calls need for this problem
+ * (T, K, E, R are read). The workspace must be 256-byte aligned and
+ * zero-filled before its first use (hipMemset to 0 once). It holds per-tile
+ * histograms, which each call rewrites before reading, and the words through
+ * which the tiles of a one-launch layout exchange their key counts (section
+ * 4.5's cross-tile merge): every call leaves those zero again when it ends,
+ * so a workspace stays ready for the next call of any problem that fits it.
+ * Nothing else in it is written by anything but these calls. */
 int dispatch_workspace_size(const dispatch_problem_t* problem, size_t* bytes);
 
 /* Worst-case row counts, for sizing outputs without reading the totals back:
@@ -146,12 +154,17 @@ int dispatch_max_rows(const dispatch_problem_t* problem, int64_t* max_recv_rows,
  * topk_idx: device [T, K] row-major of problem->topk_idx_bytes wide signed
  * integers; a negative entry is masked. Writes every field of `out` (counts
  * and psums always; slot and inverse maps when *status is 0). Needs
- * `workspace` of at least dispatch_workspace_size() bytes. */
+ * `workspace` of at least dispatch_workspace_size() bytes. A batch of up to
+ * 256 tiles is laid out by one kernel: each tile's workgroup ranks its pairs
+ * once, hands its key counts to the others through the workspace, waits for
+ * theirs (all tiles are resident together) and assigns its slots; larger
+ * batches take a count kernel and an assign kernel, or three kernels with a
+ * column scan (dispatch_kernel_count tells which). */
 int dispatch_layout(const dispatch_problem_t* problem, const void* topk_idx,
                     const dispatch_layout_t* out, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
-/* dispatch_layout, and while its kernels run, a read of the token rows x
+/* dispatch_layout, and while its kernel(s) run, a read of the token rows x
  * [T, row_bytes] (16-byte aligned) and of x_sf [T, S] (may be NULL) that
  * leaves them in the GPU's Infinity Cache for a dispatch_scatter of the same
  * rows that follows. The layout kernels are latency-bound and leave HBM
@@ -198,7 +211,7 @@ int dispatch_scatter(const dispatch_problem_t* problem, const dispatch_layout_t*
  * kernel: every workgroup ranks the whole batch itself, so none waits for
  * another, and each copies its share of the rows' 1 KB segments. That saves
  * one or two launches, the dominant cost of small (decode-sized) batches.
- * Larger batches run the layout and scatter kernels. */
+ * Larger batches run the layout kernel(s) and the scatter kernel. */
 int dispatch_layout_and_scatter(const dispatch_problem_t* problem, const void* topk_idx,
                                 const dispatch_layout_t* out, void* workspace, size_t workspace_bytes,
                                 const void* x, const float* x_sf, void* rank_x, float* rank_sf,
@@ -211,10 +224,10 @@ int dispatch_layout_and_scatter(const dispatch_problem_t* problem, const void* t
  * per GPU, held until the process ends); the call allocates nothing. A
  * problem whose dispatch_workspace_size() exceeds that size returns
  * DISPATCH_ERR_WORKSPACE before anything is enqueued; every other argument,
- * check and output is that of dispatch_layout_and_scatter. The array needs
- * no clearing, but calls that overlap in time on one GPU (concurrent
- * streams) share it and race: serialize them, or use
- * dispatch_layout_and_scatter with a workspace per stream. */
+ * check and output is that of dispatch_layout_and_scatter. The array starts
+ * zeroed and every call leaves it ready for the next, but calls that overlap
+ * in time on one GPU (concurrent streams) share it and race: serialize them,
+ * or use dispatch_layout_and_scatter with a workspace per stream. */
 #define DISPATCH_NOALLOC_WORKSPACE_BYTES 4194304 /* 4 MiB */
 int dispatch_layout_and_scatter_noalloc(const dispatch_problem_t* problem, const void* topk_idx,
                                         const dispatch_layout_t* out, const void* x, const float* x_sf,
@@ -223,12 +236,24 @@ int dispatch_layout_and_scatter_noalloc(const dispatch_problem_t* problem, const
 
 /* Kernels the calls above launch for this problem (its T, K, E, R and
  * row_bytes are read): *layout_kernels for dispatch_layout (1 when one tile
- * holds the batch, 2 with the tile histograms reduced in the assign kernel, 3
- * with the column scan) and *layout_and_scatter_kernels for
- * dispatch_layout_and_scatter (1 on its one-kernel path, else the layout's
- * kernels plus the scatter). Either pointer may be NULL. */
+ * holds the batch or its tiles exchange their counts in one launch, 2 with
+ * the tile histograms reduced in an assign kernel, 3 with the column scan)
+ * and *layout_and_scatter_kernels for dispatch_layout_and_scatter (1 on its
+ * one-kernel path, else the layout's kernels plus the scatter). Either
+ * pointer may be NULL. */
 int dispatch_kernel_count(const dispatch_problem_t* problem, int* layout_kernels,
                           int* layout_and_scatter_kernels);
+
+/* Bound on the in-kernel wait of the one-launch layout, in polls of the
+ * other tiles' words (about a microsecond each). The tiles are the first
+ * workgroups of their launch and wait only for each other, so the wait ends
+ * without it; the bound is a guard, after which a tile writes nothing and the
+ * call reports DISPATCH_STATUS_TIMEOUT (its workspace stays ready for the
+ * next call). polls = 0 restores the default of 2^20; a small bound forces
+ * the timeout path, for tests. A process-wide setting read when a call is
+ * enqueued; returns DISPATCH_ERR_ARG for a negative bound. */
+#define DISPATCH_DEFAULT_WAIT_LIMIT 1048576
+int dispatch_set_wait_limit(int64_t polls);
 
 /* ---------------------------------------------------------------------------
  * Receiver-side expand (the page's copy epilogue: sections 3, 6.4, 8.2, 8.3

@@ -17,5 +17,5 @@ from ._binding import (  # noqa: F401
     dispatch_strerror, dispatch_workspace_size, load_library, make_problem, STATUS_BAD_COUNT, ExpandProblem, ExpandLayoutTensors, make_expand_problem,
     dispatch_expand_workspace_size, alloc_expand_layout, alloc_expand_workspace, dispatch_expand_layout,
     dispatch_expand_scatter, dispatch_expand_layout_and_scatter, ExpandPlan, CombineProblem, dispatch_combine,
-    CombinePlan,
+    CombinePlan, STATUS_TIMEOUT, DEFAULT_WAIT_LIMIT, dispatch_set_wait_limit,
 )

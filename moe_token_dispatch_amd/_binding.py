@@ -17,7 +17,7 @@ import torch  # load torch's HIP runtime first so the library binds to the same 
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_dispatch.so")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 MAX_TOPK = 32
 MAX_EXPERTS = 4096
 MAX_RANKS = 1024
@@ -34,6 +34,8 @@ STATUS_RECV_OVERFLOW = 2
 STATUS_RANK_OVERFLOW = 4
 STATUS_DUP_EXPERT = 8
 STATUS_BAD_COUNT = 16
+STATUS_TIMEOUT = 32
+DEFAULT_WAIT_LIMIT = 1 << 20
 
 RANK_CONTIG = 1
 EXPERT_MAJOR = 2
@@ -112,7 +114,7 @@ _LIB = None
 SYMBOLS = ("dispatch_abi_version", "dispatch_strerror", "dispatch_workspace_size",
            "dispatch_max_rows", "dispatch_layout", "dispatch_layout_read_ahead",
            "dispatch_scatter", "dispatch_layout_and_scatter", "dispatch_layout_and_scatter_noalloc",
-           "dispatch_kernel_count",
+           "dispatch_kernel_count", "dispatch_set_wait_limit",
            "dispatch_expand_workspace_size", "dispatch_expand_max_rows", "dispatch_expand_layout",
            "dispatch_expand_scatter", "dispatch_expand_layout_and_scatter", "dispatch_combine")
 
@@ -150,6 +152,8 @@ def load_library(path: str = LIB_PATH):
     lib.dispatch_layout_and_scatter_noalloc.restype = i
     lib.dispatch_kernel_count.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(i), ctypes.POINTER(i)]
     lib.dispatch_kernel_count.restype = i
+    lib.dispatch_set_wait_limit.argtypes = [ctypes.c_int64]
+    lib.dispatch_set_wait_limit.restype = i
     ep = ctypes.POINTER(ExpandProblem)
     lib.dispatch_expand_workspace_size.argtypes = [ep, ctypes.POINTER(sz)]
     lib.dispatch_expand_workspace_size.restype = i
@@ -377,6 +381,13 @@ def dispatch_kernel_count(problem: Problem) -> tuple:
     return lay.value, both.value
 
 
+def dispatch_set_wait_limit(polls: int) -> None:
+    """Bound the one-launch layout's in-kernel wait to `polls` polls (0: the default); process-wide."""
+    rc = load_library().dispatch_set_wait_limit(int(polls))
+    if rc:
+        raise DispatchError(rc, "dispatch_set_wait_limit")
+
+
 def dispatch_layout_and_scatter(problem: Problem, topk_idx: torch.Tensor, out: LayoutTensors,
                                 workspace: torch.Tensor, x: torch.Tensor, x_sf: Optional[torch.Tensor],
                                 rank_x: Optional[torch.Tensor], rank_sf: Optional[torch.Tensor],
@@ -469,9 +480,10 @@ def alloc_layout(problem: Problem, device) -> LayoutTensors:
 
 
 def alloc_workspace(problem: Problem, device) -> torch.Tensor:
-    """Workspace for dispatch_layout (needs no clearing; torch allocations are 256-byte aligned)."""
+    """Workspace for the layout calls: zero-filled, as its first use requires (torch allocations are
+    256-byte aligned)."""
     n = dispatch_workspace_size(problem)
-    return torch.empty((n + 255) // 256 * 256, dtype=torch.uint8, device=device)
+    return torch.zeros((n + 255) // 256 * 256, dtype=torch.uint8, device=device)
 
 
 @dataclasses.dataclass

@@ -3,6 +3,7 @@
 // rejected call leaves the stream and all buffers untouched.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "dispatch_common.hpp"
@@ -11,6 +12,8 @@
 using moe_dispatch::TileGeometry;
 
 namespace {
+
+std::atomic<int64_t> g_wait_limit{DISPATCH_DEFAULT_WAIT_LIMIT};
 
 bool aligned_to(const void* ptr, uintptr_t bytes) { return (reinterpret_cast<uintptr_t>(ptr) % bytes) == 0; }
 
@@ -173,9 +176,17 @@ int check_expand_layout_args(const dispatch_expand_problem_t* problem, const voi
 
 }  // namespace
 
+int64_t moe_dispatch::exchange_wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
+
 extern "C" {
 
 int dispatch_abi_version(void) { return DISPATCH_ABI_VERSION; }
+
+int dispatch_set_wait_limit(int64_t polls) {
+    if (polls < 0) return DISPATCH_ERR_ARG;
+    g_wait_limit.store(polls == 0 ? DISPATCH_DEFAULT_WAIT_LIMIT : polls, std::memory_order_relaxed);
+    return DISPATCH_OK;
+}
 
 const char* dispatch_strerror(int code) {
     switch (code) {
@@ -215,9 +226,11 @@ int dispatch_layout(const dispatch_problem_t* problem, const void* topk_idx, con
     TileGeometry g;
     const int rc = check_layout_args(problem, topk_idx, out, workspace, workspace_bytes, &g);
     if (rc != DISPATCH_OK) return rc;
-    if (moe_dispatch::launch_layout(*problem, g, topk_idx, *out, workspace, stream) != hipSuccess)
-        return DISPATCH_ERR_HIP;
-    return DISPATCH_OK;
+    const hipError_t err = moe_dispatch::exchange_layout_fits(*problem, g)
+                               ? moe_dispatch::launch_exchange_layout(*problem, g, topk_idx, *out, workspace, nullptr,
+                                                                      stream)
+                               : moe_dispatch::launch_layout(*problem, g, topk_idx, *out, workspace, stream);
+    return err == hipSuccess ? DISPATCH_OK : DISPATCH_ERR_HIP;
 }
 
 int dispatch_layout_read_ahead(const dispatch_problem_t* problem, const void* topk_idx, const dispatch_layout_t* out,
@@ -233,10 +246,11 @@ int dispatch_layout_read_ahead(const dispatch_problem_t* problem, const void* to
         return DISPATCH_ERR_ALIGN;
     moe_dispatch::ReadAhead ra{x, p.num_tokens * p.row_bytes, x_sf, p.num_tokens * p.sf_per_token};
     const bool read_ahead = moe_dispatch::read_ahead_fits(ra.x_bytes, ra.sf_words);
-    if (moe_dispatch::launch_layout(p, g, topk_idx, *out, workspace, stream, nullptr, read_ahead ? &ra : nullptr) !=
-        hipSuccess)
-        return DISPATCH_ERR_HIP;
-    return DISPATCH_OK;
+    const hipError_t err =
+        moe_dispatch::exchange_layout_fits(p, g)
+            ? moe_dispatch::launch_exchange_layout(p, g, topk_idx, *out, workspace, read_ahead ? &ra : nullptr, stream)
+            : moe_dispatch::launch_layout(p, g, topk_idx, *out, workspace, stream, nullptr, read_ahead ? &ra : nullptr);
+    return err == hipSuccess ? DISPATCH_OK : DISPATCH_ERR_HIP;
 }
 
 int dispatch_kernel_count(const dispatch_problem_t* problem, int* layout_kernels, int* layout_and_scatter_kernels) {
@@ -244,7 +258,9 @@ int dispatch_kernel_count(const dispatch_problem_t* problem, int* layout_kernels
     if (rc != DISPATCH_OK) return rc;
     const TileGeometry g = moe_dispatch::make_geometry(problem->num_tokens, problem->num_topk,
                                                        problem->num_experts, problem->num_ranks);
-    const int layout = g.num_tiles == 1 && !g.column_scan ? 1 : (g.column_scan ? 3 : 2);
+    const int layout = (g.num_tiles == 1 && !g.column_scan) || moe_dispatch::exchange_layout_fits(*problem, g)
+                           ? 1
+                           : (g.column_scan ? 3 : 2);
     if (layout_kernels) *layout_kernels = layout;
     if (layout_and_scatter_kernels)
         *layout_and_scatter_kernels = moe_dispatch::fused_shape(*problem, g).fits ? 1 : layout + 1;
@@ -275,8 +291,11 @@ int dispatch_layout_and_scatter(const dispatch_problem_t* problem, const void* t
     const bool read_ahead = moe_dispatch::read_ahead_fits(ra.x_bytes, ra.sf_words);
     dispatch_problem_t sp = p;
     if (read_ahead) sp.flags |= DISPATCH_ROWS_READ_AHEAD;
-    if (moe_dispatch::launch_layout(p, g, topk_idx, *out, workspace, stream, nullptr,
-                                    read_ahead ? &ra : nullptr) != hipSuccess ||
+    const bool exchange = moe_dispatch::exchange_layout_fits(p, g);
+    if ((exchange ? moe_dispatch::launch_exchange_layout(p, g, topk_idx, *out, workspace, read_ahead ? &ra : nullptr,
+                                                         stream)
+                  : moe_dispatch::launch_layout(p, g, topk_idx, *out, workspace, stream, nullptr,
+                                                read_ahead ? &ra : nullptr)) != hipSuccess ||
         moe_dispatch::launch_scatter(sp, *out, x, x_sf, rank_x, rank_sf, recv_x, recv_sf, stream,
                                      has_few_destinations(p)) != hipSuccess)
         return DISPATCH_ERR_HIP;

@@ -55,8 +55,28 @@ struct TileGeometry {
     size_t ws_tile_prefix;
     size_t ws_totals;
     size_t ws_tile_err;
+    size_t ws_exchange;         // the one-launch layout's exchange region (see below): always at 0
+    int32_t exchange_words;     // 64-bit exchange words per tile (0: no one-launch layout)
     size_t ws_bytes;
 };
+
+// One-launch layout (exchange_layout_kernel): the tiles of one launch hand
+// their key counts to each other through 64-bit words in the workspace: per
+// tile, ceil(keys / 5) words of five 12-bit counts and one word of error
+// bits, each with bit 63 set once published. They live in a region of
+// kExchangeRegionWords words and a control word at the start of every
+// workspace (dispatch and expand alike), which no other kernel writes; the
+// words are zero between calls (each call clears the ones it used when it
+// ends), so a workspace must be zero-filled before its first use. Tiles
+// hold at most 4095 tokens (a count per key and tile fits 12 bits), and a
+// launch has at most kExchangeMaxTiles of them, all resident at once.
+constexpr int kExchangeCountsPerWord = 5;
+constexpr int kExchangeCountBits = 12;
+constexpr int kExchangeMaxTiles = 256;
+constexpr int64_t kExchangeRegionWords = 8192;
+constexpr size_t kExchangeRegionBytes = (size_t)(kExchangeRegionWords + 1) * sizeof(uint64_t);
+// The wait bound of the next one-launch layouts (dispatch_set_wait_limit).
+int64_t exchange_wait_limit();
 
 inline size_t round_up_256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -127,16 +147,24 @@ inline TileGeometry make_geometry(int64_t num_tokens, int32_t num_topk, int32_t 
     const int64_t tiles = (num_tokens + g.tokens_per_tile - 1) / g.tokens_per_tile;
     g.num_tiles = tiles < 1 ? 1 : (int32_t)tiles;
     const size_t table = round_up_256((size_t)g.num_tiles * (size_t)g.hist_stride * sizeof(int32_t));
-    g.ws_tile_hist = 0;
+    g.ws_exchange = 0;
+    g.ws_tile_hist = round_up_256(kExchangeRegionBytes);
     g.ws_tile_prefix = g.ws_tile_hist + table;
     g.ws_totals = g.ws_tile_prefix + table;
     g.ws_tile_err = g.ws_totals + round_up_256((size_t)g.num_keys * sizeof(int32_t));
     g.ws_bytes = g.ws_tile_err + round_up_256((size_t)g.num_tiles * sizeof(int32_t));
+    const int words = (g.num_keys + kExchangeCountsPerWord - 1) / kExchangeCountsPerWord + 1;
+    const bool exchange = !g.column_scan && g.num_tiles > 1 && g.num_tiles <= kExchangeMaxTiles &&
+                          g.tokens_per_tile < (1 << kExchangeCountBits) &&
+                          (int64_t)g.num_tiles * words <= kExchangeRegionWords;
+    g.exchange_words = exchange ? words : 0;
     return g;
 }
 
-// Workspace: tile_hist[num_tiles][hist_stride], tile_prefix[num_tiles][hist_stride],
-// totals[num_keys] and tile_err[num_tiles], int32, each 256-byte aligned.
+// Workspace: the exchange region (kExchangeRegionWords words and a control
+// word, uint64), then tile_hist[num_tiles][hist_stride],
+// tile_prefix[num_tiles][hist_stride], totals[num_keys] and
+// tile_err[num_tiles], int32, each 256-byte aligned.
 inline size_t workspace_bytes(const TileGeometry& g) { return g.ws_bytes; }
 
 // How the receiver-side expand sees its receive buffer through the layout
@@ -163,6 +191,18 @@ struct ReadAhead {
 constexpr int64_t kReadAheadMaxBytes = int64_t(160) << 20;
 constexpr int kReadAheadGroups = 256;     // read-ahead workgroups per layout kernel
 constexpr int kReadAheadCountPct = 35;    // percent of the rows the count kernel reads
+// Read-ahead workgroups of the one-launch layout, which reads all the rows:
+// about 512 KB each, at least 128 and at most 512 of them. Measured on
+// MI355X (flushed steps): 59 MB of rows read fastest by 128-160 workgroups
+// (512: 2 us slower, 64: 6 us slower), 134 MB by 256 (128 or 512: 5 us slower).
+constexpr int64_t kExchangeReadAheadBytesPerGroup = int64_t(512) << 10;
+constexpr int kExchangeReadAheadMinGroups = 128;
+constexpr int kExchangeReadAheadMaxGroups = 512;
+inline int exchange_read_ahead_groups(int64_t bytes) {
+    const int64_t g = (bytes + kExchangeReadAheadBytesPerGroup - 1) / kExchangeReadAheadBytesPerGroup;
+    return g < kExchangeReadAheadMinGroups ? kExchangeReadAheadMinGroups
+                                           : (g > kExchangeReadAheadMaxGroups ? kExchangeReadAheadMaxGroups : (int)g);
+}
 inline bool read_ahead_fits(int64_t x_bytes, int64_t sf_words) {
     return x_bytes + 4 * sf_words <= kReadAheadMaxBytes;
 }
@@ -269,6 +309,15 @@ hipError_t launch_fused_dispatch(const dispatch_problem_t& p, const TileGeometry
                                  const dispatch_layout_t& out, void* workspace, const void* x, const float* x_sf,
                                  void* rank_x, float* rank_sf, void* recv_x, float* recv_sf, hipStream_t stream,
                                  const ExpandView* expand = nullptr);
+// The one-launch layout of a dispatch: tiles that rank their pairs once,
+// exchange their key counts through the workspace and assign their slots;
+// with a read-ahead, the launch's other workgroups read the token rows
+// ahead. exchange_layout_fits() tells whether a problem's geometry takes it;
+// the outputs equal launch_layout's.
+bool exchange_layout_fits(const dispatch_problem_t& p, const TileGeometry& g);
+hipError_t launch_exchange_layout(const dispatch_problem_t& p, const TileGeometry& g, const void* topk_idx,
+                                  const dispatch_layout_t& out, void* workspace, const ReadAhead* read_ahead,
+                                  hipStream_t stream);
 hipError_t launch_combine(int64_t num_tokens, int32_t num_topk, int64_t row_bytes, int64_t expert_rows,
                           const int32_t* expert_slot, const float* weights, const void* y, void* out,
                           hipStream_t stream);

@@ -60,6 +60,8 @@ struct LayoutParams {
     int32_t num_keys;
     int32_t hist_stride;  // ints per histogram row (num_keys padded to a multiple of 4)
     int32_t num_tiles;
+    int32_t exchange_words;  // one-launch layout: exchange words per tile
+    int64_t wait_limit;      // one-launch layout: polls before a tile gives up
     // Receiver-side expand only: the table is a fixed-stride receive buffer
     // of rows_per_source rows per source, source s holding recv_count[s]
     // rows; its expert ids are global, this receiver owns
@@ -245,6 +247,8 @@ struct Workspace {
     int32_t* tile_prefix;  // [num_tiles][hist_stride] pairs of the key in earlier tiles
     int32_t* totals;       // [num_keys]
     int32_t* tile_err;     // [num_tiles] DISPATCH_STATUS_* bits seen by the tile
+    uint64_t* exchange;      // one-launch layout: [num_tiles][exchange_words] words of the exchange region
+    uint64_t* exchange_ctl;  // its control word
 };
 
 // Read-ahead of the token rows while the layout runs. The layout kernels
@@ -397,6 +401,39 @@ struct RowArgs {
     int32_t write_expert;     // recv_x / recv_sf requested
     int32_t zero_pad;         // pad rows of recv_x / recv_sf zeroed
 };
+
+// Alignment pads of recv_src_token_idx (section 7.3): the slots after an
+// expert's routed rows up to its aligned end map to no token. The experts
+// are read 64 at a time, one per lane, and the ones with pad slots are
+// shared out: the layout_groups workgroups' wavefronts are split evenly over
+// the groups of 64 experts (or take several groups each when there are fewer
+// wavefronts than groups), and wavefront `sub` of a group takes every
+// per_group-th padded expert of it. All lanes then store that expert's
+// slots. first[] holds the exclusive psums, totals[] the expert counts.
+__device__ __forceinline__ void write_pad_entries(const LayoutParams& p, const int* first, const int* totals,
+                                                  int recv_rows, int layout_groups, int group, int wave, int lane,
+                                                  int nwaves, const dispatch_layout_t& out) {
+    const int E = p.num_experts;
+    const int groups = (E + kWave - 1) / kWave;
+    const int stride = layout_groups * nwaves, me = group * nwaves + wave;
+    const int per_group = stride > groups ? stride / groups : 1;
+    const int sub = me % per_group;
+    for (int g = me / per_group; g < groups; g += stride / per_group) {
+        const int e = g * kWave + lane;
+        int lo = 0, hi = 0;
+        if (e < E) {
+            lo = first[e] + totals[e];
+            hi = (int)min((int64_t)(e + 1 < E ? first[e + 1] : recv_rows), p.recv_capacity);
+        }
+        const bool padded = hi > lo;
+        const int rank = __popcll(__ballot(padded) & ((1ull << lane) - 1ull));
+        for (uint64_t m = __ballot(padded && rank % per_group == sub); m != 0; m &= m - 1) {
+            const int i = __builtin_ctzll(m);
+            const int lo_i = __builtin_amdgcn_readlane(lo, i), hi_i = __builtin_amdgcn_readlane(hi, i);
+            for (int s = lo_i + lane; s < hi_i; s += kWave) out.recv_src_token_idx[s] = -1;
+        }
+    }
+}
 
 // Where assign_kernel takes each key's count in earlier tiles and in all tiles:
 enum AssignMode {
@@ -598,39 +635,14 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
         }
     }
 
-    // Alignment pads of recv_src_token_idx (section 7.3): the slots after an
-    // expert's routed rows up to its aligned end map to no token. The experts
-    // are read 64 at a time, one per lane, and the ones with pad slots are
-    // shared out: the grid's wavefronts are split evenly over the groups of
-    // 64 experts (or take several groups each when there are fewer
-    // wavefronts than groups), and wavefront `sub` of a group takes every
-    // per_group-th padded expert of it. All lanes then store that expert's
-    // slots. (One expert per wavefront loop step cost about 130 ns a step: 33
-    // us for a one-token layout over 256 experts, whose one tile has one
-    // wavefront; one group per wavefront left most wavefronts idle: 16 us
-    // for 257 tokens, against 11.)
-    if (p.alignment > 1) {
-        const int groups = (E + kWave - 1) / kWave;
-        const int layout_groups = FUSED ? (int)gridDim.x : p.num_tiles;  // read-ahead workgroups excluded
-        const int stride = layout_groups * nwaves, me = blockIdx.x * nwaves + wave;
-        const int per_group = stride > groups ? stride / groups : 1;
-        const int sub = me % per_group;
-        for (int g = me / per_group; g < groups; g += stride / per_group) {
-            const int e = g * kWave + lane;
-            int lo = 0, hi = 0;
-            if (e < E) {
-                lo = first[e] + totals[e];
-                hi = (int)min((int64_t)(e + 1 < E ? first[e + 1] : recv_rows), p.recv_capacity);
-            }
-            const bool padded = hi > lo;
-            const int rank = __popcll(__ballot(padded) & ((1ull << lane) - 1ull));
-            for (uint64_t m = __ballot(padded && rank % per_group == sub); m != 0; m &= m - 1) {
-                const int i = __builtin_ctzll(m);
-                const int lo_i = __builtin_amdgcn_readlane(lo, i), hi_i = __builtin_amdgcn_readlane(hi, i);
-                for (int s = lo_i + lane; s < hi_i; s += kWave) out.recv_src_token_idx[s] = -1;
-            }
-        }
-    }
+    // Alignment pads of recv_src_token_idx, spread over the layout's
+    // wavefronts. (One expert per wavefront loop step cost about 130 ns a
+    // step: 33 us for a one-token layout over 256 experts, whose one tile has
+    // one wavefront; one group of 64 experts per wavefront left most
+    // wavefronts idle: 16 us for 257 tokens, against 11.)
+    if (p.alignment > 1)
+        write_pad_entries(p, first, totals, recv_rows, FUSED ? (int)gridDim.x : p.num_tiles, blockIdx.x, wave, lane,
+                          nwaves, out);
     if constexpr (FUSED) {
         // The row copies of this workgroup's tokens (sections 6.3 and 8.2),
         // bitwise, each row read once: every thread takes 16-byte vectors of
@@ -708,6 +720,246 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
                 }
             }
         }
+    }
+}
+
+// One-launch layout: Count, Prefix Sum and the slot assignment of a batch of
+// several tiles in a single kernel, for the combined call. Workgroup `tile`
+// ranks its tile's pairs once (rank_chunk), keeping each pair's place in
+// registers, and publishes the tile's key counts and error bits as exchange
+// words: relaxed agent-scope atomic stores with bit 63 set. It then reads
+// every tile's words until all of them are published (relaxed agent-scope
+// atomic loads; each word is written once per call and carries its own
+// "published" bit, so no ordering between locations is needed), summing the
+// key totals and the counts of earlier tiles as it reads, and assigns its
+// slots exactly as assign_kernel does. Workgroups past the tiles read the
+// token rows ahead, all of them.
+// The tiles are the first workgroups of the grid and wait on nothing but
+// each other, so all of them are resident while they wait (the wait is
+// bounded all the same: a tile that gives up writes nothing and the call
+// reports DISPATCH_STATUS_TIMEOUT). Every tile ends with one atomic add on
+// the control word (finished tiles, tiles that gave up, tile 0's status
+// bits); the last one writes the status and clears the words and the control
+// word, so the next call finds them zero.
+constexpr uint64_t kPublished = uint64_t(1) << 63;
+constexpr uint64_t kCountMask = (uint64_t(1) << kExchangeCountBits) - 1;
+constexpr int kExchangeBatch = 16;  // exchange words a thread loads before it waits
+
+template <int CH, typename IdxT>
+__global__ void __launch_bounds__(kLayoutThreads)
+exchange_layout_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispatch_layout_t out) {
+    if ((int)blockIdx.x >= p.num_tiles) {  // a read-ahead workgroup
+        read_ahead(p, blockIdx.x - p.num_tiles);
+        return;
+    }
+    // LDS: [W][num_keys] wavefront counters, then totals[num_keys] and first[num_keys].
+    extern __shared__ int lds[];
+    __shared__ int scratch[2 * (kLayoutThreads / kWave + 1)];
+    __shared__ uint32_t block_err;
+    __shared__ int last_tile;
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int nthreads = blockDim.x, nwaves = nthreads / kWave, nkeys = p.num_keys;
+    const int K = p.num_topk, E = p.num_experts, R = p.num_ranks;
+    const int tile = blockIdx.x;
+    int* counters = lds + wave * nkeys;
+    int* totals = lds + nwaves * nkeys;  // per key, over all tiles
+    int* first = totals + nkeys;         // per key: pairs in earlier tiles, then the first slot
+    const int token_in_chunk = lane / K;
+    const int k = lane - token_in_chunk * K;
+    const int64_t wave_tok0 = (int64_t)tile * p.tokens_per_tile + (int64_t)wave * p.tokens_per_wave;
+    int64_t entry[CH];
+    uint32_t err = 0;
+    load_entries<CH, false>(topk, wave_tok0, token_in_chunk, k, p, entry, err);
+    for (int i = lane; i < nkeys; i += kWave) counters[i] = 0;
+    for (int j = tid; j < nkeys; j += nthreads) {
+        totals[j] = 0;
+        first[j] = 0;
+    }
+    if (tid == 0) block_err = 0;
+    __syncthreads();
+
+    PairPos pos[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) pos[c] = rank_chunk(entry[c], lane, token_in_chunk, p, counters, err);
+    {
+        uint32_t wave_err = 0;
+        for (uint32_t bit = 1; bit <= DISPATCH_STATUS_BAD_COUNT; bit <<= 1)
+            if (__ballot((err & bit) != 0)) wave_err |= bit;
+        if (lane == 0 && wave_err) atomicOr(&block_err, wave_err);
+    }
+    __syncthreads();
+
+    // Publish the tile's count of every key (its wavefronts' counters
+    // summed), kExchangeCountsPerWord to a word, then its error bits.
+    const int wpt = p.exchange_words;
+    const int qwords = wpt - 1;
+    uint64_t* mine = ws.exchange + (int64_t)tile * wpt;
+    for (int q = tid; q < wpt; q += nthreads) {
+        uint64_t v = kPublished;
+        if (q < qwords) {
+            for (int c = 0; c < kExchangeCountsPerWord; ++c) {
+                const int j = q * kExchangeCountsPerWord + c;
+                if (j >= nkeys) break;
+                int sum = 0;
+                for (int w = 0; w < nwaves; ++w) sum += lds[w * nkeys + j];
+                v |= ((uint64_t)sum & kCountMask) << (c * kExchangeCountBits);
+            }
+        } else {
+            v |= block_err;
+        }
+        __hip_atomic_store(mine + q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // Every tile's words, until all are published. While tiles are still
+    // missing, only their error words (each tile's last) are read, one word
+    // per tile a round; then every word: thread (q, g) sums count word q over
+    // tiles g, g + groups, ... (qwords <= threads per tile), the first
+    // threads also take the error words, and a round with any word missing
+    // is read again. Readiness is decided per word, never inferred from
+    // another word.
+    const int groups = nthreads / qwords;
+    const int q = tid % qwords, g = tid / qwords;
+    int tot[kExchangeCountsPerWord], bef[kExchangeCountsPerWord];
+    uint32_t errs = 0;
+    bool timed_out = false;
+    bool all_errs_seen = false;
+    for (int64_t poll = 0;; ++poll) {
+        if (poll == p.wait_limit) {
+            timed_out = true;
+            break;
+        }
+        if (!all_errs_seen) {
+            bool missing = false;
+            for (int i = tid; i < p.num_tiles; i += nthreads)
+                missing |= (__hip_atomic_load(ws.exchange + (int64_t)i * wpt + qwords, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT) &
+                            kPublished) == 0;
+            all_errs_seen = !__syncthreads_or(missing);
+            if (!all_errs_seen) {
+                __builtin_amdgcn_s_sleep(4);
+                continue;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kExchangeCountsPerWord; ++c) tot[c] = bef[c] = 0;
+        errs = 0;
+        bool missing = false;
+        if (g < groups) {
+            for (int i0 = g; i0 < p.num_tiles; i0 += groups * kExchangeBatch) {
+                uint64_t v[kExchangeBatch];
+#pragma unroll
+                for (int b = 0; b < kExchangeBatch; ++b) {
+                    const int i = i0 + b * groups;
+                    v[b] = i < p.num_tiles ? __hip_atomic_load(ws.exchange + (int64_t)i * wpt + q, __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_AGENT)
+                                           : kPublished;
+                }
+#pragma unroll
+                for (int b = 0; b < kExchangeBatch; ++b) {
+                    missing |= (v[b] & kPublished) == 0;
+                    const bool earlier = i0 + b * groups < tile;
+#pragma unroll
+                    for (int c = 0; c < kExchangeCountsPerWord; ++c) {
+                        const int n = (int)((v[b] >> (c * kExchangeCountBits)) & kCountMask);
+                        tot[c] += n;
+                        if (earlier) bef[c] += n;
+                    }
+                }
+            }
+        }
+        for (int i = tid; i < p.num_tiles; i += nthreads) {
+            const uint64_t v =
+                __hip_atomic_load(ws.exchange + (int64_t)i * wpt + qwords, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            missing |= (v & kPublished) == 0;
+            errs |= (uint32_t)v;
+        }
+        if (!__syncthreads_or(missing)) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+
+    uint32_t status = 0;
+    if (!timed_out) {
+        if (g < groups) {
+#pragma unroll
+            for (int c = 0; c < kExchangeCountsPerWord; ++c) {
+                const int j = q * kExchangeCountsPerWord + c;
+                if (j < nkeys && tot[c]) atomicAdd(&totals[j], tot[c]);
+                if (j < nkeys && bef[c]) atomicAdd(&first[j], bef[c]);
+            }
+        }
+        if (errs) atomicOr(&block_err, errs);
+        __syncthreads();
+        // Fold the earlier-tile pairs into the wavefront counters, then scan
+        // the totals into the exclusive psums (expert counts aligned up first).
+        for (int j = tid; j < nkeys; j += nthreads) {
+            int run = first[j];
+            for (int w = 0; w < nwaves; ++w) {
+                const int c = lds[w * nkeys + j];
+                lds[w * nkeys + j] = run;
+                run += c;
+            }
+        }
+        const int2 row_totals = block_exclusive_scan2(totals, first, E, nkeys, p.alignment, scratch);
+        const int recv_rows = row_totals.x, rank_rows = row_totals.y;
+        status = block_err;
+        if (recv_rows > p.recv_capacity) status |= DISPATCH_STATUS_RECV_OVERFLOW;
+        if (rank_rows > p.rank_capacity) status |= DISPATCH_STATUS_RANK_OVERFLOW;
+        if (tile == 0) {
+            for (int j = tid; j < nkeys; j += nthreads) {
+                if (j < E) {
+                    out.expert_count[j] = totals[j];
+                    out.expert_psum[j] = first[j];
+                } else {
+                    out.rank_count[j - E] = totals[j];
+                    out.rank_psum[j - E] = first[j];
+                }
+            }
+            if (status == 0 && out.expert_count_cumulative)
+                for (int j = tid; j < E; j += nthreads) atomicAdd(&out.expert_count_cumulative[j], totals[j]);
+            if (tid == 0) {
+                out.expert_psum[E] = recv_rows;
+                out.rank_psum[R] = rank_rows;
+            }
+        }
+        if (status == 0) {
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int64_t tok = wave_tok0 + (int64_t)c * p.tokens_per_chunk + token_in_chunk;
+                if (token_in_chunk >= p.tokens_per_chunk || tok >= p.num_tokens) continue;
+                const int e = pos[c].expert, r = pos[c].rank;
+                const int es = e >= 0 ? first[e] + counters[e] + pos[c].expert_pos : -1;
+                const int rs = r >= 0 ? first[E + r] + counters[E + r] + pos[c].rank_pos : -1;
+                out.expert_slot[tok * K + k] = es;
+                if (es >= 0 && es < p.recv_capacity) out.recv_src_token_idx[es] = (int32_t)tok;
+                out.rank_slot[tok * K + k] = rs;
+                if (rs >= 0 && rs < p.rank_capacity) out.rank_src_token_idx[rs] = (int32_t)tok;
+            }
+            if (p.alignment > 1)
+                write_pad_entries(p, first, totals, recv_rows, p.num_tiles, tile, wave, lane, nwaves, out);
+        }
+    }
+
+    // Done: count the tile in the control word; the last tile writes the
+    // status and clears the exchange for the next call.
+    if (tid == 0) {
+        uint64_t add = 1;                                         // bits [0, 24): tiles done
+        if (timed_out) add |= uint64_t(1) << 24;                  // bits [24, 48): tiles that gave up
+        else if (tile == 0) add |= (uint64_t)(status & 0xffffu) << 48;  // bits [48, 64): the status
+        const uint64_t old = __hip_atomic_fetch_add(ws.exchange_ctl, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_tile = (int)((old & 0xffffffu) + 1 == (uint64_t)p.num_tiles);
+        if (last_tile) {
+            const uint64_t all = old + add;
+            uint32_t st = (uint32_t)(all >> 48);
+            if ((all >> 24) & 0xffffffu) st |= DISPATCH_STATUS_TIMEOUT;
+            *out.status = (int32_t)st;
+        }
+    }
+    __syncthreads();
+    if (last_tile) {
+        const int64_t words = (int64_t)p.num_tiles * wpt;
+        for (int64_t i = tid; i < words; i += nthreads) ws.exchange[i] = 0;
+        if (tid == 0) *ws.exchange_ctl = 0;
     }
 }
 
@@ -816,6 +1068,7 @@ LayoutParams make_params(const dispatch_problem_t& prob, const TileGeometry& g) 
     p.num_keys = g.num_keys;
     p.hist_stride = g.hist_stride;
     p.num_tiles = g.num_tiles;
+    p.exchange_words = g.exchange_words;
     return p;
 }
 
@@ -826,6 +1079,8 @@ Workspace make_workspace(const TileGeometry& g, void* workspace) {
     ws.tile_prefix = reinterpret_cast<int32_t*>(base + g.ws_tile_prefix);
     ws.totals = reinterpret_cast<int32_t*>(base + g.ws_totals);
     ws.tile_err = reinterpret_cast<int32_t*>(base + g.ws_tile_err);
+    ws.exchange = reinterpret_cast<uint64_t*>(base + g.ws_exchange);
+    ws.exchange_ctl = ws.exchange + kExchangeRegionWords;
     return ws;
 }
 
@@ -913,6 +1168,60 @@ hipError_t launch_fused_dispatch(const dispatch_problem_t& prob, const TileGeome
     const bool wide = prob.topk_idx_bytes == 8;
     if (expand != nullptr) return launch_fused_chunks<true>(wide, p, tile, topk_idx, out, ws, rows, f, stream);
     return launch_fused_chunks<false>(wide, p, tile, topk_idx, out, ws, rows, f, stream);
+}
+
+namespace {
+
+template <int CH, typename IdxT>
+hipError_t launch_exchange_typed(const LayoutParams& p, const TileGeometry& g, const void* topk,
+                                 const dispatch_layout_t& out, const Workspace& ws, hipStream_t stream) {
+    const auto* idx = static_cast<const IdxT*>(topk);
+    LayoutParams pc = p;
+    Workspace wc = ws;
+    dispatch_layout_t oc = out;
+    void* args[] = {&idx, &pc, &wc, &oc};
+    const size_t lds = (size_t)(g.waves_per_tile + 2) * g.num_keys * sizeof(int);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&exchange_layout_kernel<CH, IdxT>),
+                           dim3((unsigned)(g.num_tiles + p.pf_groups)), dim3(g.waves_per_tile * kWave), args, lds,
+                           stream);
+}
+
+}  // namespace
+
+bool exchange_layout_fits(const dispatch_problem_t& prob, const TileGeometry& g) {
+    // Exchange room in the geometry, and a thread per count word of a tile.
+    return g.exchange_words > 0 && g.exchange_words - 1 <= g.waves_per_tile * kWave && prob.num_tokens > 0;
+}
+
+hipError_t launch_exchange_layout(const dispatch_problem_t& prob, const TileGeometry& g, const void* topk_idx,
+                                  const dispatch_layout_t& out, void* workspace, const ReadAhead* ra,
+                                  hipStream_t stream) {
+    if (!exchange_layout_fits(prob, g)) return hipErrorInvalidValue;
+    LayoutParams p = make_params(prob, g);
+    p.wait_limit = exchange_wait_limit();
+    if (ra != nullptr && (ra->x_bytes > 0 || ra->sf_words > 0)) {
+        p.pf_rows = static_cast<const u32x4*>(ra->x);
+        p.pf_sf = reinterpret_cast<const uint32_t*>(ra->x_sf);
+        p.pf_rows_lo = 0;
+        p.pf_rows_hi = ra->x != nullptr ? ra->x_bytes / 16 : 0;
+        p.pf_sf_lo = 0;
+        p.pf_sf_hi = ra->x_sf != nullptr ? ra->sf_words : 0;
+        p.pf_groups = exchange_read_ahead_groups(p.pf_rows_hi * 16 + p.pf_sf_hi * 4);
+    }
+    const Workspace ws = make_workspace(g, workspace);
+    const bool wide = prob.topk_idx_bytes == 8;
+#define MOE_DISPATCH_EXCHANGE_CASE(N)                                                      \
+    case N:                                                                                \
+        return wide ? launch_exchange_typed<N, int64_t>(p, g, topk_idx, out, ws, stream) \
+                    : launch_exchange_typed<N, int32_t>(p, g, topk_idx, out, ws, stream);
+    switch (g.chunks_per_wave) {
+        MOE_DISPATCH_EXCHANGE_CASE(1)
+        MOE_DISPATCH_EXCHANGE_CASE(2)
+        MOE_DISPATCH_EXCHANGE_CASE(4)
+        MOE_DISPATCH_EXCHANGE_CASE(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef MOE_DISPATCH_EXCHANGE_CASE
 }
 
 }  // namespace moe_dispatch

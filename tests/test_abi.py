@@ -36,18 +36,31 @@ def test_library_exports_every_declared_symbol():
 
 def test_binding_constants_match_header():
     d = _defines()
-    assert d["DISPATCH_ABI_VERSION"] == M.dispatch_abi_version() == 5
+    assert d["DISPATCH_ABI_VERSION"] == M.dispatch_abi_version() == 6
     assert (d["DISPATCH_ERR_NULL"], d["DISPATCH_ERR_ARG"], d["DISPATCH_ERR_ALIGN"],
             d["DISPATCH_ERR_WORKSPACE"], d["DISPATCH_ERR_HIP"]) == (
         M.ERR_NULL, M.ERR_ARG, M.ERR_ALIGN, M.ERR_WORKSPACE, M.ERR_HIP)
     assert (d["DISPATCH_STATUS_BAD_EXPERT"], d["DISPATCH_STATUS_RECV_OVERFLOW"],
-            d["DISPATCH_STATUS_RANK_OVERFLOW"], d["DISPATCH_STATUS_DUP_EXPERT"]) == (
-        M.STATUS_BAD_EXPERT, M.STATUS_RECV_OVERFLOW, M.STATUS_RANK_OVERFLOW, M.STATUS_DUP_EXPERT)
+            d["DISPATCH_STATUS_RANK_OVERFLOW"], d["DISPATCH_STATUS_DUP_EXPERT"], d["DISPATCH_STATUS_BAD_COUNT"],
+            d["DISPATCH_STATUS_TIMEOUT"]) == (
+        M.STATUS_BAD_EXPERT, M.STATUS_RECV_OVERFLOW, M.STATUS_RANK_OVERFLOW, M.STATUS_DUP_EXPERT,
+        M.STATUS_BAD_COUNT, M.STATUS_TIMEOUT)
+    assert d["DISPATCH_DEFAULT_WAIT_LIMIT"] == M.DEFAULT_WAIT_LIMIT
     assert (d["DISPATCH_RANK_CONTIG"], d["DISPATCH_EXPERT_MAJOR"], d["DISPATCH_ZERO_PAD"],
             d["DISPATCH_ROWS_READ_AHEAD"]) == (M.RANK_CONTIG, M.EXPERT_MAJOR, M.ZERO_PAD, M.ROWS_READ_AHEAD)
     assert d["DISPATCH_MAX_TOPK"] == M.MAX_TOPK and d["DISPATCH_MAX_EXPERTS"] == M.MAX_EXPERTS
     assert d["DISPATCH_MAX_RANKS"] == M.MAX_RANKS
     assert ctypes.sizeof(M.Problem) == 64 and ctypes.sizeof(M.LayoutPtrs) == 10 * 8
+
+
+def test_wait_limit_setter():
+    """The in-kernel wait bound: a negative bound is refused, 0 restores the default."""
+    lib = M.load_library()
+    assert lib.dispatch_set_wait_limit(-1) == M.ERR_ARG
+    assert lib.dispatch_set_wait_limit(5) == M.OK
+    assert lib.dispatch_set_wait_limit(0) == M.OK
+    with pytest.raises(M.DispatchError):
+        M.dispatch_set_wait_limit(-3)
 
 
 def test_strerror_covers_codes():
@@ -142,28 +155,35 @@ def test_host_errors_before_launch():
 
 
 def test_kernel_counts():
-    """The layout: one kernel for a one-tile batch, two with the histograms
-    reduced in the assign kernel, three with the column scan. The combined
-    call: one kernel up to 3072 (token, k) pairs (2048 when pad rows are
-    zeroed), else the layout's kernels and the scatter."""
+    """The layout: one kernel for a one-tile batch and for the one-launch
+    layout (several tiles that exchange their key counts: up to 256 tiles of
+    fewer than 4096 tokens, a thread per count word), else two with the
+    histograms reduced in the assign kernel, three with the column scan. The
+    combined call: one kernel up to 3072 (token, k) pairs (2048 when pad rows
+    are zeroed), else the layout's kernels and the scatter."""
     mk = M.make_problem
     assert M.dispatch_kernel_count(mk(256, 8, 256, 8, 1, row_bytes=14336)) == (1, 1)
     assert M.dispatch_kernel_count(mk(0, 8, 256, 8, 1, row_bytes=64)) == (1, 1)
     assert M.dispatch_kernel_count(mk(2048, 1, 64, 8, 1, row_bytes=48)) == (1, 1)
-    assert M.dispatch_kernel_count(mk(257, 8, 256, 8, 1, row_bytes=14336)) == (2, 1)
-    assert M.dispatch_kernel_count(mk(384, 8, 256, 8, 1, row_bytes=14336)) == (2, 1)
-    assert M.dispatch_kernel_count(mk(385, 8, 256, 8, 1, row_bytes=14336)) == (2, 3)
+    assert M.dispatch_kernel_count(mk(257, 8, 256, 8, 1, row_bytes=14336)) == (1, 1)
+    assert M.dispatch_kernel_count(mk(384, 8, 256, 8, 1, row_bytes=14336)) == (1, 1)
+    assert M.dispatch_kernel_count(mk(385, 8, 256, 8, 1, row_bytes=14336)) == (1, 2)
     assert M.dispatch_kernel_count(mk(256, 8, 256, 8, 128, row_bytes=7168, sf_per_token=56)) == (1, 1)
-    assert M.dispatch_kernel_count(mk(257, 8, 256, 8, 128, row_bytes=7168, sf_per_token=56)) == (2, 3)
-    assert M.dispatch_kernel_count(mk(384, 8, 256, 8, 2, row_bytes=64)) == (2, 3)
+    assert M.dispatch_kernel_count(mk(257, 8, 256, 8, 128, row_bytes=7168, sf_per_token=56)) == (1, 2)
+    assert M.dispatch_kernel_count(mk(384, 8, 256, 8, 2, row_bytes=64)) == (1, 2)
     # Without the zero-pad flag nothing is padded, and the 3072-pair limit holds.
     assert M.dispatch_kernel_count(mk(384, 8, 256, 8, 2, row_bytes=64,
-                                      flags=M.RANK_CONTIG | M.EXPERT_MAJOR)) == (2, 1)
-    assert M.dispatch_kernel_count(mk(3072, 1, 64, 8, 1, row_bytes=48)) == (2, 1)
-    assert M.dispatch_kernel_count(mk(4096, 8, 256, 8, 1, row_bytes=14336)) == (2, 3)
-    assert M.dispatch_kernel_count(mk(65536, 8, 256, 8, 128, row_bytes=7168, sf_per_token=56)) == (2, 3)
+                                      flags=M.RANK_CONTIG | M.EXPERT_MAJOR)) == (1, 1)
+    assert M.dispatch_kernel_count(mk(3072, 1, 64, 8, 1, row_bytes=48)) == (1, 1)
+    assert M.dispatch_kernel_count(mk(4096, 8, 256, 8, 1, row_bytes=14336)) == (1, 2)
+    assert M.dispatch_kernel_count(mk(16384, 8, 128, 16, 1, row_bytes=8192)) == (1, 2)
+    # 128 tiles of 16 wavefronts x 4 chunks (512 tokens each).
+    assert M.dispatch_kernel_count(mk(65536, 8, 256, 8, 128, row_bytes=7168, sf_per_token=56)) == (1, 2)
+    # 514 tiles of 16 wavefronts x 4 chunks: past the one-launch layout's 256 tiles.
+    assert M.dispatch_kernel_count(mk(257 * 1024, 8, 64, 8, 1, row_bytes=16)) == (2, 3)
     assert M.dispatch_kernel_count(mk(4096, 8, 4096, 1024, 1, row_bytes=64)) == (3, 4)
     assert M.dispatch_kernel_count(mk(80, 8, 4096, 1024, 1, row_bytes=64)) == (1, 1)
+    # 5120 keys: 1024 count words per tile, more than a 5-wavefront tile's threads.
     assert M.dispatch_kernel_count(mk(300, 8, 4096, 1024, 1, row_bytes=64)) == (2, 1)
     with pytest.raises(M.DispatchError):
         M.dispatch_kernel_count(M.Problem(10, 0, 8, 2, 1, 8, 0, 64, 100, 100, M.ALL_OUTPUTS, 0))

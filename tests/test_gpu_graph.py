@@ -22,14 +22,18 @@ from tests import gpu_harness as H
 pytestmark = pytest.mark.gpu
 
 
-# The layout and scatter calls on a batch of several tiles, and the combined
-# call on small batches, where it is one kernel. The last two: a small batch
-# over 256 experts at alignment 128, whose pad rows the scatter maps to row
-# blocks and the one kernel deals out in chunks.
+# The layout and scatter calls on a batch of several tiles (whose layout is
+# one launch that exchanges tile counts through the workspace: every replay
+# must leave the exchange words zero for the next), and the combined call on
+# small batches, where it is one kernel. Then a small batch over 256 experts
+# at alignment 128, whose pad rows the scatter maps to row blocks and the one
+# kernel deals out in chunks, and the combined call on several tiles (the
+# one-launch layout with its read-ahead, then the scatter).
 @pytest.mark.parametrize("dtype,with_sf,alignment,t,combined,experts", [
     ("bf16", False, 1, 1500, False, 64), ("fp8", True, 16, 1500, False, 64),
     ("bf16", False, 1, 200, True, 64), ("fp8", True, 16, 256, True, 64),
-    ("fp8", True, 128, 16, False, 256), ("fp8", True, 128, 16, True, 256)])
+    ("fp8", True, 128, 16, False, 256), ("fp8", True, 128, 16, True, 256),
+    ("bf16", False, 1, 1500, True, 64), ("fp8", True, 16, 1500, True, 64)])
 def test_captured_dispatch_replays_match_oracle(dtype, with_sf, alignment, t, combined, experts):
     print(f"\n[gpu-graph] capture dtype={dtype} sf={with_sf} A={alignment} T={t} combined={combined} E={experts}",
           flush=True)
@@ -64,7 +68,7 @@ def test_captured_dispatch_replays_match_oracle(dtype, with_sf, alignment, t, co
     out_d = torch.zeros((t, base.hidden), dtype=torch.bfloat16, device=H.DEVICE)
 
     if combined:
-        assert M.dispatch_kernel_count(prob)[1] == 1
+        assert M.dispatch_kernel_count(prob)[1] == (1 if t * k <= 2048 else 2)
 
     def step():
         if combined:

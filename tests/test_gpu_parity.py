@@ -99,25 +99,27 @@ def test_token_counts_around_tiles(t):
     _edge(_uniform(3, t, 8, 256, 0.05), 256, 8, 4)
 
 
-# Shapes on both sides of every layout geometry switch. Two launches while the
-# tile histograms (16-wavefront tiles, 1/2/4/8 chunks per wavefront) hold at
-# most 65536 ints, else a column scan over 4-wavefront tiles; very wide key
-# sets narrow the two-launch tiles to what LDS holds.
+# Shapes on both sides of every layout geometry switch. While the tile
+# histograms (16-wavefront tiles, 1/2/4/8 chunks per wavefront) hold at most
+# 65536 ints, the tiles either exchange their counts in one launch (up to 256
+# tiles whose exchange words fit the workspace's 8192-word region, a thread
+# per count word) or take two launches; beyond, a column scan over
+# 4-wavefront tiles. Very wide key sets narrow the tiles to what LDS holds.
 @pytest.mark.parametrize("t,k,e,r", [
     (31744, 8, 256, 8),     # two launches, 1 chunk per wavefront, 248 tiles (the largest)
-    (31745, 8, 256, 8),     # two launches, 2 chunks
-    (63489, 8, 256, 8),     # two launches, 4 chunks
-    (126977, 8, 256, 8),    # two launches, 8 chunks
+    (31745, 8, 256, 8),     # one launch, 2 chunks, 125 tiles
+    (63489, 8, 256, 8),     # one launch, 4 chunks
+    (126977, 8, 256, 8),    # one launch, 8 chunks
     (253952, 8, 256, 8),    # two launches, 8 chunks, 248 tiles
     (253953, 8, 256, 8),    # column scan, 8 chunks per wavefront
-    (768, 8, 4096, 1024),   # two launches, 5-wavefront tiles of 2 chunks
+    (768, 8, 4096, 1024),   # two launches, 5-wavefront tiles of 2 chunks (1025 words per tile)
     (3840, 8, 4096, 1024),  # two launches, 5-wavefront tiles of 8 chunks, 12 tiles (the largest)
     (3841, 8, 4096, 1024),  # column scan, 1 chunk
     (20000, 8, 4096, 1024), # column scan, 2 chunks
     (40000, 8, 4096, 1024), # column scan, 4 chunks
-    (6000, 8, 2048, 1024),  # two launches, 11-wavefront tiles of 4 chunks
-    (769, 8, 4096, 64),     # two launches, 7-wavefront tiles
-    (70000, 2, 512, 16),    # two launches, top-2: 32 tokens per chunk
+    (6000, 8, 2048, 1024),  # two launches, 11-wavefront tiles of 4 chunks (18 x 615 exchange words: past the region)
+    (769, 8, 4096, 64),     # two launches, 7-wavefront tiles (833 words per tile)
+    (70000, 2, 512, 16),    # one launch, top-2: 32 tokens per chunk
 ])
 def test_layout_geometry_paths(t, k, e, r):
     _banner(f"geometry T={t} K={k} E={e} R={r}")
