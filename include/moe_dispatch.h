@@ -140,8 +140,8 @@ const char* dispatch_strerror(int code);
  * histograms, which each call rewrites before reading, and the words through
  * which the tiles of a one-launch layout exchange their key counts (section
  * 4.5's cross-tile merge): every call leaves those zero again when it ends,
- * so a workspace stays ready for the next call of any problem that fits it.
- * Nothing else in it is written by anything but these calls. */
+ * so a workspace stays ready for the next call of any problem that fits it,
+ * dispatch or expand. Nothing else may write into it. */
 int dispatch_workspace_size(const dispatch_problem_t* problem, size_t* bytes);
 
 /* Worst-case row counts, for sizing outputs without reading the totals back:
@@ -154,17 +154,14 @@ int dispatch_max_rows(const dispatch_problem_t* problem, int64_t* max_recv_rows,
  * topk_idx: device [T, K] row-major of problem->topk_idx_bytes wide signed
  * integers; a negative entry is masked. Writes every field of `out` (counts
  * and psums always; slot and inverse maps when *status is 0). Needs
- * `workspace` of at least dispatch_workspace_size() bytes. A batch of up to
- * 256 tiles is laid out by one kernel: each tile's workgroup ranks its pairs
- * once, hands its key counts to the others through the workspace, waits for
- * theirs (all tiles are resident together) and assigns its slots; larger
- * batches take a count kernel and an assign kernel, or three kernels with a
- * column scan (dispatch_kernel_count tells which). */
+ * `workspace` of at least dispatch_workspace_size() bytes. A batch of one
+ * tile takes one kernel, larger batches a count kernel and an assign kernel,
+ * or three kernels with a column scan (dispatch_kernel_count tells which). */
 int dispatch_layout(const dispatch_problem_t* problem, const void* topk_idx,
                     const dispatch_layout_t* out, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
-/* dispatch_layout, and while its kernel(s) run, a read of the token rows x
+/* dispatch_layout, and while it runs, a read of the token rows x
  * [T, row_bytes] (16-byte aligned) and of x_sf [T, S] (may be NULL) that
  * leaves them in the GPU's Infinity Cache for a dispatch_scatter of the same
  * rows that follows. The layout kernels are latency-bound and leave HBM
@@ -173,7 +170,12 @@ int dispatch_layout(const dispatch_problem_t* problem, const void* topk_idx,
  * interleave HBM reads into that write stream. Rows and scale factors of
  * more than 160 MB together are not read (they would push their own first
  * rows out of the 256 MB cache). The scatter that follows is told so by
- * DISPATCH_ROWS_READ_AHEAD in its problem's flags. Outputs, checks and
+ * DISPATCH_ROWS_READ_AHEAD in its problem's flags. Rows that are read ahead
+ * let a batch of up to 256 tiles be laid out in one launch: each tile's
+ * workgroup ranks its pairs once, hands its key counts to the others
+ * through the workspace, waits for theirs (all tiles are resident together;
+ * the wait is bounded, see dispatch_set_wait_limit) and assigns its slots,
+ * while the launch's other workgroups read the rows. Outputs, checks and
  * errors are those of
  * dispatch_layout, plus DISPATCH_ERR_ALIGN for a misaligned x or x_sf;
  * nothing beyond the layout outputs is written. (Not a step of the page's
@@ -234,17 +236,18 @@ int dispatch_layout_and_scatter_noalloc(const dispatch_problem_t* problem, const
                                         void* rank_x, float* rank_sf, void* recv_x, float* recv_sf,
                                         hipStream_t stream);
 
-/* Kernels the calls above launch for this problem (its T, K, E, R and
- * row_bytes are read): *layout_kernels for dispatch_layout (1 when one tile
- * holds the batch or its tiles exchange their counts in one launch, 2 with
- * the tile histograms reduced in an assign kernel, 3 with the column scan)
- * and *layout_and_scatter_kernels for dispatch_layout_and_scatter (1 on its
- * one-kernel path, else the layout's kernels plus the scatter). Either
- * pointer may be NULL. */
+/* Kernels the calls above launch for this problem (its T, K, E, R,
+ * row_bytes and S are read): *layout_kernels for dispatch_layout (1 when one
+ * tile holds the batch, 2 with the tile histograms reduced in an assign
+ * kernel, 3 with the column scan) and *layout_and_scatter_kernels for
+ * dispatch_layout_and_scatter (1 on its one-kernel path; 2 when its layout,
+ * reading the rows ahead, is one launch; else the layout's kernels plus the
+ * scatter). Either pointer may be NULL. */
 int dispatch_kernel_count(const dispatch_problem_t* problem, int* layout_kernels,
                           int* layout_and_scatter_kernels);
 
-/* Bound on the in-kernel wait of the one-launch layout, in polls of the
+/* Bound on the in-kernel wait of the one-launch layout (the layout of
+ * dispatch_layout_read_ahead and dispatch_layout_and_scatter), in polls of the
  * other tiles' words (about a microsecond each). The tiles are the first
  * workgroups of their launch and wait only for each other, so the wait ends
  * without it; the bound is a guard, after which a tile writes nothing and the
@@ -280,7 +283,10 @@ typedef struct dispatch_expand_problem {
     int64_t recv_capacity_rows; /* rows of the expert-major output */
 } dispatch_expand_problem_t;
 
-/* Workspace bytes for dispatch_expand_layout (same rules as dispatch_layout). */
+/* Workspace bytes for dispatch_expand_layout (same layout and rules as the
+ * dispatch's: 256-byte aligned, zero-filled before its first use, so that
+ * one buffer may serve calls of either kind; the expand's own kernels never
+ * write its exchange region). */
 int dispatch_expand_workspace_size(const dispatch_expand_problem_t* problem, size_t* bytes);
 
 /* Worst-case expert-major rows: S*M*min(K, E/R) + (E/R)*(A-1). */

@@ -651,8 +651,9 @@ def alloc_expand_layout(problem: ExpandProblem, device) -> ExpandLayoutTensors:
 
 
 def alloc_expand_workspace(problem: ExpandProblem, device) -> torch.Tensor:
+    """Workspace for the expand layout calls: zero-filled, as its first use requires."""
     n = dispatch_expand_workspace_size(problem)
-    return torch.empty((n + 255) // 256 * 256, dtype=torch.uint8, device=device)
+    return torch.zeros((n + 255) // 256 * 256, dtype=torch.uint8, device=device)
 
 
 def dispatch_expand_layout(problem: ExpandProblem, recv_topk_idx: torch.Tensor, recv_count: torch.Tensor,

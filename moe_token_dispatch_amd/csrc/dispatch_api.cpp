@@ -226,11 +226,9 @@ int dispatch_layout(const dispatch_problem_t* problem, const void* topk_idx, con
     TileGeometry g;
     const int rc = check_layout_args(problem, topk_idx, out, workspace, workspace_bytes, &g);
     if (rc != DISPATCH_OK) return rc;
-    const hipError_t err = moe_dispatch::exchange_layout_fits(*problem, g)
-                               ? moe_dispatch::launch_exchange_layout(*problem, g, topk_idx, *out, workspace, nullptr,
-                                                                      stream)
-                               : moe_dispatch::launch_layout(*problem, g, topk_idx, *out, workspace, stream);
-    return err == hipSuccess ? DISPATCH_OK : DISPATCH_ERR_HIP;
+    if (moe_dispatch::launch_layout(*problem, g, topk_idx, *out, workspace, stream) != hipSuccess)
+        return DISPATCH_ERR_HIP;
+    return DISPATCH_OK;
 }
 
 int dispatch_layout_read_ahead(const dispatch_problem_t* problem, const void* topk_idx, const dispatch_layout_t* out,
@@ -247,8 +245,8 @@ int dispatch_layout_read_ahead(const dispatch_problem_t* problem, const void* to
     moe_dispatch::ReadAhead ra{x, p.num_tokens * p.row_bytes, x_sf, p.num_tokens * p.sf_per_token};
     const bool read_ahead = moe_dispatch::read_ahead_fits(ra.x_bytes, ra.sf_words);
     const hipError_t err =
-        moe_dispatch::exchange_layout_fits(p, g)
-            ? moe_dispatch::launch_exchange_layout(p, g, topk_idx, *out, workspace, read_ahead ? &ra : nullptr, stream)
+        read_ahead && moe_dispatch::exchange_layout_fits(p, g)
+            ? moe_dispatch::launch_exchange_layout(p, g, topk_idx, *out, workspace, &ra, stream)
             : moe_dispatch::launch_layout(p, g, topk_idx, *out, workspace, stream, nullptr, read_ahead ? &ra : nullptr);
     return err == hipSuccess ? DISPATCH_OK : DISPATCH_ERR_HIP;
 }
@@ -258,12 +256,15 @@ int dispatch_kernel_count(const dispatch_problem_t* problem, int* layout_kernels
     if (rc != DISPATCH_OK) return rc;
     const TileGeometry g = moe_dispatch::make_geometry(problem->num_tokens, problem->num_topk,
                                                        problem->num_experts, problem->num_ranks);
-    const int layout = (g.num_tiles == 1 && !g.column_scan) || moe_dispatch::exchange_layout_fits(*problem, g)
-                           ? 1
-                           : (g.column_scan ? 3 : 2);
+    const int layout = g.num_tiles == 1 && !g.column_scan ? 1 : (g.column_scan ? 3 : 2);
     if (layout_kernels) *layout_kernels = layout;
+    // The combined call lays out in one launch when it reads the rows ahead
+    // and the tiles can exchange their counts.
+    const bool read_ahead = moe_dispatch::read_ahead_fits(problem->num_tokens * problem->row_bytes,
+                                                          problem->num_tokens * problem->sf_per_token);
+    const bool exchange = read_ahead && moe_dispatch::exchange_layout_fits(*problem, g);
     if (layout_and_scatter_kernels)
-        *layout_and_scatter_kernels = moe_dispatch::fused_shape(*problem, g).fits ? 1 : layout + 1;
+        *layout_and_scatter_kernels = moe_dispatch::fused_shape(*problem, g).fits ? 1 : (exchange ? 1 : layout) + 1;
     return DISPATCH_OK;
 }
 
@@ -291,9 +292,8 @@ int dispatch_layout_and_scatter(const dispatch_problem_t* problem, const void* t
     const bool read_ahead = moe_dispatch::read_ahead_fits(ra.x_bytes, ra.sf_words);
     dispatch_problem_t sp = p;
     if (read_ahead) sp.flags |= DISPATCH_ROWS_READ_AHEAD;
-    const bool exchange = moe_dispatch::exchange_layout_fits(p, g);
-    if ((exchange ? moe_dispatch::launch_exchange_layout(p, g, topk_idx, *out, workspace, read_ahead ? &ra : nullptr,
-                                                         stream)
+    const bool exchange = read_ahead && moe_dispatch::exchange_layout_fits(p, g);
+    if ((exchange ? moe_dispatch::launch_exchange_layout(p, g, topk_idx, *out, workspace, &ra, stream)
                   : moe_dispatch::launch_layout(p, g, topk_idx, *out, workspace, stream, nullptr,
                                                 read_ahead ? &ra : nullptr)) != hipSuccess ||
         moe_dispatch::launch_scatter(sp, *out, x, x_sf, rank_x, rank_sf, recv_x, recv_sf, stream,

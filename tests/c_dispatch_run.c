@@ -1,9 +1,8 @@
 /* The library driven from C alone: buffers from hipMalloc, no Python or torch
  * in the process. Built by tests/c_programs.py, run by tests/test_gpu_c_caller.py
  * as `c_dispatch_run MODE input output`, MODE one of dispatch, expand, combine.
- * Every output buffer is filled with 0xA5 bytes before the calls (the dispatch
- * workspace is zero-filled, as the ABI asks; the expand workspace is filled
- * with 0xA5 too, since it needs no clearing), which run on
+ * Every output buffer is filled with 0xA5 bytes before the calls (the
+ * workspaces are zero-filled, as the ABI asks), which run on
  * a stream of their own with worst-case capacities; every output buffer is
  * then written to the output file. Exit status 0 when every HIP call
  * succeeded (the library's return code is the first field of the output).
@@ -53,7 +52,7 @@ static void* dev_filled(size_t bytes) {
     return p;
 }
 
-/* A dispatch workspace: zero-filled before its first use, as the ABI asks. */
+/* A workspace: zero-filled before its first use, as the ABI asks. */
 static void* dev_zeroed(size_t bytes) {
     void* p = NULL;
     const size_t n = bytes ? bytes : 16;
@@ -218,7 +217,7 @@ static int run_expand(FILE* in, FILE* out, hipStream_t stream) {
     lay.recv_src_token_idx = dev_filled((size_t)recv_cap * 4);
     void* recv_x = dev_filled((size_t)(recv_cap * RB));
     float* recv_sf = SF ? dev_filled((size_t)(recv_cap * SF) * 4) : NULL;
-    void* ws = dev_filled(ws_bytes);
+    void* ws = dev_zeroed(ws_bytes);
     HIP_OK(hipDeviceSynchronize());
 
     if (h[9]) {

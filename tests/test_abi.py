@@ -155,36 +155,39 @@ def test_host_errors_before_launch():
 
 
 def test_kernel_counts():
-    """The layout: one kernel for a one-tile batch and for the one-launch
-    layout (several tiles that exchange their key counts: up to 256 tiles of
-    fewer than 4096 tokens, a thread per count word), else two with the
-    histograms reduced in the assign kernel, three with the column scan. The
-    combined call: one kernel up to 3072 (token, k) pairs (2048 when pad rows
-    are zeroed), else the layout's kernels and the scatter."""
+    """The layout: one kernel for a one-tile batch, two with the histograms
+    reduced in the assign kernel, three with the column scan. The combined
+    call: one kernel up to 3072 (token, k) pairs (2048 when pad rows are
+    zeroed); beyond, when it reads the rows ahead (at most 160 MB) and the
+    tiles can exchange their counts (up to 256 tiles of fewer than 4096
+    tokens whose exchange words fit 8192, a thread per count word), the
+    one-launch layout and the scatter; else the layout's kernels and the
+    scatter."""
     mk = M.make_problem
     assert M.dispatch_kernel_count(mk(256, 8, 256, 8, 1, row_bytes=14336)) == (1, 1)
     assert M.dispatch_kernel_count(mk(0, 8, 256, 8, 1, row_bytes=64)) == (1, 1)
     assert M.dispatch_kernel_count(mk(2048, 1, 64, 8, 1, row_bytes=48)) == (1, 1)
-    assert M.dispatch_kernel_count(mk(257, 8, 256, 8, 1, row_bytes=14336)) == (1, 1)
-    assert M.dispatch_kernel_count(mk(384, 8, 256, 8, 1, row_bytes=14336)) == (1, 1)
-    assert M.dispatch_kernel_count(mk(385, 8, 256, 8, 1, row_bytes=14336)) == (1, 2)
+    assert M.dispatch_kernel_count(mk(257, 8, 256, 8, 1, row_bytes=14336)) == (2, 1)
+    assert M.dispatch_kernel_count(mk(384, 8, 256, 8, 1, row_bytes=14336)) == (2, 1)
+    assert M.dispatch_kernel_count(mk(385, 8, 256, 8, 1, row_bytes=14336)) == (2, 2)
     assert M.dispatch_kernel_count(mk(256, 8, 256, 8, 128, row_bytes=7168, sf_per_token=56)) == (1, 1)
-    assert M.dispatch_kernel_count(mk(257, 8, 256, 8, 128, row_bytes=7168, sf_per_token=56)) == (1, 2)
-    assert M.dispatch_kernel_count(mk(384, 8, 256, 8, 2, row_bytes=64)) == (1, 2)
+    assert M.dispatch_kernel_count(mk(257, 8, 256, 8, 128, row_bytes=7168, sf_per_token=56)) == (2, 2)
+    assert M.dispatch_kernel_count(mk(384, 8, 256, 8, 2, row_bytes=64)) == (2, 2)
     # Without the zero-pad flag nothing is padded, and the 3072-pair limit holds.
     assert M.dispatch_kernel_count(mk(384, 8, 256, 8, 2, row_bytes=64,
-                                      flags=M.RANK_CONTIG | M.EXPERT_MAJOR)) == (1, 1)
-    assert M.dispatch_kernel_count(mk(3072, 1, 64, 8, 1, row_bytes=48)) == (1, 1)
-    assert M.dispatch_kernel_count(mk(4096, 8, 256, 8, 1, row_bytes=14336)) == (1, 2)
-    assert M.dispatch_kernel_count(mk(16384, 8, 128, 16, 1, row_bytes=8192)) == (1, 2)
-    # 128 tiles of 16 wavefronts x 4 chunks (512 tokens each).
-    assert M.dispatch_kernel_count(mk(65536, 8, 256, 8, 128, row_bytes=7168, sf_per_token=56)) == (1, 2)
+                                      flags=M.RANK_CONTIG | M.EXPERT_MAJOR)) == (2, 1)
+    assert M.dispatch_kernel_count(mk(3072, 1, 64, 8, 1, row_bytes=48)) == (2, 1)
+    assert M.dispatch_kernel_count(mk(4096, 8, 256, 8, 1, row_bytes=14336)) == (2, 2)
+    assert M.dispatch_kernel_count(mk(16384, 8, 128, 16, 1, row_bytes=8192)) == (2, 2)
+    # 470 MB of rows: no read-ahead, so the count and assign kernels.
+    assert M.dispatch_kernel_count(mk(65536, 8, 256, 8, 128, row_bytes=7168, sf_per_token=56)) == (2, 3)
     # 514 tiles of 16 wavefronts x 4 chunks: past the one-launch layout's 256 tiles.
     assert M.dispatch_kernel_count(mk(257 * 1024, 8, 64, 8, 1, row_bytes=16)) == (2, 3)
     assert M.dispatch_kernel_count(mk(4096, 8, 4096, 1024, 1, row_bytes=64)) == (3, 4)
     assert M.dispatch_kernel_count(mk(80, 8, 4096, 1024, 1, row_bytes=64)) == (1, 1)
     # 5120 keys: 1024 count words per tile, more than a 5-wavefront tile's threads.
     assert M.dispatch_kernel_count(mk(300, 8, 4096, 1024, 1, row_bytes=64)) == (2, 1)
+    assert M.dispatch_kernel_count(mk(3841, 8, 4096, 1024, 1, row_bytes=64)) == (3, 4)
     with pytest.raises(M.DispatchError):
         M.dispatch_kernel_count(M.Problem(10, 0, 8, 2, 1, 8, 0, 64, 100, 100, M.ALL_OUTPUTS, 0))
 

@@ -1,7 +1,7 @@
 """The one-launch layout on the GPU: tiles that exchange their key counts
 through the workspace inside one kernel ("DeepEP Counting Sort /
 Bucketization" page, section 4.5's cross-tile merge, done without a central
-workgroup).
+workgroup), which the calls that read the token rows ahead take.
 
 - One zero-filled workspace serves a sequence of problems of every layout
   geometry (one launch with 1, 2, 4 or 8 chunks per wavefront, two launches,
@@ -45,16 +45,17 @@ def _exchange_region_is_zero(ws: torch.Tensor) -> bool:
     return int(torch.count_nonzero(ws[:EXCHANGE_BYTES]).item()) == 0
 
 
-# (T, K, E, R, A, row_bytes, S, kernels of dispatch_layout)
+# (T, K, E, R, A, row_bytes, S, kernels of the combined call: 2 = the
+# one-launch layout and the scatter)
 SHAPES = [
-    (4096, 8, 256, 8, 1, 64, 0, 1),      # one launch, 8-wavefront tiles, 64 tiles
-    (31744, 8, 256, 8, 1, 16, 0, 2),     # 248 tiles: words past the region, two launches
-    (31745, 8, 256, 8, 4, 16, 3, 1),     # one launch, 16-wavefront tiles of 2 chunks
-    (3841, 8, 4096, 1024, 1, 16, 0, 3),  # column scan
-    (63489, 8, 256, 8, 1, 16, 0, 1),     # one launch, 4 chunks
-    (2500, 6, 64, 8, 128, 48, 2, 1),     # top-6 (lanes 60..63 idle), pad inverse-map entries
-    (126977, 8, 256, 8, 1, 16, 0, 1),    # one launch, 8 chunks
-    (900, 1, 16, 4, 3, 32, 0, 1),        # top-1, 512-token tiles
+    (4096, 8, 256, 8, 1, 64, 0, 2),      # one launch, 8-wavefront tiles, 64 tiles
+    (31744, 8, 256, 8, 1, 16, 0, 3),     # 248 tiles: words past the region, two launches
+    (31745, 8, 256, 8, 4, 16, 3, 2),     # one launch, 16-wavefront tiles of 2 chunks
+    (3841, 8, 4096, 1024, 1, 16, 0, 4),  # column scan
+    (63489, 8, 256, 8, 1, 16, 0, 2),     # one launch, 4 chunks
+    (2500, 6, 64, 8, 128, 48, 2, 2),     # top-6 (lanes 60..63 idle), pad inverse-map entries
+    (126977, 8, 256, 8, 1, 16, 0, 2),    # one launch, 8 chunks
+    (5000, 1, 16, 4, 3, 32, 0, 2),       # top-1, 512-token tiles
 ]
 
 
@@ -62,7 +63,7 @@ def test_one_workspace_across_geometries_and_entry_points():
     probs = [M.make_problem(t, k, e, r, a, 8, rb, s) for t, k, e, r, a, rb, s, _ in SHAPES]
     ws = torch.zeros(max(M.dispatch_workspace_size(p) for p in probs) + 256, dtype=torch.uint8, device=H.DEVICE)
     for i, ((t, k, e, r, a, rb, s, kernels), prob) in enumerate(zip(SHAPES, probs)):
-        assert M.dispatch_kernel_count(prob)[0] == kernels, (t, k, e, r)
+        assert M.dispatch_kernel_count(prob)[1] == kernels, (t, k, e, r)
         topk = _uniform(100 + i, t, k, e, 0.05)
         xb = H.random_rows(100 + i, t, rb)
         sf = np.random.default_rng([i, 3]).random((t, s), dtype=np.float32) if s else None
@@ -78,7 +79,9 @@ def test_one_workspace_across_geometries_and_entry_points():
 
 
 def test_expand_layout_leaves_the_exchange_region_alone():
-    """The expand's workspace has the same region at its start and never writes it."""
+    """The expand's workspace has the same region at its start, and its
+    layout (count and assign kernels) never writes it; a dispatch that takes
+    the one-launch layout then runs on the same buffer."""
     q = M.make_expand_problem(4, 600, 8, 256, 8, 0, 1, 8, 64, 0)
     t, k, e, r = 2000, 8, 256, 8
     prob = M.make_problem(t, k, e, r, 1, 8, 64, 0)
@@ -87,12 +90,20 @@ def test_expand_layout_leaves_the_exchange_region_alone():
     recv_topk = torch.from_numpy(_uniform(9, 4 * 600, 8, 256, 0.0)).to(H.DEVICE)
     recv_count = torch.tensor([600, 500, 0, 317], dtype=torch.int32, device=H.DEVICE)
     lay = M.alloc_expand_layout(q, H.DEVICE)
+    for f in ("expert_count", "expert_psum", "expert_slot", "recv_src_row_idx"):
+        getattr(lay, f).fill_(H.CANARY)
     M.dispatch_expand_layout(q, recv_topk, recv_count, lay, ws)
     torch.cuda.synchronize()
     assert int(lay.status.item()) == 0
     assert _exchange_region_is_zero(ws)
+    ref = oracle.expand_layout(recv_topk.cpu().numpy(), recv_count.cpu().numpy(), 4, 600, 256, 8, 0, 1)
+    assert np.array_equal(lay.expert_count.cpu().numpy(), ref.expert_count)
+    assert np.array_equal(lay.expert_psum.cpu().numpy(), ref.expert_psum)
+    assert np.array_equal(lay.expert_slot.cpu().numpy().reshape(-1), ref.expert_slot.reshape(-1))
+    p_rows = int(ref.expert_psum[-1])
+    assert np.array_equal(lay.recv_src_row_idx.cpu().numpy()[:p_rows], ref.recv_src_row_idx[:p_rows])
     # The same buffer then serves a dispatch that takes the one-launch layout.
-    assert M.dispatch_kernel_count(prob)[0] == 1
+    assert M.dispatch_kernel_count(prob)[1] == 2
     topk = _uniform(10, t, k, e, 0.05)
     xb = H.random_rows(10, t, 64)
     run = H.run_gpu(topk, e, r, 1, xb, workspace=ws, combined=True)

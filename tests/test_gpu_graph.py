@@ -22,13 +22,13 @@ from tests import gpu_harness as H
 pytestmark = pytest.mark.gpu
 
 
-# The layout and scatter calls on a batch of several tiles (whose layout is
-# one launch that exchanges tile counts through the workspace: every replay
-# must leave the exchange words zero for the next), and the combined call on
-# small batches, where it is one kernel. Then a small batch over 256 experts
-# at alignment 128, whose pad rows the scatter maps to row blocks and the one
-# kernel deals out in chunks, and the combined call on several tiles (the
-# one-launch layout with its read-ahead, then the scatter).
+# The layout and scatter calls on a batch of several tiles, and the combined
+# call on small batches, where it is one kernel. Then a small batch over 256
+# experts at alignment 128, whose pad rows the scatter maps to row blocks and
+# the one kernel deals out in chunks, and the combined call on several tiles:
+# the one-launch layout, whose tiles exchange their counts through the
+# workspace (every replay must leave the exchange words zero for the next),
+# with its read-ahead, then the scatter.
 @pytest.mark.parametrize("dtype,with_sf,alignment,t,combined,experts", [
     ("bf16", False, 1, 1500, False, 64), ("fp8", True, 16, 1500, False, 64),
     ("bf16", False, 1, 200, True, 64), ("fp8", True, 16, 256, True, 64),

@@ -101,10 +101,12 @@ def test_token_counts_around_tiles(t):
 
 # Shapes on both sides of every layout geometry switch. While the tile
 # histograms (16-wavefront tiles, 1/2/4/8 chunks per wavefront) hold at most
-# 65536 ints, the tiles either exchange their counts in one launch (up to 256
-# tiles whose exchange words fit the workspace's 8192-word region, a thread
-# per count word) or take two launches; beyond, a column scan over
-# 4-wavefront tiles. Very wide key sets narrow the tiles to what LDS holds.
+# 65536 ints, two launches; beyond, a column scan over 4-wavefront tiles.
+# Very wide key sets narrow the tiles to what LDS holds. The combined call on
+# the same shapes reads the rows ahead, and then lays out in one launch where
+# the tiles can exchange their counts (up to 256 tiles whose exchange words
+# fit the workspace's 8192-word region, a thread per count word); the
+# comments name the combined call's layout.
 @pytest.mark.parametrize("t,k,e,r", [
     (31744, 8, 256, 8),     # two launches, 1 chunk per wavefront, 248 tiles (the largest)
     (31745, 8, 256, 8),     # one launch, 2 chunks, 125 tiles
