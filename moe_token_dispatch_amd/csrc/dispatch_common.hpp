@@ -57,6 +57,7 @@ struct TileGeometry {
     size_t ws_tile_err;
     size_t ws_exchange;         // the one-launch layout's exchange region (see below): always at 0
     int32_t exchange_words;     // 64-bit exchange words per tile (0: no one-launch layout)
+    int32_t exchange_sum_run;   // exchange words summed whole before their counts are split (1..16)
     size_t ws_bytes;
 };
 
@@ -154,10 +155,20 @@ inline TileGeometry make_geometry(int64_t num_tokens, int32_t num_topk, int32_t 
     g.ws_tile_err = g.ws_totals + round_up_256((size_t)g.num_keys * sizeof(int32_t));
     g.ws_bytes = g.ws_tile_err + round_up_256((size_t)g.num_tiles * sizeof(int32_t));
     const int words = (g.num_keys + kExchangeCountsPerWord - 1) / kExchangeCountsPerWord + 1;
+    // (The exchange kernel holds one more row of num_keys ints in LDS than
+    // the assign kernel: the tile's own counts.)
     const bool exchange = !g.column_scan && g.num_tiles > 1 && g.num_tiles <= kExchangeMaxTiles &&
                           g.tokens_per_tile < (1 << kExchangeCountBits) &&
-                          (int64_t)g.num_tiles * words <= kExchangeRegionWords;
+                          (int64_t)g.num_tiles * words <= kExchangeRegionWords &&
+                          (int64_t)(g.waves_per_tile + 3) * g.num_keys <= kLdsBudgetInts;
     g.exchange_words = exchange ? words : 0;
+    // A key counts at most one pair per token, so a count is at most
+    // tokens_per_tile, and this many words add up as plain 64-bit integers
+    // without one 12-bit count carrying into the next: the most, up to 16,
+    // a power of two, with run * tokens_per_tile < 2^12.
+    int run = 16;
+    while (run > 1 && (int64_t)run * g.tokens_per_tile >= (1 << kExchangeCountBits)) run /= 2;
+    g.exchange_sum_run = exchange ? run : 0;
     return g;
 }
 

@@ -61,6 +61,7 @@ struct LayoutParams {
     int32_t hist_stride;  // ints per histogram row (num_keys padded to a multiple of 4)
     int32_t num_tiles;
     int32_t exchange_words;  // one-launch layout: exchange words per tile
+    int32_t exchange_sum_run;  // words summed whole before their counts are split
     int64_t wait_limit;      // one-launch layout: polls before a tile gives up
     // Receiver-side expand only: the table is a fixed-stride receive buffer
     // of rows_per_source rows per source, source s holding recv_count[s]
@@ -180,6 +181,23 @@ __device__ __forceinline__ void load_entries(const IdxT* __restrict__ topk, int6
     }
 }
 
+// Inclusive sum over the 64 lanes of a wavefront through DPP moves, which
+// stay in the vector unit (a shuffle is an LDS instruction and waits LDS
+// latency at every step): shifts within each row of 16 lanes, then the last
+// lane of row 0 and of row 2 added to rows 1 and 3, then lane 31 added to
+// rows 2 and 3. Rows a move does not write keep 0 from `old`. (Measured on
+// MI355X in the one-launch layout: 0.3 us less per scan than shuffles.)
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+    constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+    x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 1, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 2, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 4, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 8, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kRowBcast15, 0xa, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kRowBcast31, 0xc, 0xf, false);
+    return x;
+}
+
 // Two exclusive scans in one pass by the whole workgroup: of in[0, n_a),
 // each value rounded up to a multiple of `align` first, and of in[n_a, n),
 // each starting from 0, both into out. Returns the two totals. `scratch`
@@ -196,17 +214,7 @@ __device__ int2 block_exclusive_scan2(const int* __restrict__ in, int* __restric
         if (i < n_a) la += align > 1 ? (c + align - 1) / align * align : c;
         else lb += c;
     }
-    // Kogge-Stone inclusive scans across the 64 lanes (6 steps).
-    int ia = la, ib = lb;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int ua = __shfl_up(ia, off, kWave);
-        const int ub = __shfl_up(ib, off, kWave);
-        if (lane >= off) {
-            ia += ua;
-            ib += ub;
-        }
-    }
+    const int ia = wave_inclusive_sum(la), ib = wave_inclusive_sum(lb);
     if (lane == kWave - 1) {
         scratch[2 * wave] = ia;
         scratch[2 * wave + 1] = ib;
@@ -753,11 +761,13 @@ exchange_layout_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace 
         read_ahead(p, blockIdx.x - p.num_tiles);
         return;
     }
-    // LDS: [W][num_keys] wavefront counters, then totals[num_keys] and first[num_keys].
+    // LDS: [W][num_keys] wavefront counters, then totals[num_keys],
+    // first[num_keys] and own[num_keys].
     extern __shared__ int lds[];
     __shared__ int scratch[2 * (kLayoutThreads / kWave + 1)];
     __shared__ uint32_t block_err;
     __shared__ int last_tile;
+    constexpr int kMaxWaves = kLayoutThreads / kWave;
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int nthreads = blockDim.x, nwaves = nthreads / kWave, nkeys = p.num_keys;
@@ -766,6 +776,7 @@ exchange_layout_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace 
     int* counters = lds + wave * nkeys;
     int* totals = lds + nwaves * nkeys;  // per key, over all tiles
     int* first = totals + nkeys;         // per key: pairs in earlier tiles, then the first slot
+    int* own = first + nkeys;            // per key: this tile's pairs
     const int token_in_chunk = lane / K;
     const int k = lane - token_in_chunk * K;
     const int64_t wave_tok0 = (int64_t)tile * p.tokens_per_tile + (int64_t)wave * p.tokens_per_wave;
@@ -791,20 +802,33 @@ exchange_layout_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace 
     }
     __syncthreads();
 
-    // Publish the tile's count of every key (its wavefronts' counters
-    // summed), kExchangeCountsPerWord to a word, then its error bits.
+    // Publish the tile's count of every key, kExchangeCountsPerWord to a
+    // word, then its error bits. The counts are summed over the wavefronts
+    // first, one key per thread, so the words all go out after one LDS
+    // round. (Measured on MI355X: packing the words straight from the
+    // wavefront counters, 5 keys times 8 wavefronts read in turn by each of
+    // 53 threads, took 1.8 us, and every other tile waited for it; this
+    // takes 0.9 us.)
+    for (int j = tid; j < nkeys; j += nthreads) {
+        int c[kMaxWaves];
+#pragma unroll
+        for (int w = 0; w < kMaxWaves; ++w) c[w] = w < nwaves ? lds[w * nkeys + j] : 0;
+        int sum = 0;
+#pragma unroll
+        for (int w = 0; w < kMaxWaves; ++w) sum += c[w];
+        own[j] = sum;
+    }
+    __syncthreads();
     const int wpt = p.exchange_words;
     const int qwords = wpt - 1;
     uint64_t* mine = ws.exchange + (int64_t)tile * wpt;
     for (int q = tid; q < wpt; q += nthreads) {
         uint64_t v = kPublished;
         if (q < qwords) {
+#pragma unroll
             for (int c = 0; c < kExchangeCountsPerWord; ++c) {
                 const int j = q * kExchangeCountsPerWord + c;
-                if (j >= nkeys) break;
-                int sum = 0;
-                for (int w = 0; w < nwaves; ++w) sum += lds[w * nkeys + j];
-                v |= ((uint64_t)sum & kCountMask) << (c * kExchangeCountBits);
+                if (j < nkeys) v |= ((uint64_t)own[j] & kCountMask) << (c * kExchangeCountBits);
             }
         } else {
             v |= block_err;
@@ -814,16 +838,18 @@ exchange_layout_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace 
 
     // Every tile's words, until all are published. The rounds first read
     // only the error words (each tile's last), one word per tile, until all
-    // are there; then every word: thread (q, g) sums count word q over tiles
-    // g, g + groups, ... (qwords <= threads per tile), the first threads also
-    // take the error words, and a round with any word missing is read again.
-    // Readiness is decided per word, never inferred from another word.
-    // (Measured on MI355X: rounds that read every word made the layout of 64
-    // tiles 0.7 us slower, and 256 tiles re-reading their 7680 words slowed
-    // the read-ahead beside them by 5 us.)
+    // are there, and keep the error bits of the round that found them all
+    // (a word is written once per call, so once published its value is
+    // final); then the count words: thread (q, g) sums count word q over
+    // tiles g, g + groups, ... (qwords <= threads per tile), and a round with
+    // any word missing is read again. Readiness is decided per word, never
+    // inferred from another word. (Measured on MI355X: rounds that read
+    // every word made the layout of 64 tiles 0.7 us slower, and 256 tiles
+    // re-reading their 7680 words slowed the read-ahead beside them by 5 us.)
     const int groups = nthreads / qwords;
     const int q = tid % qwords, g = tid / qwords;
     int tot[kExchangeCountsPerWord], bef[kExchangeCountsPerWord];
+    const int run_mask = p.exchange_sum_run - 1;
     uint32_t errs = 0;
     bool timed_out = false;
     bool all_errs_seen = false;
@@ -834,19 +860,22 @@ exchange_layout_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace 
         }
         if (!all_errs_seen) {
             bool missing = false;
-            for (int i = tid; i < p.num_tiles; i += nthreads)
-                missing |= (__hip_atomic_load(ws.exchange + (int64_t)i * wpt + qwords, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT) &
-                            kPublished) == 0;
+            uint32_t e = 0;
+            for (int i = tid; i < p.num_tiles; i += nthreads) {
+                const uint64_t v = __hip_atomic_load(ws.exchange + (int64_t)i * wpt + qwords, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                missing |= (v & kPublished) == 0;
+                e |= (uint32_t)v;
+            }
             all_errs_seen = !__syncthreads_or(missing);
             if (!all_errs_seen) {
                 __builtin_amdgcn_s_sleep(4);
                 continue;
             }
+            errs = e;
         }
 #pragma unroll
         for (int c = 0; c < kExchangeCountsPerWord; ++c) tot[c] = bef[c] = 0;
-        errs = 0;
         bool missing = false;
         if (g < groups) {
             for (int i0 = g; i0 < p.num_tiles; i0 += groups * kExchangeBatch) {
@@ -858,24 +887,27 @@ exchange_layout_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace 
                                                                __HIP_MEMORY_SCOPE_AGENT)
                                            : kPublished;
                 }
+                // The words are summed as 64-bit integers, run_mask + 1 at a
+                // time, and only the sums split into counts. (Measured on
+                // MI355X: splitting every word, 16 x 5 counts per thread,
+                // made this round 0.3 us longer.)
+                uint64_t sum_all = 0, sum_before = 0;
 #pragma unroll
                 for (int b = 0; b < kExchangeBatch; ++b) {
                     missing |= (v[b] & kPublished) == 0;
-                    const bool earlier = i0 + b * groups < tile;
+                    const uint64_t w = v[b] & ~kPublished;
+                    sum_all += w;
+                    if (i0 + b * groups < tile) sum_before += w;
+                    if (((b + 1) & run_mask) == 0) {
 #pragma unroll
-                    for (int c = 0; c < kExchangeCountsPerWord; ++c) {
-                        const int n = (int)((v[b] >> (c * kExchangeCountBits)) & kCountMask);
-                        tot[c] += n;
-                        if (earlier) bef[c] += n;
+                        for (int c = 0; c < kExchangeCountsPerWord; ++c) {
+                            tot[c] += (int)((sum_all >> (c * kExchangeCountBits)) & kCountMask);
+                            bef[c] += (int)((sum_before >> (c * kExchangeCountBits)) & kCountMask);
+                        }
+                        sum_all = sum_before = 0;
                     }
                 }
             }
-        }
-        for (int i = tid; i < p.num_tiles; i += nthreads) {
-            const uint64_t v =
-                __hip_atomic_load(ws.exchange + (int64_t)i * wpt + qwords, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            missing |= (v & kPublished) == 0;
-            errs |= (uint32_t)v;
         }
         if (!__syncthreads_or(missing)) break;
         __builtin_amdgcn_s_sleep(2);
@@ -897,11 +929,14 @@ exchange_layout_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace 
         // Fold the earlier-tile pairs into the wavefront counters, then scan
         // the totals into the exclusive psums (expert counts aligned up first).
         for (int j = tid; j < nkeys; j += nthreads) {
+            int c[kMaxWaves];
+#pragma unroll
+            for (int w = 0; w < kMaxWaves; ++w) c[w] = w < nwaves ? lds[w * nkeys + j] : 0;
             int run = first[j];
-            for (int w = 0; w < nwaves; ++w) {
-                const int c = lds[w * nkeys + j];
-                lds[w * nkeys + j] = run;
-                run += c;
+#pragma unroll
+            for (int w = 0; w < kMaxWaves; ++w) {
+                if (w < nwaves) lds[w * nkeys + j] = run;
+                run += c[w];
             }
         }
         const int2 row_totals = block_exclusive_scan2(totals, first, E, nkeys, p.alignment, scratch);
@@ -1075,6 +1110,7 @@ LayoutParams make_params(const dispatch_problem_t& prob, const TileGeometry& g) 
     p.hist_stride = g.hist_stride;
     p.num_tiles = g.num_tiles;
     p.exchange_words = g.exchange_words;
+    p.exchange_sum_run = g.exchange_sum_run;
     return p;
 }
 
@@ -1186,7 +1222,7 @@ hipError_t launch_exchange_typed(const LayoutParams& p, const TileGeometry& g, c
     Workspace wc = ws;
     dispatch_layout_t oc = out;
     void* args[] = {&idx, &pc, &wc, &oc};
-    const size_t lds = (size_t)(g.waves_per_tile + 2) * g.num_keys * sizeof(int);
+    const size_t lds = (size_t)(g.waves_per_tile + 3) * g.num_keys * sizeof(int);
     return hipLaunchKernel(reinterpret_cast<const void*>(&exchange_layout_kernel<CH, IdxT>),
                            dim3((unsigned)(g.num_tiles + p.pf_groups)), dim3(g.waves_per_tile * kWave), args, lds,
                            stream);
