@@ -69,8 +69,9 @@ struct TileGeometry {
 // workspace (dispatch and expand alike), which no other kernel writes; the
 // words are zero between calls (each call clears the ones it used when it
 // ends), so a workspace must be zero-filled before its first use. Tiles
-// hold at most 4095 tokens (a count per key and tile fits 12 bits), and a
-// launch has at most kExchangeMaxTiles of them, all resident at once.
+// hold at most 4095 (token, k) pairs (a count per key and tile fits 12 bits
+// whatever the routing), and a launch has at most kExchangeMaxTiles of them,
+// all resident at once.
 constexpr int kExchangeCountsPerWord = 5;
 constexpr int kExchangeCountBits = 12;
 constexpr int kExchangeMaxTiles = 256;
@@ -157,17 +158,19 @@ inline TileGeometry make_geometry(int64_t num_tokens, int32_t num_topk, int32_t 
     const int words = (g.num_keys + kExchangeCountsPerWord - 1) / kExchangeCountsPerWord + 1;
     // (The exchange kernel holds one more row of num_keys ints in LDS than
     // the assign kernel: the tile's own counts.)
+    // A tile holds tokens_per_tile * K pairs, so no count of a key in it
+    // can exceed that, even where a token repeats an expert.
+    const int64_t tile_pairs = g.tokens_per_tile * (int64_t)num_topk;
     const bool exchange = !g.column_scan && g.num_tiles > 1 && g.num_tiles <= kExchangeMaxTiles &&
-                          g.tokens_per_tile < (1 << kExchangeCountBits) &&
+                          tile_pairs < (1 << kExchangeCountBits) &&
                           (int64_t)g.num_tiles * words <= kExchangeRegionWords &&
                           (int64_t)(g.waves_per_tile + 3) * g.num_keys <= kLdsBudgetInts;
     g.exchange_words = exchange ? words : 0;
-    // A key counts at most one pair per token, so a count is at most
-    // tokens_per_tile, and this many words add up as plain 64-bit integers
-    // without one 12-bit count carrying into the next: the most, up to 16,
-    // a power of two, with run * tokens_per_tile < 2^12.
+    // This many words add up as plain 64-bit integers without one 12-bit
+    // count carrying into the next: the most, up to 16, a power of two, with
+    // run * tile_pairs < 2^12.
     int run = 16;
-    while (run > 1 && (int64_t)run * g.tokens_per_tile >= (1 << kExchangeCountBits)) run /= 2;
+    while (run > 1 && run * tile_pairs >= (1 << kExchangeCountBits)) run /= 2;
     g.exchange_sum_run = exchange ? run : 0;
     return g;
 }

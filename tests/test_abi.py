@@ -160,7 +160,8 @@ def test_kernel_counts():
     call: one kernel up to 3072 (token, k) pairs (2048 when pad rows are
     zeroed); beyond, when it reads the rows ahead (at most 160 MB) and the
     tiles can exchange their counts (up to 256 tiles of fewer than 4096
-    tokens whose exchange words fit 8192, a thread per count word), the
+    (token, k) pairs whose exchange words fit 8192, a thread per count
+    word), the
     one-launch layout and the scatter; else the layout's kernels and the
     scatter."""
     mk = M.make_problem
@@ -188,6 +189,11 @@ def test_kernel_counts():
     # 5120 keys: 1024 count words per tile, more than a 5-wavefront tile's threads.
     assert M.dispatch_kernel_count(mk(300, 8, 4096, 1024, 1, row_bytes=64)) == (2, 1)
     assert M.dispatch_kernel_count(mk(3841, 8, 4096, 1024, 1, row_bytes=64)) == (3, 4)
+    # Tiles of 256 tokens x 8 pairs hold 2048 pairs, of 512 tokens 4096: no
+    # 12-bit count then, whatever the routing.
+    assert M.dispatch_kernel_count(mk(31745, 8, 256, 8, 1, row_bytes=16)) == (2, 2)
+    assert M.dispatch_kernel_count(mk(63489, 8, 256, 8, 1, row_bytes=16)) == (2, 3)
+    assert M.dispatch_kernel_count(mk(260000, 1, 256, 8, 1, row_bytes=16)) == (2, 2)
     with pytest.raises(M.DispatchError):
         M.dispatch_kernel_count(M.Problem(10, 0, 8, 2, 1, 8, 0, 64, 100, 100, M.ALL_OUTPUTS, 0))
 

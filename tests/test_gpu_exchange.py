@@ -35,7 +35,10 @@ def _banner(msg):
 
 def _uniform(seed, t, k, e, mask):
     rng = np.random.default_rng([seed, 7])
-    topk = np.argsort(rng.random((t, e)), axis=1)[:, :k].astype(np.int64)
+    if k == 1:
+        topk = rng.integers(0, e, (t, 1), dtype=np.int64)
+    else:
+        topk = np.argsort(rng.random((t, e)), axis=1)[:, :k].astype(np.int64)
     m = rng.random((t, k)) < mask
     topk[m] = -1
     return topk
@@ -48,14 +51,16 @@ def _exchange_region_is_zero(ws: torch.Tensor) -> bool:
 # (T, K, E, R, A, row_bytes, S, kernels of the combined call: 2 = the
 # one-launch layout and the scatter)
 SHAPES = [
-    (4096, 8, 256, 8, 1, 64, 0, 2),      # one launch, 8-wavefront tiles, 64 tiles
+    (4096, 8, 256, 8, 1, 64, 0, 2),      # one launch, 8-wavefront tiles, 64 tiles; words summed 4 at a time
     (31744, 8, 256, 8, 1, 16, 0, 3),     # 248 tiles: words past the region, two launches
-    (31745, 8, 256, 8, 4, 16, 3, 2),     # one launch, 16-wavefront tiles of 2 chunks
+    (31745, 8, 256, 8, 4, 16, 3, 2),     # one launch, 16-wavefront tiles of 2 chunks; each word split alone
     (3841, 8, 4096, 1024, 1, 16, 0, 4),  # column scan
-    (63489, 8, 256, 8, 1, 16, 0, 2),     # one launch, 4 chunks
-    (2500, 6, 64, 8, 128, 48, 2, 2),     # top-6 (lanes 60..63 idle), pad inverse-map entries
-    (126977, 8, 256, 8, 1, 16, 0, 2),    # one launch, 8 chunks
+    (63489, 8, 256, 8, 1, 16, 0, 3),     # 4096 pairs per tile: past 12-bit counts, two launches
+    (2500, 6, 64, 8, 128, 48, 2, 2),     # top-6 (lanes 60..63 idle), pad inverse-map entries; 8 at a time
+    (16384, 8, 256, 8, 1, 16, 0, 2),     # one launch, 128-token tiles; 2 at a time
     (5000, 1, 16, 4, 3, 32, 0, 2),       # top-1, 512-token tiles
+    (10000, 2, 16, 4, 1, 32, 0, 2),      # top-2, 256-token tiles
+    (260000, 1, 256, 8, 1, 16, 0, 2),    # top-1, 2048-token tiles of 2 chunks
 ]
 
 
@@ -148,3 +153,22 @@ def test_wait_guard_reports_timeout_and_recovers():
     H.assert_layout_equal(run, ref)
     H.assert_rows_full(run, ref, xb, None)
     assert _exchange_region_is_zero(ws)
+
+
+@pytest.mark.parametrize("t,k,e,r", [(4096, 8, 256, 8), (31745, 8, 256, 8)])
+def test_repeated_experts_keep_exact_counts(t, k, e, r):
+    """A tile whose tokens all name one expert K times: the status reports
+    the repeat, and the counts and psums the tiles exchanged still equal the
+    oracle's, one count per (token, k) pair (the widest count a tile can
+    publish)."""
+    topk = _uniform(400, t, k, e, 0.05)
+    tpt = 64 if t == 4096 else 256  # tokens per tile of these geometries
+    topk[3 * tpt:4 * tpt, :] = 5
+    ref = oracle.layout(topk, e, r, 1)
+    assert ref.status == oracle.DUP_EXPERT
+    prob = M.make_problem(t, k, e, r, 1, 8, 64, 0)
+    assert M.dispatch_kernel_count(prob)[1] == 2  # the one-launch layout
+    _banner(f"T={t}: tile 3 routes every pair to expert 5")
+    run = H.run_gpu(topk, e, r, 1, H.random_rows(400, t, 64), combined=True)
+    torch.cuda.synchronize()
+    H.assert_layout_equal(run, ref)

@@ -104,14 +104,15 @@ def test_token_counts_around_tiles(t):
 # 65536 ints, two launches; beyond, a column scan over 4-wavefront tiles.
 # Very wide key sets narrow the tiles to what LDS holds. The combined call on
 # the same shapes reads the rows ahead, and then lays out in one launch where
-# the tiles can exchange their counts (up to 256 tiles whose exchange words
-# fit the workspace's 8192-word region, a thread per count word); the
-# comments name the combined call's layout.
+# the tiles can exchange their counts (up to 256 tiles of fewer than 4096
+# (token, k) pairs whose exchange words fit the workspace's 8192-word
+# region, a thread per count word); the comments name the combined call's
+# layout.
 @pytest.mark.parametrize("t,k,e,r", [
     (31744, 8, 256, 8),     # two launches, 1 chunk per wavefront, 248 tiles (the largest)
     (31745, 8, 256, 8),     # one launch, 2 chunks, 125 tiles
-    (63489, 8, 256, 8),     # one launch, 4 chunks
-    (126977, 8, 256, 8),    # one launch, 8 chunks
+    (63489, 8, 256, 8),     # two launches, 4 chunks (4096 pairs per tile: past 12-bit exchange counts)
+    (126977, 8, 256, 8),    # two launches, 8 chunks
     (253952, 8, 256, 8),    # two launches, 8 chunks, 248 tiles
     (253953, 8, 256, 8),    # column scan, 8 chunks per wavefront
     (768, 8, 4096, 1024),   # two launches, 5-wavefront tiles of 2 chunks (1025 words per tile)
