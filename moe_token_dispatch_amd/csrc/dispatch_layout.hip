@@ -732,7 +732,8 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
 }
 
 // One-launch layout: Count, Prefix Sum and the slot assignment of a batch of
-// several tiles in a single kernel, for the combined call. Workgroup `tile`
+// several tiles in a single kernel, for the layouts that read the token rows
+// ahead (the combined call, dispatch_layout_read_ahead). Workgroup `tile`
 // ranks its tile's pairs once (rank_chunk), keeping each pair's place in
 // registers, and publishes the tile's key counts and error bits as exchange
 // words: relaxed agent-scope atomic stores with bit 63 set. It then reads
@@ -740,7 +741,8 @@ assign_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace ws, dispa
 // atomic loads; each word is written once per call and carries its own
 // "published" bit, so no ordering between locations is needed), summing the
 // key totals and the counts of earlier tiles as it reads, and assigns its
-// slots exactly as assign_kernel does. Workgroups past the tiles read the
+// slots exactly as assign_kernel does. A tile holds fewer than 4096 (token,
+// k) pairs, so each of its counts fits the 12 bits a word gives it. Workgroups past the tiles read the
 // token rows ahead, all of them.
 // The tiles are the first workgroups of the grid and wait on nothing but
 // each other, so all of them are resident while they wait (the wait is
