@@ -37,6 +37,8 @@ def _uniform(seed, t, k, e, mask):
     rng = np.random.default_rng([seed, 7])
     if k == 1:
         topk = rng.integers(0, e, (t, 1), dtype=np.int64)
+    elif t > 100_000:  # k distinct experts per token, without sorting every row
+        topk = np.argpartition(rng.random((t, e), dtype=np.float32), k, axis=1)[:, :k].astype(np.int64)
     else:
         topk = np.argsort(rng.random((t, e)), axis=1)[:, :k].astype(np.int64)
     m = rng.random((t, k)) < mask
@@ -61,6 +63,7 @@ SHAPES = [
     (5000, 1, 16, 4, 3, 32, 0, 2),       # top-1, 512-token tiles
     (10000, 2, 16, 4, 1, 32, 0, 2),      # top-2, 256-token tiles
     (260000, 1, 256, 8, 1, 16, 0, 2),    # top-1, 2048-token tiles of 2 chunks
+    (180000, 3, 256, 8, 2, 16, 0, 2),    # top-3 (lane 63 idle), 16-wavefront tiles of 4 chunks
 ]
 
 
