@@ -854,9 +854,9 @@ exchange_layout_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace 
     // final); then the count words: thread (q, g) sums count word q over
     // tiles g, g + groups, ... (qwords <= threads per tile), and a round with
     // any word missing is read again. Readiness is decided per word, never
-    // inferred from another word. (Measured on MI355X: rounds that read
-    // every word made the layout of 64 tiles 0.7 us slower, and 256 tiles
-    // re-reading their 7680 words slowed the read-ahead beside them by 5 us.)
+    // inferred from another word. (Measured on MI355X: 256 tiles re-reading
+    // all their 7680 words every round slowed the read-ahead beside them by
+    // 5 us; with 64 tiles the two ways measured the same.)
     const int groups = nthreads / qwords;
     const int q = tid % qwords, g = tid / qwords;
     int tot[kExchangeCountsPerWord], bef[kExchangeCountsPerWord];
