@@ -847,80 +847,87 @@ exchange_layout_kernel(const IdxT* __restrict__ topk, LayoutParams p, Workspace 
         }
     }
 
-    // Every tile's words, until all are published. The rounds first read
-    // only the error words (each tile's last), one word per tile, until all
-    // are there, and keep the error bits of the round that found them all
-    // (a word is written once per call, so once published its value is
-    // final); then the count words: thread (q, g) sums count word q over
-    // tiles g, g + groups, ... (qwords <= threads per tile), and a round with
-    // any word missing is read again. Readiness is decided per word, never
-    // inferred from another word. (Measured on MI355X: 256 tiles re-reading
-    // all their 7680 words every round slowed the read-ahead beside them by
-    // 5 us; with 64 tiles the two ways measured the same.)
+    // Every tile's words, until all are published. Each round reads the
+    // words this thread has not yet found published: the error words (each
+    // tile's last) of tiles tid, tid + threads, ..., and count word q of
+    // group g's tiles, a run of consecutive tiles (qwords <= threads per
+    // tile; at most 64 tiles per group). A word is written once per call, so
+    // once published its value is final, and it is added the first time it
+    // is found. Readiness is decided per word, never inferred from another
+    // word. (Measured on MI355X, flushed steps, against reading only the
+    // error words until all were there and then every count word: the
+    // aligned fp8 batch, 64 tiles, 0.8-1.2 us faster; the metric batch, bound
+    // by its read-ahead, and the Zipf batch, 256 tiles, the same within
+    // 0.5 us. Reading the count words of a tile only after a round had found
+    // its error word, for 64 tiles or for more, gained nothing.)
     const int groups = nthreads / qwords;
     const int q = tid % qwords, g = tid / qwords;
-    int tot[kExchangeCountsPerWord], bef[kExchangeCountsPerWord];
+    const int per_group = (p.num_tiles + groups - 1) / groups;
+    const int t0 = g * per_group;
+    const int my_tiles = g < groups ? max(0, min(per_group, p.num_tiles - t0)) : 0;
+    uint64_t todo = my_tiles >= 64 ? ~uint64_t(0) : (uint64_t(1) << my_tiles) - 1;  // my tiles not yet added
+    uint32_t err_todo = 0;  // error words of tiles tid, tid + nthreads, ... not yet seen
+    for (int b = 0; b * nthreads + tid < p.num_tiles; ++b) err_todo |= 1u << b;
+    int tot[kExchangeCountsPerWord] = {}, bef[kExchangeCountsPerWord] = {};
     const int run_mask = p.exchange_sum_run - 1;
     uint32_t errs = 0;
     bool timed_out = false;
-    bool all_errs_seen = false;
     for (int64_t poll = 0;; ++poll) {
         if (poll == p.wait_limit) {
             timed_out = true;
             break;
         }
-        if (!all_errs_seen) {
-            bool missing = false;
-            uint32_t e = 0;
-            for (int i = tid; i < p.num_tiles; i += nthreads) {
-                const uint64_t v = __hip_atomic_load(ws.exchange + (int64_t)i * wpt + qwords, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-                missing |= (v & kPublished) == 0;
-                e |= (uint32_t)v;
+        const uint64_t need = todo;
+        // The error words are loaded first and looked at last, so that one
+        // memory round trip serves both kinds of word.
+        constexpr int kErrPerThread = kExchangeMaxTiles / kWave;  // tiles <= 256, threads >= 64
+        uint64_t ev[kErrPerThread];
+#pragma unroll
+        for (int b = 0; b < kErrPerThread; ++b)
+            ev[b] = ((err_todo >> b) & 1u) ? __hip_atomic_load(ws.exchange + (int64_t)(b * nthreads + tid) * wpt + qwords,
+                                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                           : 0;
+        for (int m0 = 0; m0 < my_tiles && (need >> m0) != 0; m0 += kExchangeBatch) {
+            uint64_t v[kExchangeBatch];
+#pragma unroll
+            for (int b = 0; b < kExchangeBatch; ++b) {
+                const int m = m0 + b;
+                v[b] = m < my_tiles && ((need >> m) & 1)
+                           ? __hip_atomic_load(ws.exchange + (int64_t)(t0 + m) * wpt + q, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)
+                           : 0;
             }
-            all_errs_seen = !__syncthreads_or(missing);
-            if (!all_errs_seen) {
-                __builtin_amdgcn_s_sleep(4);
-                continue;
-            }
-            errs = e;
-        }
+            // The words are summed as 64-bit integers, run_mask + 1 at a
+            // time, and only the sums split into counts. (Measured on
+            // MI355X: splitting every word, 16 x 5 counts per thread, made a
+            // round 0.3 us longer.)
+            uint64_t sum_all = 0, sum_before = 0;
 #pragma unroll
-        for (int c = 0; c < kExchangeCountsPerWord; ++c) tot[c] = bef[c] = 0;
-        bool missing = false;
-        if (g < groups) {
-            for (int i0 = g; i0 < p.num_tiles; i0 += groups * kExchangeBatch) {
-                uint64_t v[kExchangeBatch];
-#pragma unroll
-                for (int b = 0; b < kExchangeBatch; ++b) {
-                    const int i = i0 + b * groups;
-                    v[b] = i < p.num_tiles ? __hip_atomic_load(ws.exchange + (int64_t)i * wpt + q, __ATOMIC_RELAXED,
-                                                               __HIP_MEMORY_SCOPE_AGENT)
-                                           : kPublished;
-                }
-                // The words are summed as 64-bit integers, run_mask + 1 at a
-                // time, and only the sums split into counts. (Measured on
-                // MI355X: splitting every word, 16 x 5 counts per thread,
-                // made this round 0.3 us longer.)
-                uint64_t sum_all = 0, sum_before = 0;
-#pragma unroll
-                for (int b = 0; b < kExchangeBatch; ++b) {
-                    missing |= (v[b] & kPublished) == 0;
+            for (int b = 0; b < kExchangeBatch; ++b) {
+                if (v[b] & kPublished) {
                     const uint64_t w = v[b] & ~kPublished;
                     sum_all += w;
-                    if (i0 + b * groups < tile) sum_before += w;
-                    if (((b + 1) & run_mask) == 0) {
+                    if (t0 + m0 + b < tile) sum_before += w;
+                    todo &= ~(uint64_t(1) << (m0 + b));
+                }
+                if (((b + 1) & run_mask) == 0) {
 #pragma unroll
-                        for (int c = 0; c < kExchangeCountsPerWord; ++c) {
-                            tot[c] += (int)((sum_all >> (c * kExchangeCountBits)) & kCountMask);
-                            bef[c] += (int)((sum_before >> (c * kExchangeCountBits)) & kCountMask);
-                        }
-                        sum_all = sum_before = 0;
+                    for (int c = 0; c < kExchangeCountsPerWord; ++c) {
+                        tot[c] += (int)((sum_all >> (c * kExchangeCountBits)) & kCountMask);
+                        bef[c] += (int)((sum_before >> (c * kExchangeCountBits)) & kCountMask);
                     }
+                    sum_all = sum_before = 0;
                 }
             }
         }
-        if (!__syncthreads_or(missing)) break;
+#pragma unroll
+        for (int b = 0; b < kErrPerThread; ++b) {
+            if (ev[b] & kPublished) {
+                errs |= (uint32_t)ev[b];
+                err_todo &= ~(1u << b);
+            }
+        }
+        if (!__syncthreads_or(todo != 0 || err_todo != 0)) break;
         __builtin_amdgcn_s_sleep(2);
     }
 
@@ -1240,8 +1247,13 @@ hipError_t launch_exchange_typed(const LayoutParams& p, const TileGeometry& g, c
 }  // namespace
 
 bool exchange_layout_fits(const dispatch_problem_t& prob, const TileGeometry& g) {
-    // Exchange room in the geometry, and a thread per count word of a tile.
-    return g.exchange_words > 0 && g.exchange_words - 1 <= g.waves_per_tile * kWave && prob.num_tokens > 0;
+    // Exchange room in the geometry, a thread per count word of a tile, and
+    // at most 64 tiles for each group of threads that reads a tile's words.
+    if (g.exchange_words <= 0 || prob.num_tokens <= 0) return false;
+    const int threads = g.waves_per_tile * kWave, qwords = g.exchange_words - 1;
+    if (qwords > threads) return false;
+    const int groups = threads / qwords;
+    return (g.num_tiles + groups - 1) / groups <= 64;
 }
 
 hipError_t launch_exchange_layout(const dispatch_problem_t& prob, const TileGeometry& g, const void* topk_idx,
