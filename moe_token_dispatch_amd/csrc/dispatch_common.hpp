@@ -206,11 +206,14 @@ constexpr int64_t kReadAheadMaxBytes = int64_t(160) << 20;
 constexpr int kReadAheadGroups = 256;     // read-ahead workgroups per layout kernel
 constexpr int kReadAheadCountPct = 35;    // percent of the rows the count kernel reads
 // Read-ahead workgroups of the one-launch layout, which reads all the rows:
-// about 512 KB each, at least 128 and at most 512 of them. Measured on
-// MI355X (flushed steps): 59 MB of rows read fastest by 128-160 workgroups
-// (512: 2 us slower, 64: 6 us slower), 134 MB by 256 (128 or 512: 5 us slower).
+// about 512 KB each, at least 160 and at most 512 of them. Measured on
+// MI355X (flushed steps): 59 MB of rows read fastest by 160-176 workgroups
+// (with the 64 tiles, 28-30 workgroups on each XCD's 32 CUs; 128 or 144:
+// 1.1-1.6 us slower, 96: 2.7 us; before the exchange read its words as they
+// were published, 512 was 2 us and 64 was 6 us slower than 128), 134 MB by
+// 256 (128 or 512: 5 us slower).
 constexpr int64_t kExchangeReadAheadBytesPerGroup = int64_t(512) << 10;
-constexpr int kExchangeReadAheadMinGroups = 128;
+constexpr int kExchangeReadAheadMinGroups = 160;
 constexpr int kExchangeReadAheadMaxGroups = 512;
 inline int exchange_read_ahead_groups(int64_t bytes) {
     const int64_t g = (bytes + kExchangeReadAheadBytesPerGroup - 1) / kExchangeReadAheadBytesPerGroup;
